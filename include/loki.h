@@ -1,0 +1,191 @@
+/*
+ * loki.h -- C ABI of the MI355X (gfx950) low-rank-key sparse decode-attention
+ * library (libloki.so).
+ *
+ * The method (Loki: Low-rank Keys for Efficient Sparse Attention, abstract;
+ * AQUA: Attention via QUery mAgnitudes..., related work "LoKi Attention"):
+ * cached keys live in an offline orthonormal basis P (K_rot = K P); at each
+ * decode step every query head is rotated into the same basis, scores all
+ * cached tokens using only the leading r rotated dimensions, keeps its k
+ * best tokens for this step (nothing is evicted), and runs exact softmax
+ * attention over the full keys and values of just those tokens.  Decode
+ * attention itself is eqs. 1-5 of the AQUA page's preliminaries: S = q K^T,
+ * A = softmax(S / sqrt(d_head)), c = A V.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
+ *    caller; the library never allocates, frees or retains them.  They must
+ *    be 16-byte aligned.
+ *  - Layouts are contiguous and row-major:
+ *      q, out  [B, Hq, d]          K, K_rot, V  [B, Hkv, S, d]
+ *      P       [Hkv, d, d]         (K_rot[b,kv] = K[b,kv] * P[kv])
+ *      idx     [B, Hq, k] int32    scores  [B, Hq, S] fp32
+ *    q, P, K, K_rot, V and out share one storage dtype (fp32 or bf16).
+ *  - Grouped-query attention: query head h reads key/value head h / (Hq/Hkv)
+ *    (contiguous groups); P belongs to the key/value head.
+ *  - All arithmetic accumulates in fp32; the rotated query is kept in fp32
+ *    and never rounded to the storage dtype; outputs are rounded once
+ *    (round-to-nearest-even for bf16).
+ *  - The kept set of a query head is its k largest approximate scores; ties
+ *    go to the lower token index; idx lists the kept tokens in ascending
+ *    order.  Results are deterministic (bit-identical across runs).
+ *  - Every call validates all scalar arguments and pointer alignment on the
+ *    host BEFORE any HIP call and returns a status; nothing is enqueued when
+ *    the status is not LOKI_OK.  Work is enqueued asynchronously on `stream`
+ *    (0 = the null stream); buffers must stay alive until the stream reaches
+ *    it.  A failed launch returns LOKI_ERR_HIP.  The library holds no
+ *    per-call state, so calls on different streams may run concurrently as
+ *    long as they use different workspaces.
+ *  - Non-finite inputs (NaN, Inf) are not checked and give unspecified
+ *    results.
+ *  - Supported: d in {64, 128}; Hq/Hkv <= 16; dtype fp32 or bf16;
+ *    1 <= r <= d; 1 <= k <= S <= 2^24; B*Hq <= 65535.
+ */
+#ifndef LOKI_H
+#define LOKI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOKI_ABI_VERSION 1
+
+typedef enum {
+  LOKI_OK = 0,
+  LOKI_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  LOKI_ERR_SHAPE = 2,       /* a size is < 1, too large, or Hq % Hkv != 0       */
+  LOKI_ERR_RANGE = 3,       /* r outside [1, d] or k outside [1, S]             */
+  LOKI_ERR_DTYPE = 4,       /* unknown dtype code                               */
+  LOKI_ERR_ALIGN = 5,       /* a tensor pointer is not 16-byte aligned          */
+  LOKI_ERR_WORKSPACE = 6,   /* workspace smaller than the size function returns */
+  LOKI_ERR_UNSUPPORTED = 7, /* valid but not implemented (d, Hq/Hkv)            */
+  LOKI_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed       */
+  LOKI_ERR_INTERNAL = 9     /* unexpected internal failure                      */
+} loki_status;
+
+typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
+
+/* LOKI_ABI_VERSION of the built library. */
+int loki_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* loki_status_str(int status);
+
+/*
+ * Key projection into the offline basis: K_rot[b,kv] = K[b,kv] * P[kv]
+ * (row-vector convention v_hat = v P of the AQUA page's information-
+ * retention paragraph; with an orthogonal P it preserves every q.k, AQUA
+ * appendix on the lossless rotation).  Used when the cache is written
+ * (prefill, or a decode step's new key with S = 1).
+ *   K      [B, Hkv, S, d]  input keys
+ *   P      [Hkv, d, d]     basis per key/value head
+ *   K_rot  [B, Hkv, S, d]  output; must not overlap K or P
+ * bf16 runs on MFMA matrix cores with fp32 accumulation and one RNE
+ * rounding; fp32 runs on the vector ALUs.  No workspace.
+ */
+loki_status loki_project_keys(const void* K, const void* P, void* K_rot,
+                              int32_t B, int32_t Hkv, int32_t S, int32_t d,
+                              loki_dtype dt, hipStream_t stream);
+
+/*
+ * As loki_project_keys, and in the same pass also writes the leading R
+ * rotated dims of every cached key into a separate dense array:
+ *   K_lead [B, Hkv, S, R]   K_lead[b,kv,j,c] = K_rot[b,kv,j,c] for c < R
+ * K_lead is a second copy of data K_rot already holds (R/d of the key cache
+ * in extra memory).  It lets the approximate-score stage of
+ * loki_decode_lead stream R*elem bytes per token contiguously instead of a
+ * short prefix of every d-wide row, which on HBM costs a full 128-byte line
+ * per token whenever R*elem < 128.
+ * R: 1 <= R <= d (else LOKI_ERR_RANGE) and R*elem a multiple of 16 bytes
+ * (else LOKI_ERR_UNSUPPORTED).
+ */
+loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, void* K_lead,
+                                   int32_t R, int32_t B, int32_t Hkv, int32_t S, int32_t d,
+                                   loki_dtype dt, hipStream_t stream);
+
+/*
+ * Bytes of device workspace needed by loki_decode, loki_decode_lead, loki_scores and
+ * loki_attend for these sizes (0 if the sizes are invalid).  The same
+ * workspace may be reused by successive calls on one stream.
+ */
+size_t loki_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                                   int32_t d, int32_t r, int32_t k, loki_dtype dt);
+
+/*
+ * One Loki decode step for every (batch, query head):
+ *   q_rot = q P[kv]                                   (fp32, full d)
+ *   s_j   = sum_{c<r} q_rot[c] K_rot[b,kv,j,c]        (all S cached tokens)
+ *   idx   = the k tokens with the largest s_j (ties -> lower index), ascending
+ *   e_j   = q_rot . K_rot[b,kv,j,:] / sqrt(d),  j in idx
+ *   out   = sum_{j in idx} softmax(e)_j V[b,kv,j,:]
+ * Every cached token is eligible (no causal mask); V is not rotated.
+ *   q [B,Hq,d], P [Hkv,d,d], K_rot [B,Hkv,S,d], V [B,Hkv,S,d]  inputs
+ *   out [B,Hq,d] (dtype dt), idx [B,Hq,k] int32                 outputs
+ *   workspace: device buffer of >= loki_decode_workspace_bytes(...) bytes,
+ *              owned by the caller, contents need no initialisation.
+ */
+loki_status loki_decode(const void* q, const void* P, const void* K_rot, const void* V,
+                        void* out, int32_t* idx,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                        int32_t r, int32_t k, loki_dtype dt,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * loki_decode with the approximate scores read from the lead-dims copy
+ * K_lead [B,Hkv,S,R] (see loki_project_keys_lead) instead of from K_rot's
+ * rows.  Needs r <= R (else LOKI_ERR_RANGE); R constraints as for
+ * loki_project_keys_lead.  K_lead must hold the leading R dims of K_rot
+ * (results are those of loki_decode on the same K_rot).  Exact attention
+ * still reads full K_rot and V rows.  Same workspace as loki_decode.
+ */
+loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                             int32_t R, const void* V, void* out, int32_t* idx,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                             int32_t r, int32_t k, loki_dtype dt,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The approximate-score stage alone: scores[b,h,j] = s_j as defined for
+ * loki_decode (fp32, unscaled), by the same kernels that loki_decode uses.
+ * Workspace as for loki_decode with the same sizes (k = 1 may be passed).
+ */
+loki_status loki_scores(const void* q, const void* P, const void* K_rot, float* scores,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                        int32_t r, loki_dtype dt,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace needed by loki_select_topk. */
+size_t loki_select_workspace_bytes(int32_t rows, int32_t S, int32_t k);
+
+/*
+ * The selection stage alone on caller-given fp32 scores [rows, S]:
+ * idx[row] = the k largest scores of the row (ties -> lower index; -0.0
+ * equals +0.0), ascending, by the same selection kernel as loki_decode.
+ */
+loki_status loki_select_topk(const float* scores, int32_t* idx, int32_t rows, int32_t S,
+                             int32_t k, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * The exact-attention stage alone over a caller-given kept set idx
+ * [B,Hq,k] (int32): out = sum_{j in idx} softmax(e)_j V[b,kv,j,:] with e as
+ * for loki_decode, by the same kernels.  Entries outside [0, S) are ignored
+ * and repeated entries count once.  Workspace as for loki_decode.
+ */
+loki_status loki_attend(const void* q, const void* P, const void* K_rot, const void* V,
+                        const int32_t* idx, void* out,
+                        int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t k,
+                        loki_dtype dt, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOKI_H */

@@ -1,0 +1,244 @@
+"""Python binding of libloki, the gfx950 low-rank-key sparse decode-attention library.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory and the current HIP stream.  The entry points
+mirror the C ABI (``include/loki.h``) name for name:
+
+* :func:`loki_project_keys` -- ``K_rot = K P`` per key/value head;
+* :func:`loki_decode` -- one Loki decode step -> ``(out, idx)``;
+* :func:`loki_scores`, :func:`loki_select_topk`, :func:`loki_attend` -- the
+  decode stages alone (same kernels), for stage-level checks.
+
+If the built library is missing the calls raise; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libloki.so")
+
+LOKI_F32, LOKI_BF16 = 0, 1
+_DT = {torch.float32: LOKI_F32, torch.bfloat16: LOKI_BF16}
+
+_STATUS = {
+    0: "LOKI_OK", 1: "LOKI_ERR_NULL", 2: "LOKI_ERR_SHAPE", 3: "LOKI_ERR_RANGE",
+    4: "LOKI_ERR_DTYPE", 5: "LOKI_ERR_ALIGN", 6: "LOKI_ERR_WORKSPACE",
+    7: "LOKI_ERR_UNSUPPORTED", 8: "LOKI_ERR_HIP", 9: "LOKI_ERR_INTERNAL",
+}
+
+
+class LokiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_Z = ctypes.c_size_t
+
+_SIGS = {
+    "loki_abi_version": ([], ctypes.c_int),
+    "loki_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "loki_project_keys": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P], ctypes.c_int),
+    "loki_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I, ctypes.c_int], _Z),
+    "loki_project_keys_lead": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P], ctypes.c_int),
+    "loki_decode": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
+                    ctypes.c_int),
+    "loki_decode_lead": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
+                          _P, _Z, _P], ctypes.c_int),
+    "loki_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
+    "loki_select_workspace_bytes": ([_I, _I, _I], _Z),
+    "loki_select_topk": ([_P, _P, _I, _I, _I, _P, _Z, _P], ctypes.c_int),
+    "loki_attend": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
+                    ctypes.c_int),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of libloki.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libloki.so not built ({p}); run `python -m rank_key_sparse_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().loki_status_str(status).decode()
+        raise LokiError(status, msg)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype} (fp32 or bf16)")
+    return _DT[t.dtype]
+
+
+def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | None = None,
+                      R: int | None = None, K_lead: torch.Tensor | None = None):
+    """``K_rot[b, kv] = K[b, kv] @ P[kv]``; K [B,Hkv,S,d], P [Hkv,d,d].
+
+    With ``R``, also writes the lead-dims copy ``K_lead = K_rot[..., :R]``
+    (contiguous) in the same pass and returns ``(K_rot, K_lead)``.
+    """
+    _need(K, "K", ndim=4)
+    _need(P, "P", dtype=K.dtype, ndim=3, device=K.device)
+    B, Hkv, S, d = K.shape
+    if tuple(P.shape) != (Hkv, d, d):
+        raise ValueError("P must be [Hkv, d, d]")
+    if K_rot is None:
+        K_rot = torch.empty_like(K)
+    _need(K_rot, "K_rot", dtype=K.dtype, ndim=4, device=K.device)
+    lib = load_library()
+    if R is None:
+        _check(lib.loki_project_keys(_ptr(K), _ptr(P), _ptr(K_rot), B, Hkv, S, d, _dtype_code(K), _stream(K)))
+        return K_rot
+    if K_lead is None:
+        K_lead = torch.empty((B, Hkv, S, R), dtype=K.dtype, device=K.device)
+    _need(K_lead, "K_lead", dtype=K.dtype, ndim=4, device=K.device)
+    if tuple(K_lead.shape) != (B, Hkv, S, R):
+        raise ValueError("K_lead must be [B, Hkv, S, R]")
+    _check(lib.loki_project_keys_lead(_ptr(K), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, B, Hkv, S, d,
+                                      _dtype_code(K), _stream(K)))
+    return K_rot, K_lead
+
+
+def loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dtype) -> int:
+    return int(load_library().loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, _DT[dtype]))
+
+
+def _shapes(q, P, K_rot):
+    _need(q, "q", ndim=3)
+    _need(P, "P", dtype=q.dtype, ndim=3, device=q.device)
+    _need(K_rot, "K_rot", dtype=q.dtype, ndim=4, device=q.device)
+    B, Hq, d = q.shape
+    Bk, Hkv, S, dk = K_rot.shape
+    if Bk != B or dk != d or tuple(P.shape) != (Hkv, d, d):
+        raise ValueError("shape mismatch between q [B,Hq,d], P [Hkv,d,d] and K_rot [B,Hkv,S,d]")
+    return B, Hq, Hkv, S, d
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=device)
+    return workspace
+
+
+def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=None, K_lead=None):
+    """One Loki decode step.  Returns ``(out [B,Hq,d], idx [B,Hq,k] int32 ascending)``.
+
+    With ``K_lead`` ([B,Hkv,S,R], the leading R >= r dims of K_rot) the
+    approximate scores stream from it instead of from K_rot's rows.
+    """
+    B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
+    _need(V, "V", dtype=q.dtype, ndim=4, device=q.device)
+    if tuple(V.shape) != tuple(K_rot.shape):
+        raise ValueError("V must have K_rot's shape")
+    lib = load_library()
+    dt = _dtype_code(q)
+    nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dt))
+    ws = _workspace(nbytes, q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    if idx is None:
+        idx = torch.empty((B, Hq, k), dtype=torch.int32, device=q.device)
+    _need(out, "out", dtype=q.dtype, ndim=3, device=q.device)
+    _need(idx, "idx", dtype=torch.int32, ndim=3, device=q.device)
+    if K_lead is None:
+        _check(lib.loki_decode(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(V), _ptr(out), _ptr(idx),
+                               B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(), _stream(q)))
+    else:
+        _need(K_lead, "K_lead", dtype=q.dtype, ndim=4, device=q.device)
+        if tuple(K_lead.shape[:3]) != (B, Hkv, S):
+            raise ValueError("K_lead must be [B, Hkv, S, R]")
+        _check(lib.loki_decode_lead(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead), K_lead.shape[3],
+                                    _ptr(V), _ptr(out), _ptr(idx), B, Hq, Hkv, S, d, r, k, dt,
+                                    _ptr(ws), ws.numel(), _stream(q)))
+    return out, idx
+
+
+def loki_scores(q, P, K_rot, r: int, workspace=None):
+    """Approximate scores ``[B,Hq,S]`` fp32 over the leading ``r`` rotated dims."""
+    B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
+    lib = load_library()
+    dt = _dtype_code(q)
+    nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, max(1, min(r, d)), 1, dt))
+    ws = _workspace(nbytes, q.device, workspace)
+    s = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib.loki_scores(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(s), B, Hq, Hkv, S, d, r, dt,
+                           _ptr(ws), ws.numel(), _stream(q)))
+    return s
+
+
+def loki_select_topk(scores: torch.Tensor, k: int, workspace=None) -> torch.Tensor:
+    """Top-k indices (ascending, ties -> lower index) of each row of fp32 ``scores [..., S]``."""
+    _need(scores, "scores", dtype=torch.float32)
+    S = scores.shape[-1]
+    rows = scores.numel() // max(S, 1)
+    lib = load_library()
+    nbytes = int(lib.loki_select_workspace_bytes(rows, S, k))
+    ws = _workspace(nbytes, scores.device, workspace)
+    idx = torch.empty((*scores.shape[:-1], k), dtype=torch.int32, device=scores.device)
+    _check(lib.loki_select_topk(_ptr(scores), _ptr(idx), rows, S, k, _ptr(ws), ws.numel(),
+                                _stream(scores)))
+    return idx
+
+
+def loki_attend(q, P, K_rot, V, idx, workspace=None):
+    """Exact softmax attention over a given kept set ``idx [B,Hq,k]`` (int32)."""
+    B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
+    _need(V, "V", dtype=q.dtype, ndim=4, device=q.device)
+    _need(idx, "idx", dtype=torch.int32, ndim=3, device=q.device)
+    k = idx.shape[-1]
+    lib = load_library()
+    dt = _dtype_code(q)
+    nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, d, k, dt))
+    ws = _workspace(nbytes, q.device, workspace)
+    out = torch.empty_like(q)
+    _check(lib.loki_attend(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(V), _ptr(idx), _ptr(out),
+                           B, Hq, Hkv, S, d, k, dt, _ptr(ws), ws.numel(), _stream(q)))
+    return out

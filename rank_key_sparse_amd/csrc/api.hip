@@ -1,0 +1,265 @@
+// C ABI of libloki: argument validation (host only, before any HIP call),
+// workspace carving, and the launch sequence of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "../../include/loki.h"
+#include "internal.h"
+
+using namespace loki;
+
+namespace {
+
+constexpr int64_t kMaxS = int64_t(1) << 24;
+constexpr int64_t kMaxRows = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+loki_status check_dtype(loki_dtype dt) {
+  return (dt == LOKI_F32 || dt == LOKI_BF16) ? LOKI_OK : LOKI_ERR_DTYPE;
+}
+
+// Sizes shared by the decode family.
+loki_status check_sizes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || d < 1) return LOKI_ERR_SHAPE;
+  if (Hq % Hkv != 0) return LOKI_ERR_SHAPE;
+  if ((int64_t)S > kMaxS || (int64_t)B * Hq > kMaxRows) return LOKI_ERR_SHAPE;
+  if (d != 64 && d != 128) return LOKI_ERR_UNSUPPORTED;
+  if (Hq / Hkv > kMaxGroup) return LOKI_ERR_UNSUPPORTED;
+  return LOKI_OK;
+}
+
+loki_status check_workspace(void* ws, size_t have, size_t need) {
+  if (have < need) return LOKI_ERR_WORKSPACE;
+  if (need > 0 && ws == nullptr) return LOKI_ERR_NULL;
+  if (!aligned16(ws)) return LOKI_ERR_ALIGN;
+  return LOKI_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+loki_status from_hip(hipError_t e) { return e == hipSuccess ? LOKI_OK : LOKI_ERR_HIP; }
+
+#define LOKI_TRY(expr)                          \
+  do {                                          \
+    const loki_status s_ = (expr);              \
+    if (s_ != LOKI_OK) return s_;               \
+  } while (0)
+
+#define LOKI_HIP(expr)                          \
+  do {                                          \
+    const hipError_t e_ = (expr);               \
+    if (e_ != hipSuccess) return LOKI_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int loki_abi_version(void) { return LOKI_ABI_VERSION; }
+
+const char* loki_status_str(int s) {
+  switch (s) {
+    case LOKI_OK: return "ok";
+    case LOKI_ERR_NULL: return "a required pointer is NULL";
+    case LOKI_ERR_SHAPE: return "invalid sizes (a size < 1, too large, or Hq not a multiple of Hkv)";
+    case LOKI_ERR_RANGE: return "r must be in [1, d] and k in [1, S]";
+    case LOKI_ERR_DTYPE: return "unknown dtype";
+    case LOKI_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case LOKI_ERR_WORKSPACE: return "workspace too small";
+    case LOKI_ERR_UNSUPPORTED: return "unsupported configuration (d must be 64 or 128, Hq/Hkv <= 16)";
+    case LOKI_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case LOKI_ERR_INTERNAL: return "internal error";
+    default: return "unknown status";
+  }
+}
+
+static loki_status check_project(const void* K, const void* P, void* K_rot, int32_t B, int32_t Hkv,
+                          int32_t S, int32_t d, loki_dtype dt) {
+  LOKI_TRY(check_dtype(dt));
+  if (!K || !P || !K_rot) return LOKI_ERR_NULL;
+  if (B < 1 || Hkv < 1 || S < 1 || d < 1) return LOKI_ERR_SHAPE;
+  if ((int64_t)B * Hkv > kMaxRows || (int64_t)S > kMaxS) return LOKI_ERR_SHAPE;
+  if (d != 64 && d != 128) return LOKI_ERR_UNSUPPORTED;
+  if (!aligned16(K) || !aligned16(P) || !aligned16(K_rot)) return LOKI_ERR_ALIGN;
+  return LOKI_OK;
+}
+
+// R of a lead-dims copy; r = 0 skips the r <= R check.
+static loki_status check_lead(const void* K_lead, int32_t R, int32_t d, int32_t r, loki_dtype dt) {
+  if (!K_lead) return LOKI_ERR_NULL;
+  if (R < 1 || R > d || r > R) return LOKI_ERR_RANGE;
+  if ((R * (dt == LOKI_F32 ? 4 : 2)) % 16 != 0) return LOKI_ERR_UNSUPPORTED;
+  if (!aligned16(K_lead)) return LOKI_ERR_ALIGN;
+  return LOKI_OK;
+}
+
+loki_status loki_project_keys(const void* K, const void* P, void* K_rot, int32_t B, int32_t Hkv,
+                              int32_t S, int32_t d, loki_dtype dt, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_project(K, P, K_rot, B, Hkv, S, d, dt));
+    return from_hip(launch_project(K, P, K_rot, nullptr, 0, B, Hkv, S, d, (int)dt, stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, void* K_lead,
+                                   int32_t R, int32_t B, int32_t Hkv, int32_t S, int32_t d,
+                                   loki_dtype dt, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_project(K, P, K_rot, B, Hkv, S, d, dt));
+    LOKI_TRY(check_lead(K_lead, R, d, 0, dt));
+    return from_hip(launch_project(K, P, K_rot, K_lead, R, B, Hkv, S, d, (int)dt, stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+size_t loki_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                                   int32_t r, int32_t k, loki_dtype dt) {
+  if (check_dtype(dt) != LOKI_OK || check_sizes(B, Hq, Hkv, S, d) != LOKI_OK) return 0;
+  if (r < 1 || r > d || k < 1 || k > S) return 0;
+  DecodePlan p;
+  if (!make_decode_plan(p, B, Hq, Hkv, S, d, r, k, (int)dt)) return 0;
+  return p.bytes;
+}
+
+static loki_status decode_impl(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                               int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
+                               int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                               loki_dtype dt, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  LOKI_TRY(check_dtype(dt));
+  if (!q || !P || !K_rot || !V || !out || !idx) return LOKI_ERR_NULL;
+  LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
+  if (r < 1 || r > d || k < 1 || k > S) return LOKI_ERR_RANGE;
+  if (!aligned16(q) || !aligned16(P) || !aligned16(K_rot) || !aligned16(V) || !aligned16(out) ||
+      !aligned16(idx))
+    return LOKI_ERR_ALIGN;
+  if (K_lead) LOKI_TRY(check_lead(K_lead, R, d, r, dt));
+  DecodePlan p;
+  if (!make_decode_plan(p, B, Hq, Hkv, S, d, r, k, (int)dt)) return LOKI_ERR_INTERNAL;
+  LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+  float* qrot = at<float>(workspace, p.off_qrot);
+  uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
+  uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
+  uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
+  float* part = at<float>(workspace, p.off_part);
+  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+  if (K_lead) LOKI_HIP(launch_scores(p, K_lead, R, qrot, qsplit, keys, true, p.Sp, stream));
+  else LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, keys, true, p.Sp, stream));
+  LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+  LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream));
+  return LOKI_OK;
+}
+
+loki_status loki_decode(const void* q, const void* P, const void* K_rot, const void* V, void* out,
+                        int32_t* idx, int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                        int32_t r, int32_t k, loki_dtype dt, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return decode_impl(q, P, K_rot, nullptr, 0, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                             int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
+                             int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                             loki_dtype dt, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  try {
+    if (!K_lead) return LOKI_ERR_NULL;
+    return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_scores(const void* q, const void* P, const void* K_rot, float* scores, int32_t B,
+                        int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, loki_dtype dt,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_dtype(dt));
+    if (!q || !P || !K_rot || !scores) return LOKI_ERR_NULL;
+    LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
+    if (r < 1 || r > d) return LOKI_ERR_RANGE;
+    if (!aligned16(q) || !aligned16(P) || !aligned16(K_rot) || !aligned16(scores))
+      return LOKI_ERR_ALIGN;
+    DecodePlan p;
+    if (!make_decode_plan(p, B, Hq, Hkv, S, d, r, 1, (int)dt)) return LOKI_ERR_INTERNAL;
+    LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+    float* qrot = at<float>(workspace, p.off_qrot);
+    uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
+    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+    LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, scores, false, S, stream));
+    return LOKI_OK;
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+size_t loki_select_workspace_bytes(int32_t rows, int32_t S, int32_t k) {
+  if (rows < 1 || rows > kMaxRows || S < 1 || (int64_t)S > kMaxS || k < 1 || k > S) return 0;
+  SelectPlan p;
+  if (!make_select_plan(p, rows, S, k)) return 0;
+  return p.bytes;
+}
+
+loki_status loki_select_topk(const float* scores, int32_t* idx, int32_t rows, int32_t S, int32_t k,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (!scores || !idx) return LOKI_ERR_NULL;
+    if (rows < 1 || S < 1 || rows > kMaxRows || (int64_t)S > kMaxS) return LOKI_ERR_SHAPE;
+    if (k < 1 || k > S) return LOKI_ERR_RANGE;
+    if (!aligned16(scores) || !aligned16(idx)) return LOKI_ERR_ALIGN;
+    SelectPlan p;
+    if (!make_select_plan(p, rows, S, k)) return LOKI_ERR_INTERNAL;
+    LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+    uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
+    uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
+    LOKI_HIP(launch_scores_to_keys(scores, keys, rows, S, p.Sp, stream));
+    LOKI_HIP(launch_select(rows, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+    return LOKI_OK;
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_attend(const void* q, const void* P, const void* K_rot, const void* V,
+                        const int32_t* idx, void* out, int32_t B, int32_t Hq, int32_t Hkv,
+                        int32_t S, int32_t d, int32_t k, loki_dtype dt, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_dtype(dt));
+    if (!q || !P || !K_rot || !V || !idx || !out) return LOKI_ERR_NULL;
+    LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
+    if (k < 1 || k > S) return LOKI_ERR_RANGE;
+    if (!aligned16(q) || !aligned16(P) || !aligned16(K_rot) || !aligned16(V) || !aligned16(out) ||
+        !aligned16(idx))
+      return LOKI_ERR_ALIGN;
+    DecodePlan p;
+    if (!make_decode_plan(p, B, Hq, Hkv, S, d, d, k, (int)dt)) return LOKI_ERR_INTERNAL;
+    LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+    float* qrot = at<float>(workspace, p.off_qrot);
+    uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
+    uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
+    float* part = at<float>(workspace, p.off_part);
+    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+    LOKI_HIP(launch_idx_to_bitmap(p, idx, bitmap, stream));
+    LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream));
+    return LOKI_OK;
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

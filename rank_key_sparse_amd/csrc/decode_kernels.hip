@@ -1,0 +1,956 @@
+// gfx950 kernels of one low-rank-key sparse decode step.
+//
+// Stages (Loki page, abstract; AQUA page, related work on LoKi attention and
+// preliminaries eqs. 3-5):
+//   qrot     q_rot = q P[kv] in fp32                         (one block per (b, kv))
+//   scores   s_j = q_rot[:r] . K_rot[j, :r] for all tokens   (HBM stream of the r-dim prefix)
+//   select   per query head, the k largest s_j -> idx, bitmap (radix/bucket select)
+//   attend   exact scores, softmax and V-sum over the union of the group's kept
+//            tokens, split over token chunks -> (max, sum, acc) partials
+//   combine  log-sum-exp merge of the chunk partials -> out
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace loki {
+
+// Global -> LDS copy of n16 16-byte words by nthr threads with 8 loads per
+// thread in flight before the first LDS store (a plain loop would wait for
+// each load in turn).
+__device__ __forceinline__ void copy16_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src,
+                                              int n16, int tid, int nthr) {
+  for (int base = 0; base < n16; base += nthr * 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * nthr + tid;
+      v[u] = (i < n16) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * nthr + tid;
+      if (i < n16) dst[i] = v[u];
+    }
+  }
+}
+
+// ============================================================================
+// q rotation: q_rot[b, kv*G+g, c] = sum_j q[b, kv*G+g, j] * P[kv, j, c]
+// One block of 256 threads per (b, kv): P[kv] and the G queries are staged
+// in LDS with 16-byte loads; thread (c, js) sums a contiguous slice of j for
+// every head, and the slices are added in slice order.  The block also
+// clears the attention-merge counter of its (b, kv) group for this call.
+// ============================================================================
+template <typename T, int GT>
+__global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
+                                                   float* __restrict__ qrot,
+                                                   bf16_t* __restrict__ qsplit,
+                                                   uint32_t* __restrict__ counters, int Hq, int Hkv,
+                                                   int d) {
+  extern __shared__ __align__(16) unsigned char qrot_lds[];
+  T* sP = reinterpret_cast<T*>(qrot_lds);                                     // [d][d]
+  float* qs = reinterpret_cast<float*>(qrot_lds + (size_t)d * d * sizeof(T));  // [GT][d]
+  float* red = reinterpret_cast<float*>(qrot_lds);                            // reuses sP
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.x, b = bk / Hkv, kv = bk % Hkv;
+  const size_t qbase = ((size_t)b * Hq + (size_t)kv * G) * d;
+  const int tid = threadIdx.x;
+  if (tid == 0 && counters) counters[bk] = 0u;
+  copy16_to_lds(reinterpret_cast<uint4*>(sP), reinterpret_cast<const uint4*>(P + (size_t)kv * d * d),
+                d * d * (int)sizeof(T) / 16, tid, 256);
+  for (int i = tid; i < GT * d; i += 256) qs[i] = (i < G * d) ? to_f32(q[qbase + i]) : 0.f;
+  __syncthreads();
+  const int JS = 256 / d, J = d / JS;
+  const int c = tid % d, js = tid / d, j0 = js * J;
+  float acc[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) acc[g] = 0.f;
+#pragma unroll 8
+  for (int jj = 0; jj < J; ++jj) {
+    const int j = j0 + jj;
+    const float pj = to_f32(sP[j * d + c]);
+#pragma unroll
+    for (int g = 0; g < GT; ++g) acc[g] = fmaf(qs[g * d + j], pj, acc[g]);
+  }
+  __syncthreads();  // sP is no longer read; reuse it for the slice sums
+#pragma unroll
+  for (int g = 0; g < GT; ++g) red[(js * GT + g) * d + c] = acc[g];
+  __syncthreads();
+  if (js == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (g >= G) break;
+      float v = red[g * d + c];
+      for (int t = 1; t < JS; ++t) v += red[(t * GT + g) * d + c];
+      qrot[qbase + (size_t)g * d + c] = v;
+      if (qsplit) {
+        // three-way bf16 split v = h + m + l (each residual exact in fp32),
+        // plus a zero row, as MFMA operands: qsplit[row][part][c]
+        bf16_t* o = qsplit + (qbase + (size_t)g * d) * 4 + c;
+        const bf16_t h = f32_to_bf16(v);
+        const float r1 = v - to_f32(h);
+        const bf16_t mid = f32_to_bf16(r1);
+        const bf16_t lo = f32_to_bf16(r1 - to_f32(mid));
+        o[0] = h;
+        o[d] = mid;
+        o[2 * d] = lo;
+        o[3 * d] = 0;
+      }
+    }
+  }
+}
+
+// ============================================================================
+// Approximate scores over the leading r rotated dimensions.
+// The source is either K_rot itself (row stride d) or a lead-dims copy
+// K_lead holding only the leading R >= r rotated dims of each token (row
+// stride R), which turns the strided prefix reads into a dense stream.
+// A token's r-dim prefix is LPT 16-byte granules, read by LPT adjacent lanes;
+// each lane holds its granule's slice of q_rot for all G heads of the group,
+// so the prefix is streamed from HBM once per (b, kv) group.  q_rot entries at
+// c >= r are zero, so a partially used granule adds exact zeros.
+// Output: order-preserving keys (decode) or the fp32 scores themselves.
+// ============================================================================
+template <typename T, int LPT, int GT>
+__global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ src,
+                                                    const float* __restrict__ qrot,
+                                                    void* __restrict__ out, int as_keys,
+                                                    int out_stride, int Hq, int Hkv, int S, int d,
+                                                    int ld, int r, int SC) {
+  constexpr int EPL = Gran<T>::N;
+  constexpr int TPI = 256 / LPT;  // tokens per block pass
+  constexpr int U = 8;            // passes whose loads are in flight together
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
+  const int t0 = blockIdx.x * SC, t1 = min(S, t0 + SC);
+  const int gran = threadIdx.x % LPT, tsub = threadIdx.x / LPT;
+
+  float qv[GT][EPL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int c = gran * EPL + i;
+      qv[g][i] = (g < G && c < r) ? qrot[((size_t)b * Hq + (size_t)kv * G + g) * d + c] : 0.f;
+    }
+
+  const T* base = src + (size_t)bk * S * ld + gran * EPL;
+  const size_t orow0 = ((size_t)b * Hq + (size_t)kv * G) * out_stride;
+  for (int tb = t0; tb < t1; tb += TPI * U) {
+    uint4 buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u * TPI + tsub;
+      buf[u] = (t < t1) ? ldg16(base + (size_t)t * ld) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u * TPI + tsub;
+      float x[EPL];
+      Gran<T>::unpack(buf[u], x);
+      float s[GT];
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) a = fmaf(qv[g][i], x[i], a);
+        s[g] = group_sum<LPT>(a);
+      }
+      if (t < t1) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+          if (g % LPT == gran && g < G) {
+            const size_t o = orow0 + (size_t)g * out_stride + t;
+            if (as_keys) static_cast<uint32_t*>(out)[o] = score_key(s[g]);
+            else static_cast<float*>(out)[o] = s[g];
+          }
+        }
+      }
+    }
+  }
+}
+
+// fp32 scores -> keys, for the stand-alone selection entry point.
+__global__ __launch_bounds__(256) void scores_to_keys_kernel(const float* __restrict__ s,
+                                                             uint32_t* __restrict__ keys, int S,
+                                                             int Sp) {
+  const int row = blockIdx.y;
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < S; j += gridDim.x * 256)
+    keys[(size_t)row * Sp + j] = score_key(s[(size_t)row * S + j]);
+}
+
+// ============================================================================
+// Top-k selection, one block of 1024 threads per query head.
+//
+// 1. min/max key of the row;
+// 2. histogram of the scores in NB equal-width value bins over [min, max]
+//    (a monotone map, so bins order like keys);
+// 3. scan bins from the top to find the bin t holding the k-th largest;
+// 4. resolve the exact k-th key K* inside bin t: rank the (few) candidates
+//    of bin t by (key desc, index asc) in LDS; if bin t is too full (heavily
+//    tied or degenerate scores) run an exact 11/11/10-bit MSB radix select
+//    restricted to bin t instead;
+// 5. emit, in index order: key > K*, or key == K* among the first `quota`
+//    such tokens (lower index wins).  Each wave owns a 64-aligned token
+//    segment, so the kept-token bitmap words are written without atomics.
+// Keys live in LDS when the row fits (IN_LDS), else every pass re-reads them
+// from global memory (L2 / Infinity Cache).
+// ============================================================================
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kNB = 2048;   // value bins (2 per thread in the threshold scan)
+constexpr int kCap = 1024;  // candidates ranked in LDS (2 * kCap words alias the bins)
+constexpr int kRankLds = 256;  // rank limit when the row itself is in LDS
+
+struct SelScratch {
+  uint32_t red[2][kSelWaves];
+  int scan[kSelWaves];
+  int wgt[kSelWaves], weq[kSelWaves], selb[kSelWaves], eqb[kSelWaves];
+  uint32_t kmin, kmax, kstar;
+  int t, above, quota, ccount;
+};
+
+// Inclusive prefix sum over the block in thread order.
+__device__ __forceinline__ int block_incl_scan(int v, SelScratch& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) sh.scan[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += sh.scan[w];
+  __syncthreads();
+  return v + add;
+}
+
+// Find, scanning bins from the top, the bin holding the `want`-th largest key
+// (1-based).  Sets sh.t to that bin and sh.above to the count in higher bins.
+__device__ __forceinline__ void find_threshold(const uint32_t* hist, int want, SelScratch& sh) {
+  const int hb = kNB - 1 - 2 * (int)threadIdx.x;
+  const int hhi = (int)hist[hb], hlo = (int)hist[hb - 1];
+  const int incl = block_incl_scan(hhi + hlo, sh);
+  const int above = incl - hhi - hlo;
+  if (above < want && above + hhi >= want) { sh.t = hb; sh.above = above; }
+  else if (above + hhi < want && above + hhi + hlo >= want) { sh.t = hb - 1; sh.above = above + hhi; }
+  __syncthreads();
+}
+
+struct Binner {
+  float fmin, scale;
+  bool degenerate;
+  __device__ __forceinline__ int operator()(uint32_t key) const {
+    if (degenerate) return 0;
+    const int b = (int)((key_score(key) - fmin) * scale);
+    return b < kNB - 1 ? b : kNB - 1;
+  }
+};
+
+// Calls f(j, key) for every token j < S (in no particular order): each thread
+// reads 4 consecutive keys per 16-byte load with UB loads in flight.
+template <bool IN_LDS, typename F>
+__device__ __forceinline__ void for_each_key(const uint32_t* rk, const uint32_t* lk, int S, int Sp,
+                                             F&& f) {
+  constexpr int UB = IN_LDS ? 4 : 8;
+  const uint4* src = reinterpret_cast<const uint4*>(IN_LDS ? lk : rk);
+  const int n4 = Sp >> 2, tid = threadIdx.x;
+  for (int base = 0; base < n4; base += kSelThreads * UB) {
+    uint4 v[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int i = base + u * kSelThreads + tid;
+      v[u] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int j = (base + u * kSelThreads + tid) << 2;
+      if (j < S) f(j, v[u].x);
+      if (j + 1 < S) f(j + 1, v[u].y);
+      if (j + 2 < S) f(j + 2, v[u].z);
+      if (j + 3 < S) f(j + 3, v[u].w);
+    }
+  }
+}
+
+template <bool IN_LDS>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __restrict__ keys, int S,
+                                                             int Sp, int k, int W,
+                                                             int32_t* __restrict__ idx,
+                                                             uint32_t* __restrict__ bitmap) {
+  extern __shared__ __align__(16) uint32_t dyn[];
+  __shared__ SelScratch sh;
+  uint32_t* lk = dyn;                          // [Sp] keys (IN_LDS only)
+  uint32_t* hist = dyn + (IN_LDS ? Sp : 0);    // [kNB]; later cand keys / indices
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* rk = keys + (size_t)row * Sp;
+  int32_t* orow = idx + (size_t)row * k;
+  uint32_t* brow = bitmap + (size_t)row * W;
+
+  if (k >= S) {  // every token kept
+    for (int j = tid; j < S; j += kSelThreads) orow[j] = j;
+    for (int w = tid; w < W; w += kSelThreads) {
+      const int lo = 32 * w;
+      brow[w] = (lo + 32 <= S) ? 0xffffffffu : (lo >= S ? 0u : ((1u << (S - lo)) - 1u));
+    }
+    return;
+  }
+
+  // 1. min / max, and the copy of the row to LDS
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(rk);
+    uint4* dst = reinterpret_cast<uint4*>(lk);
+    const int n4 = Sp >> 2;  // Sp is a multiple of 64
+    for (int base = 0; base < n4; base += kSelThreads * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kSelThreads + tid;
+        v[u] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = base + u * kSelThreads + tid;
+        if (i >= n4) continue;
+        if constexpr (IN_LDS) dst[i] = v[u];
+        const int j = i << 2;
+        if (j < S) { mn = min(mn, v[u].x); mx = max(mx, v[u].x); }
+        if (j + 1 < S) { mn = min(mn, v[u].y); mx = max(mx, v[u].y); }
+        if (j + 2 < S) { mn = min(mn, v[u].z); mx = max(mx, v[u].z); }
+        if (j + 3 < S) { mn = min(mn, v[u].w); mx = max(mx, v[u].w); }
+      }
+    }
+  }
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
+  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  for (int i = tid; i < kNB; i += kSelThreads) hist[i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = sh.red[0][0], c = sh.red[1][0];
+    for (int w = 1; w < kSelWaves; ++w) { a = min(a, sh.red[0][w]); c = max(c, sh.red[1][w]); }
+    sh.kmin = a; sh.kmax = c;
+  }
+  __syncthreads();
+
+  // 2. value histogram
+  Binner bin;
+  {
+    const float fmin = key_score(sh.kmin), fmax = key_score(sh.kmax);
+    const float range = fmax - fmin;
+    const float scale = (float)kNB / range;
+    bin.fmin = fmin;
+    bin.scale = scale;
+    bin.degenerate = !(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f);
+  }
+  for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) { atomicAdd(&hist[bin(v)], 1u); });
+  __syncthreads();
+
+  // 3. threshold bin
+  find_threshold(hist, k, sh);
+  const int tb = sh.t;
+  const int need = k - sh.above;  // 1 <= need <= hist[tb]
+  const int nc = (int)hist[tb];
+  __syncthreads();  // hist is reused below
+
+  // 4. exact k-th key inside bin tb.  Ranking costs nc^2 compares spread over
+  // the block; the radix passes cost three sweeps of the row.
+  if (nc <= (IN_LDS ? kRankLds : kCap)) {
+    uint32_t* ck = hist;
+    uint32_t* ci = hist + kCap;
+    if (tid == 0) sh.ccount = 0;
+    __syncthreads();
+    for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int j, uint32_t v) {
+      if (bin(v) == tb) {
+        const int p = atomicAdd(&sh.ccount, 1);
+        ck[p] = v;
+        ci[p] = (uint32_t)j;
+      }
+    });
+    __syncthreads();
+    for (int i = tid; i < nc; i += kSelThreads) {
+      const uint32_t vi = ck[i], ii = ci[i];
+      int gtc = 0, rank = 0;
+      for (int c = 0; c < nc; ++c) {
+        const uint32_t vc = ck[c], ic = ci[c];
+        gtc += (vc > vi);
+        rank += (vc > vi) || (vc == vi && ic < ii);
+      }
+      if (rank == need - 1) { sh.kstar = vi; sh.quota = need - gtc; }
+    }
+    __syncthreads();
+  } else {
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = need;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = shifts[pass];
+      const uint32_t dm = (1u << widths[pass]) - 1u;
+      for (int i = tid; i < kNB; i += kSelThreads) hist[i] = 0u;
+      __syncthreads();
+      for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) {
+        if (bin(v) == tb && (v & pmask) == prefix) atomicAdd(&hist[(v >> sft) & dm], 1u);
+      });
+      __syncthreads();
+      find_threshold(hist, rem, sh);
+      rem -= sh.above;
+      prefix |= (uint32_t)sh.t << sft;
+      pmask |= dm << sft;
+      __syncthreads();
+    }
+    if (tid == 0) { sh.kstar = prefix; sh.quota = rem; }
+    __syncthreads();
+  }
+  const uint32_t kstar = sh.kstar;
+  const int quota = sh.quota;
+
+  // 5. emit in index order; each wave owns a 64-aligned segment and reads
+  // UE 64-token steps ahead
+  constexpr int UE = 8;
+  const int SEG = (S + kSelWaves * 64 - 1) / (kSelWaves * 64) * 64;
+  const int wb = wave * SEG, we = min(S, wb + SEG);
+  auto KEY = [&](int j) -> uint32_t {
+    if constexpr (IN_LDS) return lk[j];
+    else return rk[j];
+  };
+  int ngt = 0, neq = 0;
+  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
+    uint32_t v[UE];
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int j = j0 + 64 * u + lane;
+      v[u] = (j < we) ? KEY(j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const bool ok = j0 + 64 * u + lane < we;
+      ngt += __popcll(__ballot(ok && v[u] > kstar));
+      neq += __popcll(__ballot(ok && v[u] == kstar));
+    }
+  }
+  if (lane == 0) { sh.wgt[wave] = ngt; sh.weq[wave] = neq; }
+  __syncthreads();
+  if (tid == 0) {
+    int eqb = 0, selb = 0;
+    for (int w = 0; w < kSelWaves; ++w) {
+      sh.eqb[w] = eqb;
+      sh.selb[w] = selb;
+      const int take = min(max(quota - eqb, 0), sh.weq[w]);
+      selb += sh.wgt[w] + take;
+      eqb += sh.weq[w];
+    }
+  }
+  __syncthreads();
+  int selrun = sh.selb[wave], eqrun = sh.eqb[wave];
+  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
+    uint32_t v[UE];
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int j = j0 + 64 * u + lane;
+      v[u] = (j < we) ? KEY(j) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int js = j0 + 64 * u;  // 64-aligned step start
+      if (js >= we) break;         // uniform across the wave
+      const int j = js + lane;
+      const bool ok = j < we;
+      const bool gt = ok && v[u] > kstar, eq = ok && v[u] == kstar;
+      const uint64_t eqm = __ballot(eq);
+      const bool take = gt || (eq && eqrun + bits_below(eqm) < quota);
+      const uint64_t sm = __ballot(take);
+      if (take) orow[selrun + bits_below(sm)] = j;
+      if (lane == 0) {
+        brow[js >> 5] = (uint32_t)sm;
+        brow[(js >> 5) + 1] = (uint32_t)(sm >> 32);
+      }
+      selrun += __popcll(sm);
+      eqrun += __popcll(eqm);
+    }
+  }
+}
+
+// Caller-given kept sets -> bitmap (stand-alone attention entry point).
+// One block per query head clears its row, then sets the bits of in-range
+// entries (duplicates merge).
+__global__ __launch_bounds__(256) void idx_to_bitmap_kernel(const int32_t* __restrict__ idx,
+                                                            uint32_t* __restrict__ bitmap, int S,
+                                                            int k, int W) {
+  const int row = blockIdx.x;
+  uint32_t* brow = bitmap + (size_t)row * W;
+  for (int w = threadIdx.x; w < W; w += 256) brow[w] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += 256) {
+    const int j = idx[(size_t)row * k + i];
+    if (j >= 0 && j < S) atomicOr(&brow[j >> 5], 1u << (j & 31));
+  }
+}
+
+// ============================================================================
+// Exact attention over the kept tokens.
+// Each wavefront independently owns NT consecutive tokens of one (b, kv)
+// group; the four waves of a block own four consecutive spans.  A wave reads
+// the G heads' bitmap words for its span, builds the union list (token, head
+// mask) in LDS, and reads every listed K_rot row and V row ONCE for all G
+// heads (RL lanes per row, 16 bytes each, U row-passes in flight):
+//   pass 1: e = q_rot . K_rot[j] * log2(e)/sqrt(d)  (-inf for heads that did
+//           not keep j) into LDS;
+//   per head: m = max e, w = 2^(e - m), l = sum w;
+//   pass 2: acc = sum w V[j].
+// No block barrier is needed until the end, where the four waves' (m, l,
+// acc) are merged by log-sum-exp and one partial per (head, block) is
+// written.  NT shrinks as G grows so the per-wave score buffer stays 4 KB.
+// ============================================================================
+template <int GT> struct AttendTokens { static constexpr int value = GT <= 4 ? 256 : 1024 / GT; };
+
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(256) void attend_kernel(const T* __restrict__ K_rot,
+                                                     const T* __restrict__ V,
+                                                     const float* __restrict__ qrot,
+                                                     const uint32_t* __restrict__ bitmap,
+                                                     float* __restrict__ part, int Hq, int Hkv,
+                                                     int S, int W, int NC, float scale_log2) {
+  constexpr int EPL = Gran<T>::N;
+  constexpr int RL = D * (int)sizeof(T) / 16;  // lanes per row
+  constexpr int RPW = 64 / RL;                 // rows per wave pass
+  constexpr int U = 8;                         // row passes in flight
+  constexpr int NT = AttendTokens<GT>::value;  // tokens per wave
+  constexpr int NSTEP = NT / 64;
+  __shared__ int s_tok[4][NT];
+  __shared__ uint16_t s_hm[4][NT];
+  __shared__ __align__(16) float s_e[4][NT * GT];
+  __shared__ float s_m[4][GT], s_l[4][GT];
+  __shared__ __align__(16) float s_acc[4][GT][D];
+
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = (blockIdx.x * 4 + wave) * NT;
+  const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
+  int* tok = s_tok[wave];
+  uint16_t* hmk = s_hm[wave];
+  float* e = s_e[wave];
+
+  // bitmap words for every step and head, all loads in flight together
+  uint32_t words[NSTEP][GT];
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    const int t = t0 + 64 * st + lane;
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      words[st][g] = (g < G && t < S) ? bitmap[(head0 + g) * W + (t >> 5)] : 0u;
+  }
+  int n = 0;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    const int t = t0 + 64 * st + lane;
+    int hm = 0;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) hm |= (int)((words[st][g] >> (t & 31)) & 1u) << g;
+    const uint64_t m = __ballot(hm != 0);
+    if (hm) {
+      const int pos = n + bits_below(m);
+      tok[pos] = t;
+      hmk[pos] = (uint16_t)hm;
+    }
+    n += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int lg = lane / RL, li = lane % RL;
+  float qv[GT][EPL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) qv[g][i] = (g < G) ? qrot[(head0 + g) * D + li * EPL + i] : 0.f;
+  const size_t cbase = (size_t)bk * S * D + li * EPL;
+
+  // pass 1: exact scores
+  for (int p0 = 0; p0 < n; p0 += RPW * U) {
+    uint4 buf[U];
+    int hms[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * RPW + lg;
+      if (p < n) {
+        hms[u] = hmk[p];
+        buf[u] = ldg16(K_rot + cbase + (size_t)tok[p] * D);
+      } else {
+        hms[u] = 0;
+        buf[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * RPW + lg;
+      float x[EPL];
+      Gran<T>::unpack(buf[u], x);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) a = fmaf(qv[g][i], x[i], a);
+        a = group_sum<RL>(a);
+        if (p < n && g % RL == li) e[p * GT + g] = ((hms[u] >> g) & 1) ? a * scale_log2 : -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one row's temporaries live at a time
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // per-head softmax statistics of this wave's span
+  float mreg[GT], lreg[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    float mx = -INFINITY, sum = 0.f;
+    if (g < G) {
+      for (int p = lane; p < n; p += 64) mx = fmaxf(mx, e[p * GT + g]);
+      mx = wave_max(mx);
+      for (int p = lane; p < n; p += 64) {
+        const float v = e[p * GT + g];
+        const float w = (v == -INFINITY) ? 0.f : exp2f(v - mx);
+        e[p * GT + g] = w;
+        sum += w;
+      }
+      sum = wave_sum(sum);
+    }
+    mreg[g] = mx;
+    lreg[g] = sum;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // pass 2: weighted value sum
+  float acc[GT][EPL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[g][i] = 0.f;
+  for (int p0 = 0; p0 < n; p0 += RPW * U) {
+    uint4 buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * RPW + lg;
+      buf[u] = (p < n) ? ldg16(V + cbase + (size_t)tok[p] * D) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u * RPW + lg;
+      float x[EPL];
+      Gran<T>::unpack(buf[u], x);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float w = (p < n && g < G) ? e[p * GT + g] : 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[g][i] = fmaf(w, x[i], acc[g][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float v = acc[g][i];
+      for (int o = RL; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      acc[g][i] = v;
+    }
+
+  // merge the four waves' spans by log-sum-exp; one partial per (head, block)
+  if (lg == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s_acc[wave][g][li * EPL + i] = acc[g][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) { s_m[wave][g] = mreg[g]; s_l[wave][g] = lreg[g]; }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < G * D; o += 256) {
+    const int g = o / D, c = o - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (s_m[w][g] == -INFINITY) ? 0.f : exp2f(s_m[w][g] - M);
+      L = fmaf(s_l[w][g], f, L);
+      A = fmaf(s_acc[w][g][c], f, A);
+    }
+    float* pr = part + ((head0 + g) * NC + blockIdx.x) * (size_t)(D + 2);
+    pr[2 + c] = A;
+    if (c == 0) { pr[0] = M; pr[1] = L; }
+  }
+}
+
+// Log-sum-exp merge of the chunk partials: one block of d threads per head.
+// The global max over chunks is reduced first; then chunk scale factors and
+// sums are brought into LDS a tile at a time (all loads of a tile in flight)
+// and every thread accumulates its output dimension in chunk order.
+template <typename T>
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ part,
+                                                      T* __restrict__ out, int NC, int d) {
+  constexpr int TILE = 1024;
+  __shared__ float s_f[TILE];
+  __shared__ float s_l[TILE];
+  __shared__ float s_red[2];
+  const int row = blockIdx.x, c = threadIdx.x;
+  const int lane = c & 63, wave = c >> 6;
+  const size_t st = (size_t)d + 2;
+  const float* pr = part + (size_t)row * NC * st;
+  float M = -INFINITY;
+  for (int ch = c; ch < NC; ch += blockDim.x) M = fmaxf(M, pr[(size_t)ch * st]);
+  M = wave_max(M);
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = s_red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, s_red[w]);
+  float L = 0.f, a = 0.f;
+  for (int t0 = 0; t0 < NC; t0 += TILE) {
+    const int tn = min(TILE, NC - t0);
+    __syncthreads();
+    for (int i = c; i < tn; i += blockDim.x) {
+      const float m = pr[(size_t)(t0 + i) * st];
+      s_f[i] = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      s_l[i] = pr[(size_t)(t0 + i) * st + 1];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int i = 0; i < tn; ++i) {
+      const float f = s_f[i];
+      L = fmaf(s_l[i], f, L);
+      a = fmaf(pr[(size_t)(t0 + i) * st + 2 + c], f, a);
+    }
+  }
+  // a head whose kept set is empty (only possible through loki_attend with
+  // no in-range index) gets zeros
+  out[(size_t)row * d + c] = from_f32<T>(L > 0.f ? a / L : 0.f);
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+static int next_pow2(long long x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+static int chunk_for(long long S, long long groups, int lo, int hi, long long blocks) {
+  long long want = (S * groups + blocks - 1) / blocks;  // aim for >= `blocks` blocks
+  int c = next_pow2(want < 1 ? 1 : want);
+  if (c < lo) c = lo;
+  if (c > hi) c = hi;
+  return c;
+}
+
+bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r, int k, int dt) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv || (d != 64 && d != 128)) return false;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.S = S; p.d = d; p.r = r; p.k = k; p.dt = dt;
+  p.G = Hq / Hkv;
+  p.Sp = (S + 63) / 64 * 64;
+  p.W = p.Sp / 32;
+  const long long groups = (long long)B * Hkv;
+  p.SC = chunk_for(S, groups, 256, 8192, 2048);
+  p.NSC = (S + p.SC - 1) / p.SC;
+  if (dt == 1 && p.G <= 8) {
+    p.AC = 4 * kAttendMfmaTokens;  // MFMA attention: four waves per block
+  } else {
+    const int G = p.G;
+    const int nt = G <= 4 ? 256 : (G <= 8 ? 128 : 64);
+    p.AC = 4 * nt;  // vector-ALU attention: four waves per block
+  }
+  p.NAC = (S + p.AC - 1) / p.AC;
+  const size_t rows = (size_t)B * Hq;
+  size_t off = 0;
+  p.off_qrot = off;   off = align_up(off + rows * d * sizeof(float), 256);
+  p.off_qsplit = off; off = align_up(off + rows * 4 * d * sizeof(uint16_t), 256);
+  p.off_keys = off;   off = align_up(off + rows * (size_t)p.Sp * sizeof(uint32_t), 256);
+  p.off_bitmap = off; off = align_up(off + rows * (size_t)p.W * sizeof(uint32_t), 256);
+  p.off_part = off;   off = align_up(off + rows * (size_t)p.NAC * (d + 2) * sizeof(float), 256);
+  p.bytes = off;
+  return true;
+}
+
+bool make_select_plan(SelectPlan& p, int rows, int S, int k) {
+  if (rows < 1 || S < 1 || k < 1 || k > S) return false;
+  p.rows = rows; p.S = S; p.k = k;
+  p.Sp = (S + 63) / 64 * 64;
+  p.W = p.Sp / 32;
+  size_t off = 0;
+  p.off_keys = off;   off = align_up(off + (size_t)rows * p.Sp * sizeof(uint32_t), 256);
+  p.off_bitmap = off; off = align_up(off + (size_t)rows * p.W * sizeof(uint32_t), 256);
+  p.bytes = off;
+  return true;
+}
+
+template <typename F>
+static hipError_t dispatch_group(int G, F&& f) {
+  if (G <= 1) return f(std::integral_constant<int, 1>{});
+  if (G <= 2) return f(std::integral_constant<int, 2>{});
+  if (G <= 4) return f(std::integral_constant<int, 4>{});
+  if (G <= 8) return f(std::integral_constant<int, 8>{});
+  return f(std::integral_constant<int, 16>{});
+}
+
+template <typename T>
+static hipError_t qrot_t(const DecodePlan& p, const void* q, const void* P, float* qrot,
+                         bf16_t* qsplit, uint32_t* counters, hipStream_t st) {
+  return dispatch_group(p.G, [&](auto gt) {
+    constexpr int GT = decltype(gt)::value;
+    // LDS: P[kv] and the queries; the slice sums (256/d slices x GT x d fp32)
+    // reuse P's space, which is at least as large.
+    const size_t lds = (size_t)p.d * p.d * sizeof(T) + (size_t)GT * p.d * sizeof(float);
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&qrot_kernel<T, GT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return hipGetLastError();
+    hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv), dim3(256), lds, st,
+                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, counters,
+                       p.Hq, p.Hkv, p.d);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
+                       uint16_t* qsplit, uint32_t* counters, hipStream_t st) {
+  return p.dt == 0 ? qrot_t<float>(p, q, P, qrot, qsplit, counters, st)
+                   : qrot_t<bf16_t>(p, q, P, qrot, qsplit, counters, st);
+}
+
+template <typename T, int GT>
+static hipError_t scores_tg(const DecodePlan& p, const void* src, int ld, const float* qrot, void* out,
+                            bool as_keys, int out_stride, hipStream_t st) {
+  const int e = (int)sizeof(T);
+  const int gran = (p.r * e + 15) / 16;
+  const int lpt = next_pow2(gran);
+  const dim3 grid(p.NSC, p.B * p.Hkv), block(256);
+  const T* K = static_cast<const T*>(src);
+  const int ak = as_keys ? 1 : 0;
+#define LOKI_SCORE(L)                                                                         \
+  case L:                                                                                     \
+    hipLaunchKernelGGL((score_kernel<T, L, GT>), grid, block, 0, st, K, qrot, out, ak,       \
+                       out_stride, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                         \
+    break;
+  switch (lpt) {
+    LOKI_SCORE(1)
+    LOKI_SCORE(2)
+    LOKI_SCORE(4)
+    LOKI_SCORE(8)
+    LOKI_SCORE(16)
+    LOKI_SCORE(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOKI_SCORE
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const float* qrot,
+                         const uint16_t* qsplit, void* out, bool as_keys, int out_stride,
+                         hipStream_t st) {
+  if (p.dt == 1) return launch_scores_mfma(p, src, ld, qsplit, out, as_keys, out_stride, st);
+  return dispatch_group(p.G, [&](auto gt) {
+    constexpr int GT = decltype(gt)::value;
+    return p.dt == 0 ? scores_tg<float, GT>(p, src, ld, qrot, out, as_keys, out_stride, st)
+                     : scores_tg<bf16_t, GT>(p, src, ld, qrot, out, as_keys, out_stride, st);
+  });
+}
+
+static int max_lds_per_block() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 65536;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 65536;
+  return v;
+}
+
+hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, int32_t* idx,
+                         uint32_t* bitmap, hipStream_t st) {
+  const size_t static_lds = sizeof(SelScratch) + 64;
+  const size_t lds_in = ((size_t)Sp + kNB) * sizeof(uint32_t);
+  const size_t lds_out = (size_t)kNB * sizeof(uint32_t);
+  bool in_lds = lds_in + static_lds <= (size_t)max_lds_per_block();
+  if (in_lds && hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<true>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)lds_in) != hipSuccess) {
+    (void)hipGetLastError();  // clear it: the row then streams from global memory
+    in_lds = false;
+  }
+  if (in_lds) {
+    hipLaunchKernelGGL((select_kernel<true>), dim3(rows), dim3(kSelThreads), lds_in, st, keys, S, Sp,
+                       k, W, idx, bitmap);
+  } else {
+    hipLaunchKernelGGL((select_kernel<false>), dim3(rows), dim3(kSelThreads), lds_out, st, keys, S,
+                       Sp, k, W, idx, bitmap);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, int rows, int S, int Sp,
+                                 hipStream_t st) {
+  int bx = (S + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  hipLaunchKernelGGL(scores_to_keys_kernel, dim3(bx, rows), dim3(256), 0, st, scores, keys, S, Sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(idx_to_bitmap_kernel, dim3(p.B * p.Hq), dim3(256), 0, st, idx, bitmap, p.S,
+                     p.k, p.W);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t attend_td(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
+                            const uint32_t* bitmap, float* part, void* out, hipStream_t st) {
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+  hipError_t e = dispatch_group(p.G, [&](auto gt) {
+    constexpr int GT = decltype(gt)::value;
+    if (4 * AttendTokens<GT>::value != p.AC) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attend_kernel<T, D, GT>), dim3(p.NAC, p.B * p.Hkv), dim3(256), 0, st,
+                       static_cast<const T*>(K_rot), static_cast<const T*>(V), qrot, bitmap, part,
+                       p.Hq, p.Hkv, p.S, p.W, p.NAC, scale_log2);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<T>), dim3(p.B * p.Hq), dim3(D), 0, st, part, static_cast<T*>(out),
+                     p.NAC, D);
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
+                         const uint16_t* qsplit, const uint32_t* bitmap, float* part, void* out,
+                         hipStream_t st) {
+  if (p.dt == 1 && p.G <= 8) {
+    const hipError_t e = launch_attend_mfma(p, K_rot, V, qsplit, bitmap, part, st);
+    if (e != hipSuccess) return e;
+    if (p.d == 64)
+      hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(p.B * p.Hq), dim3(64), 0, st, part,
+                         static_cast<bf16_t*>(out), p.NAC, 64);
+    else
+      hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(p.B * p.Hq), dim3(128), 0, st, part,
+                         static_cast<bf16_t*>(out), p.NAC, 128);
+    return hipGetLastError();
+  }
+  if (p.dt == 0)
+    return p.d == 64 ? attend_td<float, 64>(p, K_rot, V, qrot, bitmap, part, out, st)
+                     : attend_td<float, 128>(p, K_rot, V, qrot, bitmap, part, out, st);
+  return p.d == 64 ? attend_td<bf16_t, 64>(p, K_rot, V, qrot, bitmap, part, out, st)
+                   : attend_td<bf16_t, 128>(p, K_rot, V, qrot, bitmap, part, out, st);
+}
+
+}  // namespace loki

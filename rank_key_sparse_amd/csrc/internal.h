@@ -1,0 +1,65 @@
+// Host-side plan of a decode call (workspace layout, chunking) and the
+// kernel launchers.  Shared by the C ABI and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace loki {
+
+constexpr int kMaxGroup = 16;        // largest supported Hq/Hkv
+constexpr int kAttendMfmaTokens = 256;  // tokens per wave in the MFMA attention kernel
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Everything a decode-family launch needs, derived from the sizes alone.
+struct DecodePlan {
+  int B, Hq, Hkv, S, d, r, k, G, dt;  // dt: 0 fp32, 1 bf16
+  int Sp;        // key row stride in the workspace: S rounded up to 64
+  int W;         // bitmap words per query head: Sp / 32
+  int SC, NSC;   // approximate-score kernel: tokens per block, blocks per (b,kv)
+  int AC, NAC;   // attention kernel: tokens per block, blocks per (b,kv)
+  size_t off_qrot, off_qsplit, off_keys, off_bitmap, off_part, bytes;
+};
+
+// Fills `p` from the sizes; returns false if they are out of the supported range
+// (the C ABI validates first, so this only guards internal misuse).
+bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r, int k, int dt);
+
+// Selection-only plan (loki_select_topk).
+struct SelectPlan {
+  int rows, S, Sp, W, k;
+  size_t off_keys, off_bitmap, bytes;
+};
+bool make_select_plan(SelectPlan& p, int rows, int S, int k);
+
+// ---- launchers: enqueue on `st`; return hipGetLastError() after the launches.
+// q_rot in fp32 and, when qsplit is non-null, its three-way bf16 split as
+// MFMA operands qsplit[row][part][d] (part 3 is zero).
+hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
+                       uint16_t* qsplit, uint32_t* counters, hipStream_t st);
+// Scores from `src` = K_rot (ld = d) or a lead-dims copy K_lead (ld = R >= r).
+hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const float* qrot,
+                         const uint16_t* qsplit, void* out, bool as_keys, int out_stride,
+                         hipStream_t st);
+hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys,
+                         int32_t* idx, uint32_t* bitmap, hipStream_t st);
+hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, int rows, int S, int Sp,
+                                 hipStream_t st);
+hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,
+                                hipStream_t st);
+hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
+                         const uint16_t* qsplit, const uint32_t* bitmap, float* part, void* out,
+                         hipStream_t st);
+// K_rot = K P; when K_lead is non-null its rows also receive the leading R dims.
+// MFMA paths (bf16 storage).
+hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                              void* out, bool as_keys, int out_stride, hipStream_t st);
+hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
+                              const uint16_t* qsplit, const uint32_t* bitmap, float* part,
+                              hipStream_t st);
+hipError_t launch_project(const void* K, const void* P, void* K_rot, void* K_lead, int R, int B,
+                          int Hkv, int S, int d, int dt, hipStream_t st);
+
+}  // namespace loki

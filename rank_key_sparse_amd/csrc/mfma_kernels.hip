@@ -1,0 +1,429 @@
+// MFMA forms of the two contractions of a decode step over bf16 caches:
+//   scores   s[j, h] = sum_{c<r} K[j, c] q_rot[h, c]   (all tokens j, the G heads of a group)
+//   exact    e[j, h] = sum_{c<d} K_rot[j, c] q_rot[h, c] (the kept tokens)
+// Both are [tokens x dims] x [dims x heads] products.  With G query heads per
+// key row they cost 4G flops per cached element, which on the vector ALUs
+// (no packed fp32) would take most of the issue rate at HBM speed; on
+// v_mfma_f32_16x16x32_bf16 they cost a few instructions per 16 tokens.
+//
+// q_rot is fp32 and must not be rounded to bf16: the rotation kernel splits
+// it into three bf16 parts q = h + m + l (|q - h - m - l| <= 2^-27 |q|),
+// placed here in separate B columns (column n = head (n % 4) + 4 * split, n = 12..15 zero), so that
+// one MFMA yields the three partial products of four heads with exact
+// bf16 x bf16 products and fp32 accumulation; two DPP row shifts then add
+// each head's three columns.
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, element i):
+//   A[m][k] : m = l % 16, k = 8 (l / 16) + i
+//   B[k][n] : n = l % 16, k = 8 (l / 16) + i
+//   D[m][n] : n = l % 16, m = 4 (l / 16) + v   (v = 0..3, one fp32 each)
+// The mapping of k to head dimensions is free as long as A and B agree; each
+// kernel picks the one that keeps a lane's loads contiguous.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <type_traits>
+
+#include "common.h"
+#include "internal.h"
+
+namespace loki {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Lane n (< 4) of each 16-lane row receives x[n] + x[n+4] + x[n+8] + x[n+12]
+// of its row: DPP row_shl:4 then row_shl:8 (lane i reads lane i + k of its
+// row; reads past the row's end give 0).
+__device__ __forceinline__ float add_split_columns(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xF, 0xF, false));
+  return x;
+}
+
+// B operand of column group `grp` for the 8 dims starting at dim0 (a
+// multiple of 8): column n = head 4 grp + (n % 4), split part n / 4 (part 3
+// is the zero row), read with one 16-byte load from qsplit[row][part][d].
+// Elements at dims >= r are zeroed.
+__device__ __forceinline__ bf16x8_t q_operand(const uint16_t* __restrict__ qsplit, size_t head0, int d,
+                                              int G, int r, int grp, int n, int dim0) {
+  const int g = 4 * grp + (n & 3), part = n >> 2;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (g < G && dim0 < r) v = ldg16(qsplit + ((head0 + g) * 4 + part) * (size_t)d + dim0);
+  const int valid = r - dim0;
+  if (valid < 8) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t keep = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
+      w[e] &= keep;
+    }
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return as_bf16x8(v);
+}
+
+// ============================================================================
+// Approximate scores, bf16 source (K_rot with ld = d, or K_lead with ld = R).
+// Each wave takes 16-token tiles of the block's chunk; for k-step s a lane
+// loads dims [32 s + 8 (l/16), +8) of token l % 16, so one load instruction
+// covers 16 tokens x 64 contiguous bytes of a dense K_lead.  Lanes n < 4 of
+// each row end with the scores of 4 consecutive tokens for head 4 grp + n
+// and store them with one 16-byte write.
+// ============================================================================
+template <int GT, int KS, bool KEYS>
+__global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restrict__ src,
+                                                         const uint16_t* __restrict__ qsplit,
+                                                         void* __restrict__ out, int out_stride,
+                                                         int Hq, int Hkv, int S, int d, int ld,
+                                                         int r, int SC) {
+  constexpr int NGRP = (GT + 3) / 4;
+  constexpr int UK = 8 / (KS * NGRP);
+  constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
+  const int t0 = blockIdx.x * SC, t1 = min(S, t0 + SC);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 15, q = lane >> 4;
+  const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
+
+  bf16x8_t bv[NGRP][KS];
+#pragma unroll
+  for (int grp = 0; grp < NGRP; ++grp)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      bv[grp][s] = q_operand(qsplit, head0, d, G, r, grp, m, 32 * s + 8 * q);
+
+  const bf16_t* base = src + (size_t)bk * S * ld;
+  for (int j0 = wave; t0 + 16 * j0 < t1; j0 += 4 * U) {
+    uint4 a[U][KS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + 16 * (j0 + 4 * u) + m;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dim0 = 32 * s + 8 * q;
+        a[u][s] = (t < t1 && dim0 < r) ? ldg16(base + (size_t)t * ld + dim0) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tb = t0 + 16 * (j0 + 4 * u) + 4 * q;  // this lane's 4 output tokens
+#pragma unroll
+      for (int grp = 0; grp < NGRP; ++grp) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][s]), bv[grp][s], acc, 0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) x[v] = add_split_columns(acc[v]);
+        const int g = 4 * grp + m;
+        if (m < 4 && g < G && tb < t1) {
+          const size_t o = (head0 + g) * (size_t)out_stride + tb;
+          if constexpr (KEYS) {
+            uint32_t* ko = static_cast<uint32_t*>(out);
+            if (tb + 3 < t1) {
+              *reinterpret_cast<uint4*>(ko + o) =
+                  make_uint4(score_key(x[0]), score_key(x[1]), score_key(x[2]), score_key(x[3]));
+            } else {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (tb + v < t1) ko[o + v] = score_key(x[v]);
+            }
+          } else {
+            float* fo = static_cast<float*>(out);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (tb + v < t1) fo[o + v] = x[v];
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// ============================================================================
+// Exact attention over the kept tokens, bf16 caches, G <= 8.
+// Wave = NT consecutive tokens of one (b, kv) group; four waves per block.
+// The G heads' bitmap words of the span go through LDS (one load per lane)
+// and give the union list (token, head mask).  Then two passes over it:
+//   pass 1: 16-row K tiles in MFMA A layout (a lane reads 8*KS contiguous
+//           dims of one row), up to KT tiles requested before any is used;
+//           exact scores of all G heads from MFMA, scaled to log2 units,
+//           -inf where a head did not keep the token, into LDS;
+//   per head: m = max, w = 2^(e - m), l = sum w;
+//   pass 2: V rows (16-byte granules, RL lanes per row), up to UV row
+//           passes in flight; acc += w V on the vector ALUs.
+// Each pass holds only its own buffers, which keeps the register file small
+// enough for several waves per SIMD.  The block then merges its four waves'
+// (m, l, acc) by log-sum-exp and writes one partial per (head, block).
+// ============================================================================
+template <int D, int GT>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restrict__ K_rot,
+                                                          const bf16_t* __restrict__ V,
+                                                          const uint16_t* __restrict__ qsplit,
+                                                          const uint32_t* __restrict__ bitmap,
+                                                          float* __restrict__ part, int Hq, int Hkv,
+                                                          int S, int W, int NC, float scale_log2) {
+  constexpr int NGRP = (GT + 3) / 4;
+  constexpr int KS = D / 32;         // 32-dim k-steps of the exact dot
+  constexpr int EPL = 8;             // bf16 per 16-byte granule
+  constexpr int RL = D / 8;          // lanes per V row
+  constexpr int RPW = 64 / RL;       // V rows per wave pass
+  constexpr int KT = 16 / KS;        // K tiles in flight (16 loads per lane)
+  constexpr int UV = 16;             // V row passes in flight
+  constexpr int NT = kAttendMfmaTokens;
+  constexpr int NSTEP = NT / 64;
+  constexpr int NW = NT / 32;        // bitmap words per head
+  static_assert(GT * NW <= 64, "one bitmap word per lane");
+  __shared__ uint32_t s_bits[4][GT * NW];
+  __shared__ int s_tok[4][NT];
+  __shared__ uint16_t s_hm[4][NT];
+  __shared__ __align__(16) float s_e[4][NT * GT];
+  __shared__ float s_m[4][GT], s_l[4][GT];
+  __shared__ __align__(16) float s_acc[4][GT][D];
+
+  const int G = Hq / Hkv;
+  const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = lane & 15, q = lane >> 4;
+  const int t0 = (blockIdx.x * 4 + wave) * NT;
+  const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
+  int* tok = s_tok[wave];
+  uint16_t* hmk = s_hm[wave];
+  float* e = s_e[wave];
+  uint32_t* bits = s_bits[wave];
+
+  // union list of the span
+  if (lane < G * NW) {
+    const int g = lane / NW, w = lane - g * NW;
+    const int t = t0 + 32 * w;
+    bits[lane] = (t < S) ? bitmap[(head0 + g) * W + (t >> 5)] : 0u;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int n = 0;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) {
+    const int t = t0 + 64 * st + lane;
+    const int wi = 2 * st + (lane >> 5);
+    int hm = 0;
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      if (g < G) hm |= (int)((bits[g * NW + wi] >> (t & 31)) & 1u) << g;
+    const uint64_t mk = __ballot(hm != 0);
+    if (hm) {
+      const int pos = n + bits_below(mk);
+      tok[pos] = t;
+      hmk[pos] = (uint16_t)hm;
+    }
+    n += __popcll(mk);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const size_t cb = (size_t)bk * S * D;
+
+  // pass 1: exact scores.  B operands: lane quarter q covers dims
+  // [8 KS q, 8 KS (q+1)), step s the 8 dims from 8 KS q + 8 s.
+  {
+    bf16x8_t bv[NGRP][KS];
+#pragma unroll
+    for (int grp = 0; grp < NGRP; ++grp)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        bv[grp][s] = q_operand(qsplit, head0, D, G, D, grp, m, 8 * KS * q + 8 * s);
+    for (int p0 = 0; p0 < n; p0 += 16 * KT) {
+      uint4 ka[KT][KS];
+#pragma unroll
+      for (int tl = 0; tl < KT; ++tl) {
+        const int p = p0 + 16 * tl + m;
+        const bf16_t* row = K_rot + cb + (size_t)(p < n ? tok[p] : 0) * D + 8 * KS * q;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ka[tl][s] = (p < n) ? ldg16(row + 8 * s) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int tl = 0; tl < KT; ++tl) {
+        if (p0 + 16 * tl >= n) break;  // uniform across the wave
+#pragma unroll
+        for (int grp = 0; grp < NGRP; ++grp) {
+          floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[tl][s]), bv[grp][s], sacc, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float x = add_split_columns(sacc[v]);
+            const int p = p0 + 16 * tl + 4 * q + v, g = 4 * grp + m;
+            if (m < 4 && g < GT && p < n)
+              e[p * GT + g] = (g < G && ((hmk[p] >> g) & 1)) ? x * scale_log2 : -INFINITY;
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // per-head softmax statistics of the span
+  float mreg[GT], lreg[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) {
+    float mx = -INFINITY, sum = 0.f;
+    if (g < G) {
+      for (int p = lane; p < n; p += 64) mx = fmaxf(mx, e[p * GT + g]);
+      mx = wave_max(mx);
+      for (int p = lane; p < n; p += 64) {
+        const float v = e[p * GT + g];
+        const float w = (v == -INFINITY) ? 0.f : exp2f(v - mx);
+        e[p * GT + g] = w;
+        sum += w;
+      }
+      sum = wave_sum(sum);
+    }
+    mreg[g] = mx;
+    lreg[g] = sum;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // pass 2: weighted value sum
+  const int lg = lane / RL, li = lane % RL;
+  float acc[GT][EPL];
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[g][i] = 0.f;
+  for (int p0 = 0; p0 < n; p0 += RPW * UV) {
+    uint4 vb[UV];
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int p = p0 + RPW * u + lg;
+      vb[u] = (p < n) ? ldg16(V + cb + (size_t)tok[p] * D + li * EPL) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      if (p0 + RPW * u >= n) break;  // uniform across the wave
+      const int p = p0 + RPW * u + lg;
+      float x[EPL];
+      Gran<bf16_t>::unpack(vb[u], x);
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float w = (p < n && g < G) ? e[p * GT + g] : 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[g][i] = fmaf(w, x[i], acc[g][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < GT; ++g)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      float v = acc[g][i];
+      for (int o = RL; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      acc[g][i] = v;
+    }
+
+  // merge the four waves' spans by log-sum-exp; one partial per (head, block)
+  if (lg == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) s_acc[wave][g][li * EPL + i] = acc[g][i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) { s_m[wave][g] = mreg[g]; s_l[wave][g] = lreg[g]; }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < G * D; o += 256) {
+    const int g = o / D, c = o - g * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = (s_m[w][g] == -INFINITY) ? 0.f : exp2f(s_m[w][g] - M);
+      L = fmaf(s_l[w][g], f, L);
+      A = fmaf(s_acc[w][g][c], f, A);
+    }
+    float* pr = part + ((head0 + g) * NC + blockIdx.x) * (size_t)(D + 2);
+    pr[2 + c] = A;
+    if (c == 0) { pr[0] = M; pr[1] = L; }
+  }
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+template <int GT, bool KEYS>
+static hipError_t score_mfma_g(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                               void* out, int out_stride, hipStream_t st) {
+  const dim3 grid(p.NSC, p.B * p.Hkv), block(256);
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  const int ks = (p.r + 31) / 32;
+#define LOKI_SM(K)                                                                                 \
+  case K:                                                                                          \
+    hipLaunchKernelGGL((score_mfma_kernel<GT, K, KEYS>), grid, block, 0, st, s, qsplit, out,       \
+                       out_stride, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                          \
+    break;
+  switch (ks) {
+    LOKI_SM(1)
+    LOKI_SM(2)
+    LOKI_SM(3)
+    LOKI_SM(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOKI_SM
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                              void* out, bool as_keys, int out_stride, hipStream_t st) {
+  if (p.dt != 1 || p.SC % 16 != 0) return hipErrorInvalidValue;
+  auto go = [&](auto gt) {
+    constexpr int GT = decltype(gt)::value;
+    return as_keys ? score_mfma_g<GT, true>(p, src, ld, qsplit, out, out_stride, st)
+                   : score_mfma_g<GT, false>(p, src, ld, qsplit, out, out_stride, st);
+  };
+  if (p.G <= 1) return go(std::integral_constant<int, 1>{});
+  if (p.G <= 2) return go(std::integral_constant<int, 2>{});
+  if (p.G <= 4) return go(std::integral_constant<int, 4>{});
+  if (p.G <= 8) return go(std::integral_constant<int, 8>{});
+  return go(std::integral_constant<int, 16>{});
+}
+
+hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
+                              const uint16_t* qsplit, const uint32_t* bitmap, float* part,
+                              hipStream_t st) {
+  if (p.dt != 1 || p.G > 8 || p.AC != 4 * kAttendMfmaTokens) return hipErrorInvalidValue;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d));
+  const dim3 grid(p.NAC, p.B * p.Hkv), block(256);
+  const bf16_t* k = static_cast<const bf16_t*>(K_rot);
+  const bf16_t* v = static_cast<const bf16_t*>(V);
+  auto go = [&](auto dd, auto gt) {
+    constexpr int D = decltype(dd)::value, GT = decltype(gt)::value;
+    hipLaunchKernelGGL((attend_mfma_kernel<D, GT>), grid, block, 0, st, k, v, qsplit, bitmap, part,
+                       p.Hq, p.Hkv, p.S, p.W, p.NAC, scale_log2);
+    return hipGetLastError();
+  };
+  auto by_g = [&](auto dd) {
+    if (p.G <= 1) return go(dd, std::integral_constant<int, 1>{});
+    if (p.G <= 2) return go(dd, std::integral_constant<int, 2>{});
+    if (p.G <= 4) return go(dd, std::integral_constant<int, 4>{});
+    return go(dd, std::integral_constant<int, 8>{});
+  };
+  return p.d == 64 ? by_g(std::integral_constant<int, 64>{}) : by_g(std::integral_constant<int, 128>{});
+}
+
+}  // namespace loki

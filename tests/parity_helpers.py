@@ -1,0 +1,48 @@
+"""Comparison rules between the HIP path and the float64 oracle.
+
+Selected index sets: bit-exact, except tokens whose oracle approximate score
+lies within 1e-4 (relative) of the oracle's k-th largest score; those may be
+exchanged for one another (several answers are then correct).
+Outputs: max-abs 1e-5 for fp32 storage, 2e-2 for bf16 storage.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+BAND_REL = 1e-4
+OUT_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+
+
+def check_index_sets(idx_gpu: np.ndarray, idx_oracle: np.ndarray, s_oracle: np.ndarray, k: int):
+    """Returns the list of (b, h) rows whose GPU set differs from the oracle's
+    (inside the band only); raises AssertionError on any real mismatch."""
+    B, Hq, kk = idx_gpu.shape
+    assert kk == k
+    differ = []
+    for b in range(B):
+        for h in range(Hq):
+            g = idx_gpu[b, h]
+            assert np.all(np.diff(g) > 0), f"row {(b, h)}: not strictly ascending"
+            assert g[0] >= 0 and g[-1] < s_oracle.shape[-1], f"row {(b, h)}: index out of range"
+            o = idx_oracle[b, h]
+            if np.array_equal(g, o):
+                continue
+            s = s_oracle[b, h]
+            sstar = np.sort(s)[::-1][k - 1]
+            if sstar == 0.0:
+                band = set(np.nonzero(s == 0.0)[0].tolist())
+            else:
+                band = set(np.nonzero(np.abs(s - sstar) <= BAND_REL * abs(sstar))[0].tolist())
+            gs, os_ = set(g.tolist()) - band, set(o.tolist()) - band
+            assert gs == os_, (f"row {(b, h)}: {len(gs ^ os_)} tokens differ outside the tie band "
+                               f"(band size {len(band)})")
+            differ.append((b, h))
+    return differ
+
+
+def max_abs(a, b) -> float:
+    a = a.double().cpu().numpy() if isinstance(a, torch.Tensor) else np.asarray(a, dtype=np.float64)
+    b = b.double().cpu().numpy() if isinstance(b, torch.Tensor) else np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0

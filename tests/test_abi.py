@@ -1,0 +1,128 @@
+"""The C ABI library on the CPU: it loads, exports every entry point that
+include/loki.h declares, and rejects every invalid argument with the
+documented status before touching HIP (so none of these calls needs a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_key_sparse_amd as rks
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+F32, BF16 = 0, 1
+OK, NULL, SHAPE, RANGE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, HIP = range(9)
+
+# fake, 16-byte aligned, non-null device addresses: only ever passed to calls
+# that must fail validation before any HIP call
+A = ctypes.c_void_p(0x10000)
+A2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+NULLP = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rks.load_library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "loki.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loki_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert "loki_decode" in names and "loki_project_keys" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(rks.EXPORTED) == names
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.loki_abi_version() == 1
+    for s in range(10):
+        assert lib.loki_status_str(s)
+    assert lib.loki_status_str(12345) == b"unknown status"
+
+
+def decode(lib, q=A, P=A, K=A, V=A, out=A, idx=A, B=1, Hq=4, Hkv=2, S=100, d=128, r=8, k=10,
+           dt=BF16, ws=A2, wsb=1 << 30):
+    return lib.loki_decode(q, P, K, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, ws, wsb, NULLP)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULLP), NULL), (dict(P=NULLP), NULL), (dict(K=NULLP), NULL), (dict(V=NULLP), NULL),
+    (dict(out=NULLP), NULL), (dict(idx=NULLP), NULL),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(Hq=5, Hkv=2), SHAPE), (dict(S=(1 << 24) + 1, k=1), SHAPE), (dict(B=70000, Hq=1, Hkv=1), SHAPE),
+    (dict(r=0), RANGE), (dict(r=129), RANGE), (dict(k=0), RANGE), (dict(k=101), RANGE),
+    (dict(dt=7), DTYPE),
+    (dict(d=96), UNSUPPORTED), (dict(Hq=34, Hkv=2), UNSUPPORTED),
+    (dict(q=MIS), ALIGN), (dict(V=MIS), ALIGN), (dict(idx=MIS), ALIGN), (dict(ws=MIS), ALIGN),
+    (dict(wsb=16), WORKSPACE), (dict(ws=NULLP), NULL),
+])
+def test_decode_rejects(lib, kw, want):
+    assert decode(lib, **kw) == want
+
+
+def test_project_rejects(lib):
+    f = lib.loki_project_keys
+    assert f(NULLP, A, A, 1, 1, 8, 128, BF16, NULLP) == NULL
+    assert f(A, A, A, 0, 1, 8, 128, BF16, NULLP) == SHAPE
+    assert f(A, A, A, 1, 1, 8, 100, BF16, NULLP) == UNSUPPORTED
+    assert f(A, A, MIS, 1, 1, 8, 128, BF16, NULLP) == ALIGN
+    assert f(A, A, A, 1, 1, 8, 128, 3, NULLP) == DTYPE
+
+
+def test_stage_entry_points_reject(lib):
+    assert lib.loki_scores(A, A, A, NULLP, 1, 1, 1, 8, 64, 4, F32, A2, 1 << 20, NULLP) == NULL
+    assert lib.loki_scores(A, A, A, A, 1, 1, 1, 8, 64, 65, F32, A2, 1 << 20, NULLP) == RANGE
+    assert lib.loki_select_topk(A, A, 4, 100, 0, A2, 1 << 20, NULLP) == RANGE
+    assert lib.loki_select_topk(A, A, 0, 100, 5, A2, 1 << 20, NULLP) == SHAPE
+    assert lib.loki_select_topk(A, MIS, 4, 100, 5, A2, 1 << 20, NULLP) == ALIGN
+    assert lib.loki_select_topk(A, A, 4, 100, 5, A2, 8, NULLP) == WORKSPACE
+    assert lib.loki_attend(A, A, A, A, NULLP, A, 1, 2, 1, 50, 64, 5, BF16, A2, 1 << 20, NULLP) == NULL
+    assert lib.loki_attend(A, A, A, A, A, A, 1, 2, 1, 50, 64, 51, BF16, A2, 1 << 20, NULLP) == RANGE
+
+
+def test_workspace_sizes(lib):
+    ws = lib.loki_decode_workspace_bytes
+    assert ws(1, 4, 2, 100, 128, 8, 10, BF16) > 0
+    assert ws(1, 4, 2, 100, 128, 0, 10, BF16) == 0
+    assert ws(1, 4, 2, 100, 96, 8, 10, BF16) == 0
+    assert ws(1, 5, 2, 100, 128, 8, 10, BF16) == 0
+    # must hold at least the fp32 keys and the rotated queries of every head
+    B, Hq, Hkv, S, d = 16, 32, 8, 16384, 128
+    n = ws(B, Hq, Hkv, S, d, 32, 1024, BF16)
+    assert n >= B * Hq * S * 4 + B * Hq * d * 4
+    assert n % 256 == 0
+    # independent of r and k (one workspace serves every stage entry point)
+    assert n == ws(B, Hq, Hkv, S, d, 1, 1, BF16) == ws(B, Hq, Hkv, S, d, d, S, BF16)
+    assert lib.loki_select_workspace_bytes(4, 100, 5) >= 4 * 100 * 4
+    assert lib.loki_select_workspace_bytes(4, 100, 101) == 0
+
+
+def test_python_binding_validates_before_the_library():
+    import torch
+    with pytest.raises(ValueError):
+        rks.loki_decode(torch.zeros(1, 1, 64), torch.zeros(1, 64, 64), torch.zeros(1, 1, 8, 64),
+                        torch.zeros(1, 1, 8, 64), r=4, k=2)  # CPU tensors are rejected
+
+
+def test_lead_entry_points_reject(lib):
+    f = lib.loki_decode_lead
+    def call(Kl=A, R=32, r=8, d=128, dt=BF16):
+        return f(A, A, A, Kl, R, A, A, A, 1, 4, 2, 100, d, r, 10, dt, A2, 1 << 30, NULLP)
+    assert call(Kl=NULLP) == NULL
+    assert call(R=0) == RANGE
+    assert call(R=129) == RANGE
+    assert call(R=8, r=9) == RANGE
+    assert call(R=12) == UNSUPPORTED       # 24 bytes per token: not a multiple of 16
+    assert call(Kl=MIS) == ALIGN
+    g = lib.loki_project_keys_lead
+    assert g(A, A, A, NULLP, 32, 1, 1, 8, 128, BF16, NULLP) == NULL
+    assert g(A, A, A, A, 200, 1, 1, 8, 128, BF16, NULLP) == RANGE
+    assert g(A, A, A, A, 6, 1, 1, 8, 128, F32, NULLP) == UNSUPPORTED

@@ -1,0 +1,346 @@
+"""GPU parity: every stage and the whole decode step against the float64 oracle.
+
+All calls go through the C ABI (rank_key_sparse_amd's ctypes binding).  Inputs
+come from the seeded generator; expected values come only from the oracle.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from loki_inputs import CONFIGS, make_inputs, make_integer_inputs
+from parity_helpers import OUT_TOL, check_index_sets, max_abs
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def dev(x):
+    return x.to("cuda") if isinstance(x, torch.Tensor) else x
+
+
+def as_np(t):
+    return t.detach().cpu().double().numpy()
+
+
+# ---------------------------------------------------------------- helpers
+
+
+def run_decode(rks, x, r, k, check_out=True, R=None):
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    K_lead = Kr[..., :R].contiguous() if R else None
+    out_g, idx_g = rks.loki_decode(q, P, Kr, V, r=r, k=k, K_lead=K_lead)
+    torch.cuda.synchronize()
+    idx_o, s_o = oracle.select(x["q"], x["P"], x["K_rot"], r, k, return_scores=True)
+    out_o = oracle.attend(x["q"], x["P"], x["K_rot"], x["V"], idx_o)
+    ig = idx_g.cpu().numpy().astype(np.int64)
+    differ = check_index_sets(ig, idx_o, s_o, k)
+    tol = OUT_TOL[x["q"].dtype]
+    og = as_np(out_g)
+    same = np.ones(og.shape[:2], dtype=bool)
+    for b, h in differ:
+        same[b, h] = False
+    if check_out:
+        err = float(np.max(np.abs(og - out_o)[same])) if same.any() else 0.0
+        assert err <= tol, f"output max-abs {err} > {tol}"
+    if differ:
+        # rows whose kept set legitimately differs (inside the tie band): the
+        # decode output must be the attention over ITS set, and the attention
+        # stage must match the oracle on the oracle's set
+        again = rks.loki_attend(q, P, Kr, V, idx_g)
+        on_o = rks.loki_attend(q, P, Kr, V, torch.from_numpy(idx_o.astype(np.int32)).to("cuda"))
+        for b, h in differ:
+            assert torch.equal(again[b, h], out_g[b, h])
+            assert max_abs(on_o[b, h], out_o[b, h]) <= tol
+    return out_g, idx_g, differ
+
+
+def cfg_case(name, **kw):
+    cfg = CONFIGS[name]
+    return cfg.scaled(**kw) if kw else cfg
+
+
+DECODE_CASES = {
+    "C1": cfg_case("C1"),
+    "C2@S1024": cfg_case("C2", S=1024),
+    "C3@B2S4096": cfg_case("C3", S=4096, B=2),
+    "C4@S16384": cfg_case("C4", S=16384),
+    "C5@B1S8192": cfg_case("C5", S=8192, B=1),
+    "C2": cfg_case("C2"),
+    "C3": cfg_case("C3"),
+    "C4": cfg_case("C4"),
+    "C5": cfg_case("C5"),
+}
+
+
+
+# ---------------------------------------------------------------- stages
+
+
+SCORE_CASES = [
+    ("C1", CONFIGS["C1"]),
+    ("C3@B2S2048", CONFIGS["C3"].scaled(S=2048, B=2)),
+    ("ragged_f32_r5", CONFIGS["C3"].replace(name="rf", cfg_no=51, B=1, Hq=6, Hkv=3, S=1001, dtype="f32", r=5)),
+    ("d64_bf16_G2_r40", CONFIGS["C3"].replace(name="d64", cfg_no=52, B=2, Hq=4, Hkv=2, S=700, d=64, r=40)),
+    ("f32_d128_r128", CONFIGS["C3"].replace(name="f128", cfg_no=53, B=1, Hq=2, Hkv=1, S=333, dtype="f32", r=128)),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=[c[0] for c in SCORE_CASES])
+def test_scores_within_fp32_bound(gpu_lib, case):
+    _, cfg = case
+    x = make_inputs(cfg)
+    s_g = gpu_lib.loki_scores(dev(x["q"]), dev(x["P"]), dev(x["K_rot"]), cfg.r).cpu().double().numpy()
+    s_o = oracle.approx_scores(x["q"], x["P"], x["K_rot"], cfg.r)
+    # bound from the arithmetic: fp32 q_rot (d FMAs) then an r-term fp32 dot
+    qabs = oracle.rotate_queries(x["q"].abs(), x["P"].abs())
+    G = cfg.G
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            ka = as_np(x["K_rot"][b, h // G, :, :cfg.r]).__abs__()
+            bound = 2.0 * (cfg.r + cfg.d + 2) * U * (ka @ qabs[b, h, :cfg.r]) + 1e-30
+            assert np.all(np.abs(s_g[b, h] - s_o[b, h]) <= bound), (b, h)
+
+
+def _score_rows():
+    g = np.random.default_rng(7)
+    rows = {}
+    rows["normal"] = g.standard_normal((8, 3000)).astype(np.float32)
+    rows["int_ties"] = g.integers(-5, 6, size=(6, 2500)).astype(np.float32)
+    rows["all_equal"] = np.full((3, 1000), 2.5, dtype=np.float32)
+    z = np.zeros((2, 500), dtype=np.float32)
+    z[:, ::2] = -0.0
+    z[:, 7] = 1.0
+    rows["signed_zero"] = z
+    h = g.standard_normal((4, 4000)).astype(np.float32)
+    h[:, 0] = 1e30
+    h[:, 1] = -1e30
+    rows["huge_range"] = h
+    t = g.standard_normal((4, 20000)).astype(np.float32)
+    t[:, 5000:9000] = 0.75  # thousands of exact ties around the threshold
+    rows["crowded_bin"] = t
+    rows["ascending"] = np.tile(np.arange(4097, dtype=np.float32), (2, 1))
+    rows["big_global"] = g.standard_normal((3, 70000)).astype(np.float32)
+    c = g.standard_normal((2, 70000)).astype(np.float32)
+    c[:, 1000:30000] = -0.25
+    rows["big_crowded"] = c
+    rows["S1"] = np.array([[3.0], [-1.0]], dtype=np.float32)
+    return rows
+
+
+SCORE_ROWS = _score_rows()
+
+
+@pytest.mark.parametrize("name", list(SCORE_ROWS))
+def test_select_topk_bit_exact(gpu_lib, name):
+    s = SCORE_ROWS[name]
+    S = s.shape[1]
+    ks = sorted({1, max(1, S // 16), max(1, S // 2), S, min(S, 7)})
+    sd = torch.from_numpy(s).to("cuda")
+    for k in ks:
+        idx_g = gpu_lib.loki_select_topk(sd, k).cpu().numpy()
+        for i in range(s.shape[0]):
+            want = oracle.topk_indices(s[i].astype(np.float64), k)
+            assert np.array_equal(idx_g[i], want), (name, k, i)
+
+
+@pytest.mark.parametrize("name", ["C1", "C3@B2S4096", "C4@S16384"])
+def test_attend_on_oracle_sets(gpu_lib, name):
+    cfg = DECODE_CASES[name]
+    x = make_inputs(cfg)
+    idx_o = oracle.select(x["q"], x["P"], x["K_rot"], cfg.r, cfg.k)
+    out_o = oracle.attend(x["q"], x["P"], x["K_rot"], x["V"], idx_o)
+    out_g = gpu_lib.loki_attend(dev(x["q"]), dev(x["P"]), dev(x["K_rot"]), dev(x["V"]),
+                                torch.from_numpy(idx_o.astype(np.int32)).to("cuda"))
+    assert max_abs(out_g, out_o) <= OUT_TOL[x["q"].dtype]
+
+
+def test_attend_ignores_out_of_range_and_duplicates(gpu_lib):
+    cfg = CONFIGS["C3"].replace(name="dup", cfg_no=54, B=1, Hq=4, Hkv=2, S=500, r=8, k=6)
+    x = make_inputs(cfg)
+    idx = np.array([[[3, 3, 10, -1, 499, 700]] * 4], dtype=np.int32)
+    out_g = gpu_lib.loki_attend(dev(x["q"]), dev(x["P"]), dev(x["K_rot"]), dev(x["V"]),
+                                torch.from_numpy(idx).to("cuda"))
+    clean = np.array([[[3, 10, 499]] * 4])
+    out_o = oracle.attend(x["q"], x["P"], x["K_rot"], x["V"], clean)
+    assert max_abs(out_g, out_o) <= OUT_TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------- projection
+
+
+def _proj_inputs(B, Hkv, S, d, dt, kind, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    K = torch.randn((B, Hkv, S, d), generator=g).to(tdt)
+    if kind == "random":
+        from loki_inputs import make_basis
+        P = torch.from_numpy(np.stack([make_basis(d, 60, kv) for kv in range(Hkv)])).to(tdt)
+    elif kind == "identity":
+        P = torch.eye(d).expand(Hkv, d, d).contiguous().to(tdt)
+    else:
+        P = torch.zeros((Hkv, d, d))
+        for kv in range(Hkv):
+            perm = torch.randperm(d, generator=g)
+            sg = torch.randint(0, 2, (d,), generator=g).float() * 2 - 1
+            P[kv, torch.arange(d), perm] = sg
+        P = P.to(tdt)
+    return K, P
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind", ["identity", "signed_perm", "random"])
+def test_project_keys(gpu_lib, dt, d, kind):
+    B, Hkv, S = 2, 3, 1000  # ragged: not a multiple of the 128-row tile
+    K, P = _proj_inputs(B, Hkv, S, d, dt, kind)
+    got = gpu_lib.loki_project_keys(dev(K), dev(P)).cpu()
+    exact = oracle.project(K, P)
+    if kind != "random":
+        # products with +-1 and sums with exact zeros: exactly representable
+        want = torch.from_numpy(exact).to(K.dtype)
+        assert torch.equal(got.view(torch.int16) if dt == "bf16" else got, want.view(torch.int16) if dt == "bf16" else want)
+        return
+    absprod = oracle.project(K.abs(), P.abs())
+    acc_err = 2.0 * (d + 2) * U * absprod
+    g = got.double().numpy()
+    if dt == "bf16":
+        tol = 2.0 ** -8 * (np.abs(exact) + acc_err) + acc_err
+    else:
+        tol = acc_err + 1e-30
+    assert np.all(np.abs(g - exact) <= tol)
+
+
+def test_project_then_decode_c5_shape(gpu_lib):
+    # the prefill-plus-decode workload: the GPU projection agrees with the
+    # oracle's projection element-wise, and decode over the oracle's
+    # (rounded) rotated keys matches the oracle
+    cfg = CONFIGS["C5"].scaled(S=4096, B=2)
+    x = make_inputs(cfg, need_K=True)
+    K, P = x["K"], x["P"]
+    got = gpu_lib.loki_project_keys(dev(K), dev(P)).cpu()
+    exact = oracle.project(K, P)
+    acc_err = 2.0 * (cfg.d + 2) * U * oracle.project(K.abs(), P.abs())
+    assert np.all(np.abs(got.double().numpy() - exact) <= 2.0 ** -8 * (np.abs(exact) + acc_err) + acc_err)
+    y = dict(x)
+    y["K_rot"] = torch.from_numpy(exact).to(torch.bfloat16)
+    run_decode(gpu_lib, y, cfg.r, cfg.k)
+
+
+# ---------------------------------------------------------------- decode parity
+FULL = {"C2", "C3", "C4", "C5"}
+
+
+@pytest.mark.parametrize("name", [pytest.param(n, marks=pytest.mark.slow) if n in FULL else n
+                                  for n in DECODE_CASES])
+def test_decode_workloads(gpu_lib, name):
+    cfg = DECODE_CASES[name]
+    x = make_inputs(cfg)
+    print(f"\n[{name}] B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} S={cfg.S} d={cfg.d} r={cfg.r} k={cfg.k}", flush=True)
+    _, _, differ = run_decode(gpu_lib, x, cfg.r, cfg.k)
+    print(f"[{name}] rows with band-equivalent sets: {len(differ)}", flush=True)
+
+
+EDGE = [
+    # (label, B, Hq, Hkv, S, d, dtype, r, k)
+    ("S1", 1, 2, 1, 1, 128, "bf16", 8, 1),
+    ("k_eq_S", 1, 4, 2, 300, 128, "bf16", 16, 300),
+    ("k1", 2, 4, 4, 500, 64, "f32", 8, 1),
+    ("r_eq_d", 1, 4, 1, 777, 128, "bf16", 128, 40),
+    ("r1", 1, 2, 2, 1000, 64, "bf16", 1, 100),
+    ("r5_ragged", 2, 6, 2, 1000, 128, "f32", 5, 33),
+    ("r13_G3", 1, 6, 2, 2049, 64, "bf16", 13, 200),
+    ("G16", 1, 16, 1, 1500, 128, "bf16", 32, 64),
+    ("G8_f32_d128", 1, 16, 2, 1111, 128, "f32", 24, 128),
+    ("d64_bf16_r64", 3, 8, 8, 640, 64, "bf16", 64, 64),
+    ("global_select", 1, 4, 2, 40000, 128, "bf16", 32, 1500),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_decode_edge_cases(gpu_lib, case):
+    label, B, Hq, Hkv, S, d, dt, r, k = case
+    print(f"\n[{label}] B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} {dt} r={r} k={k}", flush=True)
+    cfg = CONFIGS["C3"].replace(name=label, cfg_no=50, B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, dtype=dt,
+                                r=r, k=k)
+    x = make_inputs(cfg)
+    run_decode(gpu_lib, x, r, k)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("pk", ["identity", "signed_perm"])
+def test_decode_exact_ties(gpu_lib, dt, pk):
+    # integer-valued inputs: every score is an exact integer on both sides, so
+    # the kept sets must agree bit for bit, ties broken towards lower indices
+    x = make_integer_inputs(2, 8, 2, 128, 3000, dt, seed=3, P_kind=pk)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    for r, k in ((8, 100), (3, 777), (128, 5)):
+        _, idx_g = gpu_lib.loki_decode(q, P, Kr, V, r=r, k=k)
+        idx_o = oracle.select(x["q"], x["P"], x["K_rot"], r, k)
+        assert np.array_equal(idx_g.cpu().numpy(), idx_o), (r, k)
+
+
+def test_decode_all_equal_keys(gpu_lib):
+    B, Hq, Hkv, S, d = 1, 4, 2, 5000, 128
+    Kr = torch.ones((B, Hkv, S, d), dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(0)
+    V = torch.randn((B, Hkv, S, d), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g).to(torch.bfloat16)
+    P = torch.eye(d).expand(Hkv, d, d).contiguous().to(torch.bfloat16)
+    k = 1234
+    out_g, idx_g = gpu_lib.loki_decode(dev(q), dev(P), dev(Kr), dev(V), r=16, k=k)
+    assert np.array_equal(idx_g.cpu().numpy(), np.broadcast_to(np.arange(k), (B, Hq, k)))
+    out_o = oracle.attend(q, P, Kr, V, np.broadcast_to(np.arange(k), (B, Hq, k)))
+    assert max_abs(out_g, out_o) <= OUT_TOL[torch.bfloat16]
+
+
+def test_decode_deterministic(gpu_lib):
+    cfg = cfg_case("C3", S=8192, B=2)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    o1, i1 = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k)
+    o2, i2 = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k)
+    assert torch.equal(i1, i2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+
+
+# ---------------------------------------------------------------- lead-dims layout
+
+
+LEAD_CASES = [
+    # (label, cfg, R)
+    ("C1_R16", CONFIGS["C1"], 16),
+    ("C3_R32", CONFIGS["C3"].scaled(S=4096, B=2), 32),
+    ("C3_R64", CONFIGS["C3"].scaled(S=4096, B=1), 64),
+    ("C4_R16", CONFIGS["C4"].scaled(S=16384), 16),
+    ("C5_R64", CONFIGS["C5"].scaled(S=8192, B=1), 64),
+    ("f32_d128_R8_r5", CONFIGS["C3"].replace(name="l8", cfg_no=55, B=1, Hq=4, Hkv=2, S=999, dtype="f32", r=5, k=33), 8),
+]
+
+
+@pytest.mark.parametrize("case", LEAD_CASES, ids=[c[0] for c in LEAD_CASES])
+def test_decode_lead_layout(gpu_lib, case):
+    label, cfg, R = case
+    x = make_inputs(cfg)
+    out_l, idx_l, _ = run_decode(gpu_lib, x, cfg.r, cfg.k, R=R)
+    # the lead copy holds the same values, so the result is bit-identical to
+    # decoding from K_rot's own rows
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    out_r, idx_r = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k)
+    assert torch.equal(idx_l, idx_r)
+    assert torch.equal(out_l.view(torch.int16) if out_l.dtype == torch.bfloat16 else out_l,
+                       out_r.view(torch.int16) if out_r.dtype == torch.bfloat16 else out_r)
+
+
+@pytest.mark.parametrize("dt,d,R", [("bf16", 128, 32), ("bf16", 128, 16), ("bf16", 64, 64), ("f32", 64, 16), ("f32", 128, 4)])
+def test_project_lead_copy(gpu_lib, dt, d, R):
+    K, P = _proj_inputs(2, 3, 777, d, dt, "random", seed=4)
+    Kr, Kl = gpu_lib.loki_project_keys(dev(K), dev(P), R=R)
+    Kr2 = gpu_lib.loki_project_keys(dev(K), dev(P))
+    assert torch.equal(Kr.view(torch.int16) if dt == "bf16" else Kr, Kr2.view(torch.int16) if dt == "bf16" else Kr2)
+    assert torch.equal(Kl, Kr[..., :R].contiguous())
