@@ -1,0 +1,332 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of low-rank-key (Loki-style) sparse decode attention.
+
+Default run: the Llama-3-8B-shaped GQA decode workload (batch 16, 32 query
+heads sharing 8 key/value heads, head dim 128, 16384 cached tokens per
+sequence, leading r = 32 rotated dims for the approximate scores, k = 1024
+kept tokens per query head, bf16 cache).  One step = one ``loki_decode``
+over every (batch, query head): query rotation, approximate scores, top-k,
+exact attention over the kept rows, merge.
+
+Measurement:
+* inputs are resident in HBM before timing; NBUF copies of the caches are
+  rotated so every step reads a cache last touched NBUF-1 steps earlier,
+  with more data touched in between than the 256 MB Infinity Cache holds;
+* region A times exactly ``--steps`` plain steps (wall clock between two
+  device synchronisations): value, ms_per_step;
+* region B re-times the same steps through the instrumented entry point,
+  whose HIP events on the library's stream give each kernel's average
+  duration -> the roofline of the dominant kernel;
+* the CPU baseline runs the float64 oracle, single-threaded, on a bounded
+  sample of the same workload (whole batch elements) on the host, and also
+  confirms the GPU output on that sample.
+
+Also: ``--calibrate-copy`` runs a 1 GiB elementwise copy (torch.neg; for
+rocprofv3 counter scaling), ``--summarize-trace DB`` and ``--summarize-pmc FETCH_DB WRITE_DB``
+turn rocprofv3 result databases into the summaries kept under profiles/.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+STAGES = ["qrot", "scores", "select", "attend", "merge"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rank_key_sparse_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- profiles tooling
+
+
+def summarize_trace(db: str) -> str:
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, start, end from kernels").fetchall()
+    agg: dict = {}
+    for name, st, en in rows:
+        agg.setdefault(name.split("(")[0], []).append((en - st) / 1000.0)
+    tot = sum(sum(v) for v in agg.values())
+    out = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| `{name}` | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                   f"{100 * sum(v) / tot:.1f}% |")
+    return "\n".join(out)
+
+
+def _pmc(db: str, counter: str) -> dict:
+    con = sqlite3.connect(db)
+    rows = con.execute("select kernel_name, grid_size, value from counters_collection where counter_name=?",
+                       (counter,)).fetchall()
+    agg: dict = {}
+    for kn, gs, v in rows:
+        agg.setdefault((kn.split("(")[0], gs), []).append(v)
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 30) -> dict:
+    """Per-kernel HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB),
+    each scaled by what the counter reads for the calibration copy."""
+    fetch, write = _pmc(fetch_db, "FETCH_SIZE"), _pmc(write_db, "WRITE_SIZE")
+    kib = copy_bytes / 1024.0
+
+    def copy_entry(d):
+        # the calibration copy: torch.neg over 1 GiB (one read, one write)
+        cands = [(v, k) for k, v in d.items() if "neg" in k[0]]
+        return max(cands)[1] if cands else None
+
+    cf, cw = copy_entry(fetch), copy_entry(write)
+    f_scale = kib / fetch[cf] if cf else None
+    w_scale = kib / write[cw] if cw else None
+    kernels = {}
+    for (name, gs), v in fetch.items():
+        if "loki" not in name:
+            continue
+        w = write.get((name, gs))
+        kernels[f"{name}|grid={gs}"] = {
+            "fetch_kib": v, "write_kib": w,
+            "fetch_bytes": v * 1024.0 * f_scale if f_scale else None,
+            "write_bytes": (w * 1024.0 * w_scale) if (w is not None and w_scale) else None,
+        }
+    return {"source_hash": kernel_source_hash(), "copy_kernel_fetch": cf and cf[0],
+            "copy_kernel_write": cw and cw[0], "copy_bytes": copy_bytes,
+            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
+
+
+def load_traffic(workload: str, kernel_name: str):
+    """Scaled HBM bytes per dispatch of `kernel_name` from the committed PMC
+    summary, or None when absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    for key, v in t.get("kernels", {}).items():
+        if key.split("|")[0].endswith(kernel_name) and v.get("fetch_bytes") is not None:
+            return v["fetch_bytes"] + (v.get("write_bytes") or 0.0)
+    return None
+
+
+# ----------------------------------------------------------------------------- benchmark
+
+
+def union_rows(idx, G: int) -> int:
+    """Number of distinct kept tokens per (b, kv) group, summed."""
+    import torch
+    B, Hq, k = idx.shape
+    Hkv = Hq // G
+    grp = idx.view(B, Hkv, G * k).to(torch.int64)
+    srt, _ = torch.sort(grp, dim=-1)
+    distinct = 1 + (srt[..., 1:] != srt[..., :-1]).sum(dim=-1)
+    return int(distinct.sum().item())
+
+
+def cpu_baseline(x, cfg, out_gpu, idx_gpu, seconds: float):
+    """The float64 oracle, one thread, on whole batch elements until `seconds`
+    of CPU work; also checks the GPU result on that sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_helpers import OUT_TOL, check_index_sets
+
+    done, t_used, ok = 0, 0.0, True
+    with threadpool_limits(limits=1):
+        while t_used < seconds or done == 0:
+            b = done % cfg.B
+            sl = {n: x[n][b:b + 1] for n in ("q", "K_rot", "V")}
+            t = time.perf_counter()
+            idx_o, s_o = oracle.select(sl["q"], x["P"], sl["K_rot"], cfg.r, cfg.k, return_scores=True)
+            out_o = oracle.attend(sl["q"], x["P"], sl["K_rot"], sl["V"], idx_o)
+            t_used += time.perf_counter() - t
+            if done < cfg.B:  # first pass over the batch: confirm the GPU result
+                try:
+                    differ = check_index_sets(idx_gpu[b:b + 1].astype(np.int64), idx_o, s_o, cfg.k)
+                    err = np.abs(out_gpu[b:b + 1] - out_o)
+                    for bb, h in differ:
+                        err[bb, h] = 0.0
+                    ok = ok and float(err.max()) <= OUT_TOL[x["q"].dtype]
+                except AssertionError:
+                    ok = False
+            done += 1
+    per_step = t_used / done * cfg.B
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} batch-element decodes of the same workload ({done / cfg.B:.2f} full steps, "
+                      f"{done * cfg.Hq} query heads), {t_used:.1f} s single-threaded",
+            "gpu_matches_oracle_on_sample": ok}
+
+
+def run(args) -> dict:
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = time.perf_counter()
+    x = make_inputs(cfg)
+    gen_s = time.perf_counter() - t
+    print(f"[bench] inputs for {cfg.name} generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    q = x["q"].to(dev)
+    P = x["P"].to(dev)
+    R = cfg.r if args.layout == "lead" else 0
+    bufs = []
+    for i in range(args.buffers):
+        Kr = x["K_rot"].to(dev)
+        V = x["V"].to(dev)
+        Kl = Kr[..., :R].contiguous() if R else None
+        bufs.append((Kr, V, Kl))
+    nbytes = rks.loki_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.d, cfg.r, cfg.k, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    idx = torch.empty((cfg.B, cfg.Hq, cfg.k), dtype=torch.int32, device=dev)
+
+    def step(i, events=None):
+        Kr, V, Kl = bufs[i % len(bufs)]
+        rks.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, K_lead=Kl, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # region A: the headline
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    print(f"[bench] region A: {args.steps} steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    # region B: per-kernel durations from stage events on the library's stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in evs:  # create the underlying events
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    stage_us = {s: 0.0 for s in STAGES}
+    for row in evs:
+        for j, s in enumerate(STAGES):
+            stage_us[s] += 1e3 * row[j].elapsed_time(row[j + 1])
+    stage_us = {s: v / args.steps for s, v in stage_us.items()}
+
+    # algorithmic bytes (what the method must move; intermediates excluded)
+    e = cfg.elem_bytes
+    U = union_rows(idx, cfg.G)
+    by_prefix = cfg.B * cfg.Hkv * cfg.S * cfg.r * e
+    by_gather = U * cfg.d * 2 * e
+    by_step = by_prefix + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
+        + cfg.B * cfg.Hq * cfg.k * 4
+    per_kernel_bytes = {"scores": by_prefix, "attend": by_gather}
+    dom = max(("scores", "attend"), key=lambda s: stage_us[s])
+    dom_kernel = {"scores": "score_mfma_kernel", "attend": "attend_mfma_kernel"}[dom]
+    achieved = per_kernel_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    traffic = load_traffic(args.workload, dom_kernel)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic, 0),
+                "kernel": dom_kernel, "alg_bytes_per_launch": per_kernel_bytes[dom],
+                "avg_launch_us": round(stage_us[dom], 2)}
+    step_gbs = by_step / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "decode attention steps/s (all heads) and achieved HBM GB/s vs ~8 TB/s peak",
+        "value": round(1e3 / ms_per_step, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Llama-3-8B-shaped GQA decode" if cfg.name == "C3" else cfg.name,
+                   "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.d,
+                   "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k, "score_source":
+                   f"K_lead (R={R})" if R else "K_rot rows", "cache_copies_rotated": args.buffers},
+        "hbm_gbs_step": round(step_gbs, 1),
+        "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "alg_bytes_per_step": by_step,
+        "union_rows": U,
+        "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline(x, cfg, out.float().cpu().numpy().astype(np.float64),
+                                           idx.cpu().numpy(), args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C3", choices=["C2", "C3", "C4", "C5"])
+    ap.add_argument("--layout", default="lead", choices=["lead", "rowmajor"])
+    ap.add_argument("--buffers", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
+    args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the decode shards over (batch, kv head) groups with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+    res = run(args)
+    print(json.dumps(res))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

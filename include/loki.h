@@ -151,6 +151,23 @@ loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, co
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Instrumented decode for measurement: exactly the work of loki_decode
+ * (K_lead == NULL) or loki_decode_lead, plus hipEventRecord(events[i],
+ * stream) at the stage boundaries:
+ *   [0] before the query rotation    [1] after it
+ *   [2] after the approximate scores [3] after the top-k selection
+ *   [4] after exact attention        [5] after the partial merge (the end)
+ * events: host array of 6 events created by the caller (LOKI_ERR_NULL if
+ * any is NULL).  Other arguments and errors as for loki_decode_lead.
+ */
+loki_status loki_decode_profiled(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                                 int32_t R, const void* V, void* out, int32_t* idx,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                                 int32_t r, int32_t k, loki_dtype dt,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipEvent_t* events, hipStream_t stream);
+
+/*
  * The approximate-score stage alone: scores[b,h,j] = s_j as defined for
  * loki_decode (fp32, unscaled), by the same kernels that loki_decode uses.
  * Workspace as for loki_decode with the same sizes (k = 1 may be passed).

@@ -133,7 +133,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
                                int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
                                int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
                                loki_dtype dt, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
+                               hipStream_t stream, hipEvent_t* ev = nullptr) {
   LOKI_TRY(check_dtype(dt));
   if (!q || !P || !K_rot || !V || !out || !idx) return LOKI_ERR_NULL;
   LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
@@ -150,11 +150,16 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
   uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
   float* part = at<float>(workspace, p.off_part);
+  if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
   LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+  if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
   if (K_lead) LOKI_HIP(launch_scores(p, K_lead, R, qrot, qsplit, keys, true, p.Sp, stream));
   else LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, keys, true, p.Sp, stream));
+  if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
   LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
-  LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream));
+  if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
+  LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
+  if (ev) LOKI_HIP(hipEventRecord(ev[5], stream));
   return LOKI_OK;
 }
 
@@ -179,6 +184,22 @@ loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, co
     if (!K_lead) return LOKI_ERR_NULL;
     return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
                        workspace_bytes, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_profiled(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                                 int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
+                                 int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                                 loki_dtype dt, void* workspace, size_t workspace_bytes,
+                                 hipEvent_t* events, hipStream_t stream) {
+  try {
+    if (!events) return LOKI_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return LOKI_ERR_NULL;
+    return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream, events);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

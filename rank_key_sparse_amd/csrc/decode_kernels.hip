@@ -916,7 +916,8 @@ hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_
 
 template <typename T, int D>
 static hipError_t attend_td(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
-                            const uint32_t* bitmap, float* part, void* out, hipStream_t st) {
+                            const uint32_t* bitmap, float* part, void* out, hipStream_t st,
+                            hipEvent_t mid) {
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
   hipError_t e = dispatch_group(p.G, [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
@@ -927,6 +928,7 @@ static hipError_t attend_td(const DecodePlan& p, const void* K_rot, const void* 
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
+  if (mid && (e = hipEventRecord(mid, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((combine_kernel<T>), dim3(p.B * p.Hq), dim3(D), 0, st, part, static_cast<T*>(out),
                      p.NAC, D);
   return hipGetLastError();
@@ -934,10 +936,11 @@ static hipError_t attend_td(const DecodePlan& p, const void* K_rot, const void* 
 
 hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
                          const uint16_t* qsplit, const uint32_t* bitmap, float* part, void* out,
-                         hipStream_t st) {
+                         hipStream_t st, hipEvent_t mid) {
   if (p.dt == 1 && p.G <= 8) {
-    const hipError_t e = launch_attend_mfma(p, K_rot, V, qsplit, bitmap, part, st);
+    hipError_t e = launch_attend_mfma(p, K_rot, V, qsplit, bitmap, part, st);
     if (e != hipSuccess) return e;
+    if (mid && (e = hipEventRecord(mid, st)) != hipSuccess) return e;
     if (p.d == 64)
       hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(p.B * p.Hq), dim3(64), 0, st, part,
                          static_cast<bf16_t*>(out), p.NAC, 64);
@@ -947,10 +950,10 @@ hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, 
     return hipGetLastError();
   }
   if (p.dt == 0)
-    return p.d == 64 ? attend_td<float, 64>(p, K_rot, V, qrot, bitmap, part, out, st)
-                     : attend_td<float, 128>(p, K_rot, V, qrot, bitmap, part, out, st);
-  return p.d == 64 ? attend_td<bf16_t, 64>(p, K_rot, V, qrot, bitmap, part, out, st)
-                   : attend_td<bf16_t, 128>(p, K_rot, V, qrot, bitmap, part, out, st);
+    return p.d == 64 ? attend_td<float, 64>(p, K_rot, V, qrot, bitmap, part, out, st, mid)
+                     : attend_td<float, 128>(p, K_rot, V, qrot, bitmap, part, out, st, mid);
+  return p.d == 64 ? attend_td<bf16_t, 64>(p, K_rot, V, qrot, bitmap, part, out, st, mid)
+                   : attend_td<bf16_t, 128>(p, K_rot, V, qrot, bitmap, part, out, st, mid);
 }
 
 }  // namespace loki

@@ -49,9 +49,10 @@ hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, int rows, 
                                  hipStream_t st);
 hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,
                                 hipStream_t st);
+// Attention then the partial merge; `mid` (may be null) is recorded between them.
 hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
                          const uint16_t* qsplit, const uint32_t* bitmap, float* part, void* out,
-                         hipStream_t st);
+                         hipStream_t st, hipEvent_t mid = nullptr);
 // K_rot = K P; when K_lead is non-null its rows also receive the leading R dims.
 // MFMA paths (bf16 storage).
 hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
