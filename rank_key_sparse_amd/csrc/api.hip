@@ -151,12 +151,23 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
   float* part = at<float>(workspace, p.off_part);
   if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
-  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
   if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
-  if (K_lead) LOKI_HIP(launch_scores(p, K_lead, R, qrot, qsplit, keys, true, p.Sp, stream));
-  else LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, keys, true, p.Sp, stream));
-  if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
-  LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+  const void* src = K_lead ? K_lead : K_rot;
+  const int ld = K_lead ? R : d;
+  // bf16, one query head per key head (so no two blocks read the same
+  // source), a head's keys small enough for LDS and enough heads to fill
+  // the chip: scores and selection in one kernel; otherwise two kernels with
+  // the keys in the workspace
+  const bool fused = dt == LOKI_BF16 && Hq == Hkv && S <= kFusedMaxS && (int64_t)B * Hq >= 256;
+  if (fused) {
+    LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
+    if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+  } else {
+    LOKI_HIP(launch_scores(p, src, ld, qrot, qsplit, keys, true, p.Sp, stream));
+    if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+    LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+  }
   if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
   LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
   if (ev) LOKI_HIP(hipEventRecord(ev[5], stream));
@@ -220,7 +231,7 @@ loki_status loki_scores(const void* q, const void* P, const void* K_rot, float* 
     LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
     float* qrot = at<float>(workspace, p.off_qrot);
     uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
-    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
     LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, scores, false, S, stream));
     return LOKI_OK;
   } catch (...) {
@@ -274,7 +285,7 @@ loki_status loki_attend(const void* q, const void* P, const void* K_rot, const v
     uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
     uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
     float* part = at<float>(workspace, p.off_part);
-    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, nullptr, stream));
+    LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
     LOKI_HIP(launch_idx_to_bitmap(p, idx, bitmap, stream));
     LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream));
     return LOKI_OK;

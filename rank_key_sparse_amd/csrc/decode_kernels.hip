@@ -15,6 +15,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "select_core.h"
 
 namespace loki {
 
@@ -40,31 +41,31 @@ __device__ __forceinline__ void copy16_to_lds(uint4* __restrict__ dst, const uin
 
 // ============================================================================
 // q rotation: q_rot[b, kv*G+g, c] = sum_j q[b, kv*G+g, j] * P[kv, j, c]
-// One block of 256 threads per (b, kv): P[kv] and the G queries are staged
-// in LDS with 16-byte loads; thread (c, js) sums a contiguous slice of j for
-// every head, and the slices are added in slice order.  The block also
-// clears the attention-merge counter of its (b, kv) group for this call.
+// One block of 8 d threads per (b, kv): P[kv] and the G queries are staged
+// in LDS with 16-byte loads; thread (c, js) sums the js-th of 8 contiguous
+// slices of j for every head, and the slices are added in slice order.  The
+// block also writes the three-way bf16 split of q_rot used as MFMA operands.
 // ============================================================================
+constexpr int kQrotSlices = 8;
+
 template <typename T, int GT>
-__global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
-                                                   float* __restrict__ qrot,
-                                                   bf16_t* __restrict__ qsplit,
-                                                   uint32_t* __restrict__ counters, int Hq, int Hkv,
-                                                   int d) {
+__global__ __launch_bounds__(1024) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
+                                                    float* __restrict__ qrot,
+                                                    bf16_t* __restrict__ qsplit, int Hq, int Hkv,
+                                                    int d) {
   extern __shared__ __align__(16) unsigned char qrot_lds[];
   T* sP = reinterpret_cast<T*>(qrot_lds);                                     // [d][d]
   float* qs = reinterpret_cast<float*>(qrot_lds + (size_t)d * d * sizeof(T));  // [GT][d]
-  float* red = reinterpret_cast<float*>(qrot_lds);                            // reuses sP
+  float* red = qs + GT * d;                                                   // [slices][GT][d]
   const int G = Hq / Hkv;
   const int bk = blockIdx.x, b = bk / Hkv, kv = bk % Hkv;
   const size_t qbase = ((size_t)b * Hq + (size_t)kv * G) * d;
-  const int tid = threadIdx.x;
-  if (tid == 0 && counters) counters[bk] = 0u;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   copy16_to_lds(reinterpret_cast<uint4*>(sP), reinterpret_cast<const uint4*>(P + (size_t)kv * d * d),
-                d * d * (int)sizeof(T) / 16, tid, 256);
-  for (int i = tid; i < GT * d; i += 256) qs[i] = (i < G * d) ? to_f32(q[qbase + i]) : 0.f;
+                d * d * (int)sizeof(T) / 16, tid, nthr);
+  for (int i = tid; i < GT * d; i += nthr) qs[i] = (i < G * d) ? to_f32(q[qbase + i]) : 0.f;
   __syncthreads();
-  const int JS = 256 / d, J = d / JS;
+  const int J = d / kQrotSlices;
   const int c = tid % d, js = tid / d, j0 = js * J;
   float acc[GT];
 #pragma unroll
@@ -76,7 +77,6 @@ __global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, cons
 #pragma unroll
     for (int g = 0; g < GT; ++g) acc[g] = fmaf(qs[g * d + j], pj, acc[g]);
   }
-  __syncthreads();  // sP is no longer read; reuse it for the slice sums
 #pragma unroll
   for (int g = 0; g < GT; ++g) red[(js * GT + g) * d + c] = acc[g];
   __syncthreads();
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, cons
     for (int g = 0; g < GT; ++g) {
       if (g >= G) break;
       float v = red[g * d + c];
-      for (int t = 1; t < JS; ++t) v += red[(t * GT + g) * d + c];
+      for (int t = 1; t < kQrotSlices; ++t) v += red[(t * GT + g) * d + c];
       qrot[qbase + (size_t)g * d + c] = v;
       if (qsplit) {
         // three-way bf16 split v = h + m + l (each residual exact in fp32),
@@ -184,123 +184,33 @@ __global__ __launch_bounds__(256) void scores_to_keys_kernel(const float* __rest
 }
 
 // ============================================================================
-// Top-k selection, one block of 1024 threads per query head.
-//
-// 1. min/max key of the row;
-// 2. histogram of the scores in NB equal-width value bins over [min, max]
-//    (a monotone map, so bins order like keys);
-// 3. scan bins from the top to find the bin t holding the k-th largest;
-// 4. resolve the exact k-th key K* inside bin t: rank the (few) candidates
-//    of bin t by (key desc, index asc) in LDS; if bin t is too full (heavily
-//    tied or degenerate scores) run an exact 11/11/10-bit MSB radix select
-//    restricted to bin t instead;
-// 5. emit, in index order: key > K*, or key == K* among the first `quota`
-//    such tokens (lower index wins).  Each wave owns a 64-aligned token
-//    segment, so the kept-token bitmap words are written without atomics.
-// Keys live in LDS when the row fits (IN_LDS), else every pass re-reads them
-// from global memory (L2 / Infinity Cache).
+// Top-k selection from workspace keys, one block of 1024 threads per query
+// head (see select_core.h): the row's keys are copied to LDS when they fit
+// (IN_LDS), else every pass re-reads them from global memory (L2 / Infinity
+// Cache).  Min / max are found during the first read.
 // ============================================================================
 constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kNB = 2048;   // value bins (2 per thread in the threshold scan)
-constexpr int kCap = 1024;  // candidates ranked in LDS (2 * kCap words alias the bins)
-constexpr int kRankLds = 256;  // rank limit when the row itself is in LDS
-
-struct SelScratch {
-  uint32_t red[2][kSelWaves];
-  int scan[kSelWaves];
-  int wgt[kSelWaves], weq[kSelWaves], selb[kSelWaves], eqb[kSelWaves];
-  uint32_t kmin, kmax, kstar;
-  int t, above, quota, ccount;
-};
-
-// Inclusive prefix sum over the block in thread order.
-__device__ __forceinline__ int block_incl_scan(int v, SelScratch& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  if (lane == 63) sh.scan[wave] = v;
-  __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += sh.scan[w];
-  __syncthreads();
-  return v + add;
-}
-
-// Find, scanning bins from the top, the bin holding the `want`-th largest key
-// (1-based).  Sets sh.t to that bin and sh.above to the count in higher bins.
-__device__ __forceinline__ void find_threshold(const uint32_t* hist, int want, SelScratch& sh) {
-  const int hb = kNB - 1 - 2 * (int)threadIdx.x;
-  const int hhi = (int)hist[hb], hlo = (int)hist[hb - 1];
-  const int incl = block_incl_scan(hhi + hlo, sh);
-  const int above = incl - hhi - hlo;
-  if (above < want && above + hhi >= want) { sh.t = hb; sh.above = above; }
-  else if (above + hhi < want && above + hhi + hlo >= want) { sh.t = hb - 1; sh.above = above + hhi; }
-  __syncthreads();
-}
-
-struct Binner {
-  float fmin, scale;
-  bool degenerate;
-  __device__ __forceinline__ int operator()(uint32_t key) const {
-    if (degenerate) return 0;
-    const int b = (int)((key_score(key) - fmin) * scale);
-    return b < kNB - 1 ? b : kNB - 1;
-  }
-};
-
-// Calls f(j, key) for every token j < S (in no particular order): each thread
-// reads 4 consecutive keys per 16-byte load with UB loads in flight.
-template <bool IN_LDS, typename F>
-__device__ __forceinline__ void for_each_key(const uint32_t* rk, const uint32_t* lk, int S, int Sp,
-                                             F&& f) {
-  constexpr int UB = IN_LDS ? 4 : 8;
-  const uint4* src = reinterpret_cast<const uint4*>(IN_LDS ? lk : rk);
-  const int n4 = Sp >> 2, tid = threadIdx.x;
-  for (int base = 0; base < n4; base += kSelThreads * UB) {
-    uint4 v[UB];
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int i = base + u * kSelThreads + tid;
-      v[u] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int j = (base + u * kSelThreads + tid) << 2;
-      if (j < S) f(j, v[u].x);
-      if (j + 1 < S) f(j + 1, v[u].y);
-      if (j + 2 < S) f(j + 2, v[u].z);
-      if (j + 3 < S) f(j + 3, v[u].w);
-    }
-  }
-}
 
 template <bool IN_LDS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __restrict__ keys, int S,
                                                              int Sp, int k, int W,
                                                              int32_t* __restrict__ idx,
                                                              uint32_t* __restrict__ bitmap) {
+  constexpr int NW = kSelThreads / 64;
   extern __shared__ __align__(16) uint32_t dyn[];
-  __shared__ SelScratch sh;
+  __shared__ SelScratch<kSelThreads> sh;
   uint32_t* lk = dyn;                          // [Sp] keys (IN_LDS only)
-  uint32_t* hist = dyn + (IN_LDS ? Sp : 0);    // [kNB]; later cand keys / indices
+  uint32_t* hist = dyn + (IN_LDS ? Sp : 0);    // [kNB]
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t* rk = keys + (size_t)row * Sp;
   int32_t* orow = idx + (size_t)row * k;
   uint32_t* brow = bitmap + (size_t)row * W;
 
-  if (k >= S) {  // every token kept
-    for (int j = tid; j < S; j += kSelThreads) orow[j] = j;
-    for (int w = tid; w < W; w += kSelThreads) {
-      const int lo = 32 * w;
-      brow[w] = (lo + 32 <= S) ? 0xffffffffu : (lo >= S ? 0u : ((1u << (S - lo)) - 1u));
-    }
+  if (k >= S) {
+    keep_all<kSelThreads>(S, W, orow, brow);
     return;
   }
-
-  // 1. min / max, and the copy of the row to LDS
+  // min / max, and the copy of the row to LDS (8 loads per thread in flight)
   uint32_t mn = 0xffffffffu, mx = 0u;
   {
     const uint4* src = reinterpret_cast<const uint4*>(rk);
@@ -329,151 +239,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __r
   mn = wave_min_u(mn);
   mx = wave_max_u(mx);
   if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
-  for (int i = tid; i < kNB; i += kSelThreads) hist[i] = 0u;
   __syncthreads();
   if (tid == 0) {
     uint32_t a = sh.red[0][0], c = sh.red[1][0];
-    for (int w = 1; w < kSelWaves; ++w) { a = min(a, sh.red[0][w]); c = max(c, sh.red[1][w]); }
+    for (int w = 1; w < NW; ++w) { a = min(a, sh.red[0][w]); c = max(c, sh.red[1][w]); }
     sh.kmin = a; sh.kmax = c;
   }
   __syncthreads();
-
-  // 2. value histogram
-  Binner bin;
-  {
-    const float fmin = key_score(sh.kmin), fmax = key_score(sh.kmax);
-    const float range = fmax - fmin;
-    const float scale = (float)kNB / range;
-    bin.fmin = fmin;
-    bin.scale = scale;
-    bin.degenerate = !(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f);
-  }
-  for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) { atomicAdd(&hist[bin(v)], 1u); });
-  __syncthreads();
-
-  // 3. threshold bin
-  find_threshold(hist, k, sh);
-  const int tb = sh.t;
-  const int need = k - sh.above;  // 1 <= need <= hist[tb]
-  const int nc = (int)hist[tb];
-  __syncthreads();  // hist is reused below
-
-  // 4. exact k-th key inside bin tb.  Ranking costs nc^2 compares spread over
-  // the block; the radix passes cost three sweeps of the row.
-  if (nc <= (IN_LDS ? kRankLds : kCap)) {
-    uint32_t* ck = hist;
-    uint32_t* ci = hist + kCap;
-    if (tid == 0) sh.ccount = 0;
-    __syncthreads();
-    for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int j, uint32_t v) {
-      if (bin(v) == tb) {
-        const int p = atomicAdd(&sh.ccount, 1);
-        ck[p] = v;
-        ci[p] = (uint32_t)j;
-      }
-    });
-    __syncthreads();
-    for (int i = tid; i < nc; i += kSelThreads) {
-      const uint32_t vi = ck[i], ii = ci[i];
-      int gtc = 0, rank = 0;
-      for (int c = 0; c < nc; ++c) {
-        const uint32_t vc = ck[c], ic = ci[c];
-        gtc += (vc > vi);
-        rank += (vc > vi) || (vc == vi && ic < ii);
-      }
-      if (rank == need - 1) { sh.kstar = vi; sh.quota = need - gtc; }
-    }
-    __syncthreads();
-  } else {
-    uint32_t prefix = 0u, pmask = 0u;
-    int rem = need;
-    const int shifts[3] = {21, 10, 0};
-    const int widths[3] = {11, 11, 10};
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sft = shifts[pass];
-      const uint32_t dm = (1u << widths[pass]) - 1u;
-      for (int i = tid; i < kNB; i += kSelThreads) hist[i] = 0u;
-      __syncthreads();
-      for_each_key<IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) {
-        if (bin(v) == tb && (v & pmask) == prefix) atomicAdd(&hist[(v >> sft) & dm], 1u);
-      });
-      __syncthreads();
-      find_threshold(hist, rem, sh);
-      rem -= sh.above;
-      prefix |= (uint32_t)sh.t << sft;
-      pmask |= dm << sft;
-      __syncthreads();
-    }
-    if (tid == 0) { sh.kstar = prefix; sh.quota = rem; }
-    __syncthreads();
-  }
-  const uint32_t kstar = sh.kstar;
-  const int quota = sh.quota;
-
-  // 5. emit in index order; each wave owns a 64-aligned segment and reads
-  // UE 64-token steps ahead
-  constexpr int UE = 8;
-  const int SEG = (S + kSelWaves * 64 - 1) / (kSelWaves * 64) * 64;
-  const int wb = wave * SEG, we = min(S, wb + SEG);
-  auto KEY = [&](int j) -> uint32_t {
-    if constexpr (IN_LDS) return lk[j];
-    else return rk[j];
-  };
-  int ngt = 0, neq = 0;
-  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
-    uint32_t v[UE];
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int j = j0 + 64 * u + lane;
-      v[u] = (j < we) ? KEY(j) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const bool ok = j0 + 64 * u + lane < we;
-      ngt += __popcll(__ballot(ok && v[u] > kstar));
-      neq += __popcll(__ballot(ok && v[u] == kstar));
-    }
-  }
-  if (lane == 0) { sh.wgt[wave] = ngt; sh.weq[wave] = neq; }
-  __syncthreads();
-  if (tid == 0) {
-    int eqb = 0, selb = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      sh.eqb[w] = eqb;
-      sh.selb[w] = selb;
-      const int take = min(max(quota - eqb, 0), sh.weq[w]);
-      selb += sh.wgt[w] + take;
-      eqb += sh.weq[w];
-    }
-  }
-  __syncthreads();
-  int selrun = sh.selb[wave], eqrun = sh.eqb[wave];
-  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
-    uint32_t v[UE];
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int j = j0 + 64 * u + lane;
-      v[u] = (j < we) ? KEY(j) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int js = j0 + 64 * u;  // 64-aligned step start
-      if (js >= we) break;         // uniform across the wave
-      const int j = js + lane;
-      const bool ok = j < we;
-      const bool gt = ok && v[u] > kstar, eq = ok && v[u] == kstar;
-      const uint64_t eqm = __ballot(eq);
-      const bool take = gt || (eq && eqrun + bits_below(eqm) < quota);
-      const uint64_t sm = __ballot(take);
-      if (take) orow[selrun + bits_below(sm)] = j;
-      if (lane == 0) {
-        brow[js >> 5] = (uint32_t)sm;
-        brow[(js >> 5) + 1] = (uint32_t)(sm >> 32);
-      }
-      selrun += __popcll(sm);
-      eqrun += __popcll(eqm);
-    }
-  }
+  select_head<kSelThreads, IN_LDS>(rk, lk, hist, S, Sp, k, sh.kmin, sh.kmax, orow, brow, sh);
 }
 
 // Caller-given kept sets -> bitmap (stand-alone attention entry point).
@@ -809,27 +582,26 @@ static hipError_t dispatch_group(int G, F&& f) {
 
 template <typename T>
 static hipError_t qrot_t(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                         bf16_t* qsplit, uint32_t* counters, hipStream_t st) {
+                         bf16_t* qsplit, hipStream_t st) {
   return dispatch_group(p.G, [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
-    // LDS: P[kv] and the queries; the slice sums (256/d slices x GT x d fp32)
-    // reuse P's space, which is at least as large.
-    const size_t lds = (size_t)p.d * p.d * sizeof(T) + (size_t)GT * p.d * sizeof(float);
+    // LDS: P[kv], the queries, and the slice sums
+    const size_t lds = (size_t)p.d * p.d * sizeof(T) + (size_t)GT * p.d * sizeof(float) * (1 + kQrotSlices);
     if (lds > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(&qrot_kernel<T, GT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return hipGetLastError();
-    hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv), dim3(256), lds, st,
-                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, counters,
-                       p.Hq, p.Hkv, p.d);
+    hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv), dim3(kQrotSlices * p.d), lds, st,
+                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, p.Hq,
+                       p.Hkv, p.d);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                       uint16_t* qsplit, uint32_t* counters, hipStream_t st) {
-  return p.dt == 0 ? qrot_t<float>(p, q, P, qrot, qsplit, counters, st)
-                   : qrot_t<bf16_t>(p, q, P, qrot, qsplit, counters, st);
+                       uint16_t* qsplit, hipStream_t st) {
+  return p.dt == 0 ? qrot_t<float>(p, q, P, qrot, qsplit, st)
+                   : qrot_t<bf16_t>(p, q, P, qrot, qsplit, st);
 }
 
 template <typename T, int GT>
@@ -879,7 +651,7 @@ static int max_lds_per_block() {
 
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, int32_t* idx,
                          uint32_t* bitmap, hipStream_t st) {
-  const size_t static_lds = sizeof(SelScratch) + 64;
+  const size_t static_lds = sizeof(SelScratch<kSelThreads>) + 64;
   const size_t lds_in = ((size_t)Sp + kNB) * sizeof(uint32_t);
   const size_t lds_out = (size_t)kNB * sizeof(uint32_t);
   bool in_lds = lds_in + static_lds <= (size_t)max_lds_per_block();

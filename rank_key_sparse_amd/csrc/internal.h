@@ -10,6 +10,8 @@ namespace loki {
 
 constexpr int kMaxGroup = 16;        // largest supported Hq/Hkv
 constexpr int kAttendMfmaTokens = 256;  // tokens per wave in the MFMA attention kernel
+constexpr int kFusedThreads = 512;      // threads of the fused score+select kernel
+constexpr int kFusedMaxS = 16384;       // fused path when a head's keys fit twice per CU's LDS
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -38,7 +40,7 @@ bool make_select_plan(SelectPlan& p, int rows, int S, int k);
 // q_rot in fp32 and, when qsplit is non-null, its three-way bf16 split as
 // MFMA operands qsplit[row][part][d] (part 3 is zero).
 hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                       uint16_t* qsplit, uint32_t* counters, hipStream_t st);
+                       uint16_t* qsplit, hipStream_t st);
 // Scores from `src` = K_rot (ld = d) or a lead-dims copy K_lead (ld = R >= r).
 hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const float* qrot,
                          const uint16_t* qsplit, void* out, bool as_keys, int out_stride,
@@ -57,6 +59,10 @@ hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, 
 // MFMA paths (bf16 storage).
 hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
                               void* out, bool as_keys, int out_stride, hipStream_t st);
+// Fused scores + top-k into idx / bitmap (bf16, S <= kFusedMaxS).
+size_t score_select_lds_bytes(int Sp);
+hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                               int32_t* idx, uint32_t* bitmap, hipStream_t st);
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
                               const uint16_t* qsplit, const uint32_t* bitmap, float* part,
                               hipStream_t st);

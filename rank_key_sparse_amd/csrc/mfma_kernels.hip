@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "internal.h"
+#include "select_core.h"
 
 namespace loki {
 
@@ -147,12 +148,109 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
 }
 
 // ============================================================================
+// Fused approximate scores + top-k, one block of 512 threads per query head
+// (bf16 source, the head's S keys fit in LDS).  The block streams its group's
+// score source (16-token MFMA tiles as in score_mfma_kernel, with only this
+// head's three split columns non-zero), writes the order-preserving keys
+// straight into LDS while tracking their min / max, and then runs the
+// selection of select_core.h in place: no key ever goes to global memory.
+// Block -> (group, head) mapping: the G heads of a (b, kv) group get block
+// ids with the same value mod 8 (the same XCD under round-robin dispatch)
+// and consecutive dispatch order, so their identical reads of the group's
+// source hit in L2 / the Infinity Cache.
+// ============================================================================
+template <int KS>
+__global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
+    const bf16_t* __restrict__ src, int ld, const uint16_t* __restrict__ qsplit, int B, int Hq,
+    int Hkv, int S, int Sp, int d, int r, int k, int W, int32_t* __restrict__ idx,
+    uint32_t* __restrict__ bitmap) {
+  constexpr int NWV = kFusedThreads / 64;
+  constexpr int UK = 8 / KS;
+  constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
+  extern __shared__ __align__(16) uint32_t fdyn[];
+  __shared__ SelScratch<kFusedThreads> sh;
+  uint32_t* lk = fdyn;         // [Sp] keys
+  uint32_t* hist = fdyn + Sp;  // [kNB]
+  const int G = Hq / Hkv;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gh = slot % G, gi = (slot / G) * 8 + xcd;
+  if (gi >= B * Hkv) return;  // padding block (uniform)
+  const int b = gi / Hkv, kv = gi - b * Hkv;
+  const size_t row = (size_t)b * Hq + (size_t)kv * G + gh;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, q = lane >> 4;
+  int32_t* orow = idx + row * k;
+  uint32_t* brow = bitmap + row * W;
+
+  if (k >= S) {
+    keep_all<kFusedThreads>(S, W, orow, brow);
+    return;
+  }
+
+  // B operands: this head alone (column n = split n / 4 when n % 4 == 0)
+  bf16x8_t bv[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) bv[s] = q_operand(qsplit, row, d, 1, r, 0, m, 32 * s + 8 * q);
+
+  const bf16_t* base = src + (size_t)gi * S * ld;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int j0 = wave; 16 * j0 < S; j0 += NWV * U) {
+    uint4 a[U][KS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = 16 * (j0 + NWV * u) + m;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int dim0 = 32 * s + 8 * q;
+        a[u][s] = (t < S && dim0 < r) ? ldg16(base + (size_t)t * ld + dim0) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][s]), bv[s], acc, 0, 0, 0);
+      uint32_t key[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) key[v] = score_key(add_split_columns(acc[v]));
+      const int tb = 16 * (j0 + NWV * u) + 4 * q;  // this lane's 4 tokens
+      if (m == 0 && tb < S) {
+        if (tb + 3 < S) {
+          *reinterpret_cast<uint4*>(lk + tb) = make_uint4(key[0], key[1], key[2], key[3]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (tb + v < S) lk[tb + v] = key[v];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (tb + v < S) { mn = min(mn, key[v]); mx = max(mx, key[v]); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
+  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
+    for (int w = 1; w < NWV; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
+    sh.kmin = lo; sh.kmax = hi;
+  }
+  __syncthreads();
+  select_head<kFusedThreads, true>(nullptr, lk, hist, S, Sp, k, sh.kmin, sh.kmax, orow, brow, sh);
+}
+
+// ============================================================================
 // Exact attention over the kept tokens, bf16 caches, G <= 8.
 // Wave = NT consecutive tokens of one (b, kv) group; four waves per block.
 // The G heads' bitmap words of the span go through LDS (one load per lane)
 // and give the union list (token, head mask).  Then two passes over it:
-//   pass 1: 16-row K tiles in MFMA A layout (a lane reads 8*KS contiguous
-//           dims of one row), up to KT tiles requested before any is used;
+//   pass 1: 16-row K tiles in MFMA A layout (a load instruction reads 64
+//           contiguous bytes of each of 16 rows), up to KT tiles requested
+//           before any is used;
 //           exact scores of all G heads from MFMA, scaled to log2 units,
 //           -inf where a head did not keep the token, into LDS;
 //   per head: m = max, w = 2^(e - m), l = sum w;
@@ -230,23 +328,24 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
 
   const size_t cb = (size_t)bk * S * D;
 
-  // pass 1: exact scores.  B operands: lane quarter q covers dims
-  // [8 KS q, 8 KS (q+1)), step s the 8 dims from 8 KS q + 8 s.
+  // pass 1: exact scores.  k-step s covers dims [32 s, 32 s + 32), lane
+  // quarter q the 8 dims from 32 s + 8 q, so one load instruction reads 64
+  // contiguous bytes of each of the tile's 16 rows.
   {
     bf16x8_t bv[NGRP][KS];
 #pragma unroll
     for (int grp = 0; grp < NGRP; ++grp)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        bv[grp][s] = q_operand(qsplit, head0, D, G, D, grp, m, 8 * KS * q + 8 * s);
+        bv[grp][s] = q_operand(qsplit, head0, D, G, D, grp, m, 32 * s + 8 * q);
     for (int p0 = 0; p0 < n; p0 += 16 * KT) {
       uint4 ka[KT][KS];
 #pragma unroll
       for (int tl = 0; tl < KT; ++tl) {
         const int p = p0 + 16 * tl + m;
-        const bf16_t* row = K_rot + cb + (size_t)(p < n ? tok[p] : 0) * D + 8 * KS * q;
+        const bf16_t* row = K_rot + cb + (size_t)(p < n ? tok[p] : 0) * D + 8 * q;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ka[tl][s] = (p < n) ? ldg16(row + 8 * s) : make_uint4(0u, 0u, 0u, 0u);
+        for (int s = 0; s < KS; ++s) ka[tl][s] = (p < n) ? ldg16(row + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
       }
 #pragma unroll
       for (int tl = 0; tl < KT; ++tl) {
@@ -361,6 +460,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
     pr[2 + c] = A;
     if (c == 0) { pr[0] = M; pr[1] = L; }
   }
+
 }
 
 // ============================================================================
@@ -401,6 +501,38 @@ hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, cons
   if (p.G <= 4) return go(std::integral_constant<int, 4>{});
   if (p.G <= 8) return go(std::integral_constant<int, 8>{});
   return go(std::integral_constant<int, 16>{});
+}
+
+size_t score_select_lds_bytes(int Sp) {
+  return ((size_t)Sp + kNB) * sizeof(uint32_t);
+}
+
+hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                               int32_t* idx, uint32_t* bitmap, hipStream_t st) {
+  if (p.dt != 1) return hipErrorInvalidValue;
+  const size_t lds = score_select_lds_bytes(p.Sp);
+  const int ngroups = p.B * p.Hkv;
+  const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * p.G)), block(kFusedThreads);
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  const int ks = (p.r + 31) / 32;
+  hipError_t e = hipSuccess;
+#define LOKI_SS(K)                                                                                     \
+  case K:                                                                                              \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<K>),                    \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                     \
+    if (e != hipSuccess) return e;                                                                     \
+    hipLaunchKernelGGL((score_select_kernel<K>), grid, block, lds, st, s, ld, qsplit, p.B, p.Hq, p.Hkv, \
+                       p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap);                                    \
+    break;
+  switch (ks) {
+    LOKI_SS(1)
+    LOKI_SS(2)
+    LOKI_SS(3)
+    LOKI_SS(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOKI_SS
+  return hipGetLastError();
 }
 
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,

@@ -70,6 +70,8 @@ DECODE_CASES = {
     "C3@B2S4096": cfg_case("C3", S=4096, B=2),
     "C4@S16384": cfg_case("C4", S=16384),
     "C5@B1S8192": cfg_case("C5", S=8192, B=1),
+    "C3@B8S4096": cfg_case("C3", S=4096, B=8),
+    "C2@B8S4096": cfg_case("C2", S=4096, B=8),      # MHA, >= 256 heads: fused score+select path
     "C2": cfg_case("C2"),
     "C3": cfg_case("C3"),
     "C4": cfg_case("C4"),
@@ -258,6 +260,12 @@ EDGE = [
     ("G8_f32_d128", 1, 16, 2, 1111, 128, "f32", 24, 128),
     ("d64_bf16_r64", 3, 8, 8, 640, 64, "bf16", 64, 64),
     ("global_select", 1, 4, 2, 40000, 128, "bf16", 32, 1500),
+    # fused score+select path (MHA, >= 256 heads, S <= 16384)
+    ("fused_ragged_r24", 16, 16, 16, 1000, 128, "bf16", 24, 77),
+    ("fused_d64_r40", 32, 8, 8, 3001, 64, "bf16", 40, 300),
+    ("fused_r128_k1", 8, 32, 32, 777, 128, "bf16", 128, 1),
+    ("fused_S16384", 4, 64, 64, 16384, 128, "bf16", 32, 700),
+    ("many_heads_G4", 16, 16, 4, 1000, 128, "bf16", 24, 77),
 ]
 
 
@@ -296,6 +304,33 @@ def test_decode_all_equal_keys(gpu_lib):
     assert np.array_equal(idx_g.cpu().numpy(), np.broadcast_to(np.arange(k), (B, Hq, k)))
     out_o = oracle.attend(q, P, Kr, V, np.broadcast_to(np.arange(k), (B, Hq, k)))
     assert max_abs(out_g, out_o) <= OUT_TOL[torch.bfloat16]
+
+
+def test_decode_all_equal_keys_fused(gpu_lib):
+    B, Hq, Hkv, S, d = 64, 4, 4, 2000, 128  # 256 MHA heads: fused path
+    Kr = torch.ones((B, Hkv, S, d), dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(1)
+    V = torch.randn((B, Hkv, S, d), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g).to(torch.bfloat16)
+    P = torch.eye(d).expand(Hkv, d, d).contiguous().to(torch.bfloat16)
+    k = 333
+    out_g, idx_g = gpu_lib.loki_decode(dev(q), dev(P), dev(Kr), dev(V), r=32, k=k,
+                                       K_lead=dev(Kr[..., :32].contiguous()))
+    assert np.array_equal(idx_g.cpu().numpy(), np.broadcast_to(np.arange(k), (B, Hq, k)))
+    out_o = oracle.attend(q, P, Kr, V, np.broadcast_to(np.arange(k), (B, Hq, k)))
+    assert max_abs(out_g, out_o) <= OUT_TOL[torch.bfloat16]
+
+
+def test_fused_matches_two_kernel_path(gpu_lib):
+    # the same heads decoded with 256 (fused) and 128 (two kernels) query heads
+    cfg = cfg_case("C2", S=4096, B=8)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    o_all, i_all = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k)
+    o_half, i_half = gpu_lib.loki_decode(q[:4].contiguous(), P, Kr[:4].contiguous(), V[:4].contiguous(),
+                                         r=cfg.r, k=cfg.k)
+    assert torch.equal(i_all[:4], i_half)
+    assert torch.equal(o_all[:4].view(torch.int16), o_half.view(torch.int16))
 
 
 def test_decode_deterministic(gpu_lib):
