@@ -164,9 +164,11 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
   } else {
-    LOKI_HIP(launch_scores(p, src, ld, qrot, qsplit, keys, true, p.Sp, stream));
+    uint2* mm = select_needs_minmax(S) ? at<uint2>(workspace, p.off_mm) : nullptr;
+    LOKI_HIP(launch_scores(p, src, ld, qrot, qsplit, keys, true, p.Sp, mm, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
-    LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+    LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, mm, p.NSC, at<uint32_t>(workspace, p.off_masks),
+                           idx, bitmap, stream));
   }
   if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
   LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
@@ -232,7 +234,7 @@ loki_status loki_scores(const void* q, const void* P, const void* K_rot, float* 
     float* qrot = at<float>(workspace, p.off_qrot);
     uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
     LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
-    LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, scores, false, S, stream));
+    LOKI_HIP(launch_scores(p, K_rot, d, qrot, qsplit, scores, false, S, nullptr, stream));
     return LOKI_OK;
   } catch (...) {
     return LOKI_ERR_INTERNAL;
@@ -258,8 +260,10 @@ loki_status loki_select_topk(const float* scores, int32_t* idx, int32_t rows, in
     LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
     uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
     uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
-    LOKI_HIP(launch_scores_to_keys(scores, keys, rows, S, p.Sp, stream));
-    LOKI_HIP(launch_select(rows, S, p.Sp, k, p.W, keys, idx, bitmap, stream));
+    uint2* mm = at<uint2>(workspace, p.off_mm);
+    LOKI_HIP(launch_scores_to_keys(scores, keys, mm, p.NMM, rows, S, p.Sp, stream));
+    LOKI_HIP(launch_select(rows, S, p.Sp, k, p.W, keys, mm, p.NMM, at<uint32_t>(workspace, p.off_masks),
+                           idx, bitmap, stream));
     return LOKI_OK;
   } catch (...) {
     return LOKI_ERR_INTERNAL;

@@ -119,8 +119,9 @@ template <typename T, int LPT, int GT>
 __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ src,
                                                     const float* __restrict__ qrot,
                                                     void* __restrict__ out, int as_keys,
-                                                    int out_stride, int Hq, int Hkv, int S, int d,
-                                                    int ld, int r, int SC) {
+                                                    int out_stride, uint2* __restrict__ mm,
+                                                    int Hq, int Hkv, int S, int d, int ld, int r,
+                                                    int SC) {
   constexpr int EPL = Gran<T>::N;
   constexpr int TPI = 256 / LPT;  // tokens per block pass
   constexpr int U = 8;            // passes whose loads are in flight together
@@ -140,6 +141,11 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ src,
 
   const T* base = src + (size_t)bk * S * ld + gran * EPL;
   const size_t orow0 = ((size_t)b * Hq + (size_t)kv * G) * out_stride;
+  __shared__ uint32_t smn[GT], smx[GT];
+  if (threadIdx.x < GT) { smn[threadIdx.x] = 0xffffffffu; smx[threadIdx.x] = 0u; }
+  uint32_t mn[GT], mx[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) { mn[g] = 0xffffffffu; mx[g] = 0u; }
   for (int tb = t0; tb < t1; tb += TPI * U) {
     uint4 buf[U];
 #pragma unroll
@@ -165,88 +171,104 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ src,
         for (int g = 0; g < GT; ++g) {
           if (g % LPT == gran && g < G) {
             const size_t o = orow0 + (size_t)g * out_stride + t;
-            if (as_keys) static_cast<uint32_t*>(out)[o] = score_key(s[g]);
-            else static_cast<float*>(out)[o] = s[g];
+            if (as_keys) {
+              const uint32_t key = score_key(s[g]);
+              static_cast<uint32_t*>(out)[o] = key;
+              mn[g] = min(mn[g], key);
+              mx[g] = max(mx[g], key);
+            } else {
+              static_cast<float*>(out)[o] = s[g];
+            }
           }
         }
       }
     }
   }
+  if (as_keys && mm) {  // uniform: the chunk's min / max key per head
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
+      if (g % LPT == gran && g < G && mn[g] <= mx[g]) { atomicMin(&smn[g], mn[g]); atomicMax(&smx[g], mx[g]); }
+    __syncthreads();
+    if (threadIdx.x < G)
+      mm[((size_t)b * Hq + (size_t)kv * G + threadIdx.x) * gridDim.x + blockIdx.x] =
+          make_uint2(smn[threadIdx.x], smx[threadIdx.x]);
+  }
 }
 
 // fp32 scores -> keys, for the stand-alone selection entry point.
 __global__ __launch_bounds__(256) void scores_to_keys_kernel(const float* __restrict__ s,
-                                                             uint32_t* __restrict__ keys, int S,
+                                                             uint32_t* __restrict__ keys,
+                                                             uint2* __restrict__ mm, int S,
                                                              int Sp) {
-  const int row = blockIdx.y;
-  for (int j = blockIdx.x * 256 + threadIdx.x; j < S; j += gridDim.x * 256)
-    keys[(size_t)row * Sp + j] = score_key(s[(size_t)row * S + j]);
+  __shared__ uint32_t red[2][4];
+  const int row = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < S; j += gridDim.x * 256) {
+    const uint32_t key = score_key(s[(size_t)row * S + j]);
+    keys[(size_t)row * Sp + j] = key;
+    mn = min(mn, key);
+    mx = max(mx, key);
+  }
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
+  if (lane == 0) { red[0][wave] = mn; red[1][wave] = mx; }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    mm[(size_t)row * gridDim.x + blockIdx.x] =
+        make_uint2(min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3])),
+                   max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3])));
 }
 
 // ============================================================================
 // Top-k selection from workspace keys, one block of 1024 threads per query
-// head (see select_core.h): the row's keys are copied to LDS when they fit
-// (IN_LDS), else every pass re-reads them from global memory (L2 / Infinity
-// Cache).  Min / max are found during the first read.
+// head (see select_core.h).  Heads of up to 1024 T tokens load their keys
+// once into registers (coalesced dword loads, lane l of wave w reading tokens
+// w*64T + 64i + l); longer heads stream their keys from global memory with
+// min / max from the per-chunk extremes mm and step masks in gmasks.
 // ============================================================================
 constexpr int kSelThreads = 1024;
 
-template <bool IN_LDS>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const uint32_t* __restrict__ keys, int S,
-                                                             int Sp, int k, int W,
-                                                             int32_t* __restrict__ idx,
-                                                             uint32_t* __restrict__ bitmap) {
-  constexpr int NW = kSelThreads / 64;
-  extern __shared__ __align__(16) uint32_t dyn[];
+// T = 16 is held to 64 VGPRs so that two blocks share a CU.
+template <int T>
+__global__ __launch_bounds__(kSelThreads, T <= 16 ? 8 : 4) void select_regs_kernel(const uint32_t* __restrict__ keys,
+                                                                  int S, int Sp, int k, int W,
+                                                                  int32_t* __restrict__ idx,
+                                                                  uint32_t* __restrict__ bitmap) {
+  __shared__ uint32_t lds[kNB];
+  __shared__ uint32_t take[kSelThreads * T / 32];
   __shared__ SelScratch<kSelThreads> sh;
-  uint32_t* lk = dyn;                          // [Sp] keys (IN_LDS only)
-  uint32_t* hist = dyn + (IN_LDS ? Sp : 0);    // [kNB]
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.x;
   const uint32_t* rk = keys + (size_t)row * Sp;
   int32_t* orow = idx + (size_t)row * k;
   uint32_t* brow = bitmap + (size_t)row * W;
-
   if (k >= S) {
     keep_all<kSelThreads>(S, W, orow, brow);
     return;
   }
-  // min / max, and the copy of the row to LDS (8 loads per thread in flight)
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(rk);
-    uint4* dst = reinterpret_cast<uint4*>(lk);
-    const int n4 = Sp >> 2;  // Sp is a multiple of 64
-    for (int base = 0; base < n4; base += kSelThreads * 8) {
-      uint4 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kSelThreads + tid;
-        v[u] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = base + u * kSelThreads + tid;
-        if (i >= n4) continue;
-        if constexpr (IN_LDS) dst[i] = v[u];
-        const int j = i << 2;
-        if (j < S) { mn = min(mn, v[u].x); mx = max(mx, v[u].x); }
-        if (j + 1 < S) { mn = min(mn, v[u].y); mx = max(mx, v[u].y); }
-        if (j + 2 < S) { mn = min(mn, v[u].z); mx = max(mx, v[u].z); }
-        if (j + 3 < S) { mn = min(mn, v[u].w); mx = max(mx, v[u].w); }
-      }
-    }
+  uint32_t key[T];
+  load_regs<T>(rk, S, key);
+  select_regs<kSelThreads, T>(key, lds, take, S, k, W, orow, brow, sh);
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_global_kernel(const uint32_t* __restrict__ keys,
+                                                                    const uint2* __restrict__ mm,
+                                                                    int nmm, uint32_t* __restrict__ gmasks,
+                                                                    int S, int Sp, int k, int W,
+                                                                    int32_t* __restrict__ idx,
+                                                                    uint32_t* __restrict__ bitmap) {
+  __shared__ uint32_t hist[kNB];
+  __shared__ SelScratch<kSelThreads> sh;
+  const int row = blockIdx.x;
+  int32_t* orow = idx + (size_t)row * k;
+  uint32_t* brow = bitmap + (size_t)row * W;
+  if (k >= S) {
+    keep_all<kSelThreads>(S, W, orow, brow);
+    return;
   }
-  mn = wave_min_u(mn);
-  mx = wave_max_u(mx);
-  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t a = sh.red[0][0], c = sh.red[1][0];
-    for (int w = 1; w < NW; ++w) { a = min(a, sh.red[0][w]); c = max(c, sh.red[1][w]); }
-    sh.kmin = a; sh.kmax = c;
-  }
-  __syncthreads();
-  select_head<kSelThreads, IN_LDS>(rk, lk, hist, S, Sp, k, sh.kmin, sh.kmax, orow, brow, sh);
+  for (int i = threadIdx.x; i < kNB; i += kSelThreads) hist[i] = 0u;
+  select_head<kSelThreads>(keys + (size_t)row * Sp, mm + (size_t)row * nmm, nmm, hist,
+                           gmasks + (size_t)row * (Sp / 16), S, Sp, k, orow, brow, sh);
 }
 
 // Caller-given kept sets -> bitmap (stand-alone attention entry point).
@@ -553,6 +575,8 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
   p.off_qrot = off;   off = align_up(off + rows * d * sizeof(float), 256);
   p.off_qsplit = off; off = align_up(off + rows * 4 * d * sizeof(uint16_t), 256);
   p.off_keys = off;   off = align_up(off + rows * (size_t)p.Sp * sizeof(uint32_t), 256);
+  p.off_mm = off;     off = align_up(off + rows * (size_t)p.NSC * sizeof(uint2), 256);
+  p.off_masks = off;  off = align_up(off + rows * (size_t)(p.Sp / 16) * sizeof(uint32_t), 256);
   p.off_bitmap = off; off = align_up(off + rows * (size_t)p.W * sizeof(uint32_t), 256);
   p.off_part = off;   off = align_up(off + rows * (size_t)p.NAC * (d + 2) * sizeof(float), 256);
   p.bytes = off;
@@ -564,8 +588,11 @@ bool make_select_plan(SelectPlan& p, int rows, int S, int k) {
   p.rows = rows; p.S = S; p.k = k;
   p.Sp = (S + 63) / 64 * 64;
   p.W = p.Sp / 32;
+  p.NMM = (S + 255) / 256 < 1024 ? (S + 255) / 256 : 1024;
   size_t off = 0;
   p.off_keys = off;   off = align_up(off + (size_t)rows * p.Sp * sizeof(uint32_t), 256);
+  p.off_mm = off;     off = align_up(off + (size_t)rows * p.NMM * sizeof(uint2), 256);
+  p.off_masks = off;  off = align_up(off + (size_t)rows * (p.Sp / 16) * sizeof(uint32_t), 256);
   p.off_bitmap = off; off = align_up(off + (size_t)rows * p.W * sizeof(uint32_t), 256);
   p.bytes = off;
   return true;
@@ -606,7 +633,7 @@ hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float*
 
 template <typename T, int GT>
 static hipError_t scores_tg(const DecodePlan& p, const void* src, int ld, const float* qrot, void* out,
-                            bool as_keys, int out_stride, hipStream_t st) {
+                            bool as_keys, int out_stride, uint2* mm, hipStream_t st) {
   const int e = (int)sizeof(T);
   const int gran = (p.r * e + 15) / 16;
   const int lpt = next_pow2(gran);
@@ -616,7 +643,7 @@ static hipError_t scores_tg(const DecodePlan& p, const void* src, int ld, const 
 #define LOKI_SCORE(L)                                                                         \
   case L:                                                                                     \
     hipLaunchKernelGGL((score_kernel<T, L, GT>), grid, block, 0, st, K, qrot, out, ak,       \
-                       out_stride, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                         \
+                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                     \
     break;
   switch (lpt) {
     LOKI_SCORE(1)
@@ -633,49 +660,36 @@ static hipError_t scores_tg(const DecodePlan& p, const void* src, int ld, const 
 
 hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const float* qrot,
                          const uint16_t* qsplit, void* out, bool as_keys, int out_stride,
-                         hipStream_t st) {
-  if (p.dt == 1) return launch_scores_mfma(p, src, ld, qsplit, out, as_keys, out_stride, st);
+                         uint2* mm, hipStream_t st) {
+  if (p.dt == 1) return launch_scores_mfma(p, src, ld, qsplit, out, as_keys, out_stride, mm, st);
   return dispatch_group(p.G, [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
-    return p.dt == 0 ? scores_tg<float, GT>(p, src, ld, qrot, out, as_keys, out_stride, st)
-                     : scores_tg<bf16_t, GT>(p, src, ld, qrot, out, as_keys, out_stride, st);
+    return p.dt == 0 ? scores_tg<float, GT>(p, src, ld, qrot, out, as_keys, out_stride, mm, st)
+                     : scores_tg<bf16_t, GT>(p, src, ld, qrot, out, as_keys, out_stride, mm, st);
   });
 }
 
-static int max_lds_per_block() {
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 65536;
-  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 65536;
-  return v;
-}
+bool select_needs_minmax(int S) { return S > kSelThreads * kSelRegMaxT; }
 
-hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, int32_t* idx,
-                         uint32_t* bitmap, hipStream_t st) {
-  const size_t static_lds = sizeof(SelScratch<kSelThreads>) + 64;
-  const size_t lds_in = ((size_t)Sp + kNB) * sizeof(uint32_t);
-  const size_t lds_out = (size_t)kNB * sizeof(uint32_t);
-  bool in_lds = lds_in + static_lds <= (size_t)max_lds_per_block();
-  if (in_lds && hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<true>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)lds_in) != hipSuccess) {
-    (void)hipGetLastError();  // clear it: the row then streams from global memory
-    in_lds = false;
-  }
-  if (in_lds) {
-    hipLaunchKernelGGL((select_kernel<true>), dim3(rows), dim3(kSelThreads), lds_in, st, keys, S, Sp,
-                       k, W, idx, bitmap);
-  } else {
-    hipLaunchKernelGGL((select_kernel<false>), dim3(rows), dim3(kSelThreads), lds_out, st, keys, S,
+hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
+                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st) {
+  if (S <= kSelThreads * 16) {
+    hipLaunchKernelGGL((select_regs_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
+                       idx, bitmap);
+  } else if (S <= kSelThreads * kSelRegMaxT) {
+    hipLaunchKernelGGL((select_regs_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, keys, S,
                        Sp, k, W, idx, bitmap);
+  } else {
+    if (!mm || !gmasks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_global_kernel, dim3(rows), dim3(kSelThreads), 0, st, keys, mm, nmm, gmasks,
+                       S, Sp, k, W, idx, bitmap);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, int rows, int S, int Sp,
-                                 hipStream_t st) {
-  int bx = (S + 255) / 256;
-  if (bx > 1024) bx = 1024;
-  hipLaunchKernelGGL(scores_to_keys_kernel, dim3(bx, rows), dim3(256), 0, st, scores, keys, S, Sp);
+hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, uint2* mm, int nmm, int rows,
+                                 int S, int Sp, hipStream_t st) {
+  hipLaunchKernelGGL(scores_to_keys_kernel, dim3(nmm, rows), dim3(256), 0, st, scores, keys, mm, S, Sp);
   return hipGetLastError();
 }
 

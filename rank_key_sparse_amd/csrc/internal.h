@@ -11,7 +11,8 @@ namespace loki {
 constexpr int kMaxGroup = 16;        // largest supported Hq/Hkv
 constexpr int kAttendMfmaTokens = 256;  // tokens per wave in the MFMA attention kernel
 constexpr int kFusedThreads = 512;      // threads of the fused score+select kernel
-constexpr int kFusedMaxS = 16384;       // fused path when a head's keys fit twice per CU's LDS
+constexpr int kFusedMaxS = 16384;       // fused path: a head's keys fit in LDS and in 512 x 32 registers
+constexpr int kSelRegMaxT = 32;         // selection keeps up to 1024 x 32 keys of a head in registers
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -22,7 +23,10 @@ struct DecodePlan {
   int W;         // bitmap words per query head: Sp / 32
   int SC, NSC;   // approximate-score kernel: tokens per block, blocks per (b,kv)
   int AC, NAC;   // attention kernel: tokens per block, blocks per (b,kv)
-  size_t off_qrot, off_qsplit, off_keys, off_bitmap, off_part, bytes;
+  // workspace: q_rot, its bf16 split, keys [row][Sp], per-score-chunk key
+  // extremes [row][NSC] (uint2 min, max), selection masks [row][Sp/16] (used
+  // when a row's keys do not fit in LDS), bitmap [row][W], attention partials
+  size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_bitmap, off_part, bytes;
 };
 
 // Fills `p` from the sizes; returns false if they are out of the supported range
@@ -32,7 +36,8 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
 // Selection-only plan (loki_select_topk).
 struct SelectPlan {
   int rows, S, Sp, W, k;
-  size_t off_keys, off_bitmap, bytes;
+  int NMM;  // key-conversion blocks per row (one min / max pair each)
+  size_t off_keys, off_mm, off_masks, off_bitmap, bytes;
 };
 bool make_select_plan(SelectPlan& p, int rows, int S, int k);
 
@@ -42,13 +47,19 @@ bool make_select_plan(SelectPlan& p, int rows, int S, int k);
 hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
                        uint16_t* qsplit, hipStream_t st);
 // Scores from `src` = K_rot (ld = d) or a lead-dims copy K_lead (ld = R >= r).
+// With as_keys, `out` receives order-preserving keys and, when mm is not
+// null, mm[row][chunk] the min / max key of each of the NSC score chunks.
 hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const float* qrot,
                          const uint16_t* qsplit, void* out, bool as_keys, int out_stride,
-                         hipStream_t st);
-hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys,
-                         int32_t* idx, uint32_t* bitmap, hipStream_t st);
-hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, int rows, int S, int Sp,
-                                 hipStream_t st);
+                         uint2* mm, hipStream_t st);
+// Top-k of each key row.  Rows longer than the register form
+// (select_needs_minmax) also need mm[row][0..nmm), min / max pairs covering
+// the row, and gmasks (rows * Sp / 16 words of scratch); else both may be null.
+bool select_needs_minmax(int S);
+hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
+                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st);
+hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, uint2* mm, int nmm, int rows,
+                                 int S, int Sp, hipStream_t st);
 hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,
                                 hipStream_t st);
 // Attention then the partial merge; `mid` (may be null) is recorded between them.
@@ -58,7 +69,7 @@ hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, 
 // K_rot = K P; when K_lead is non-null its rows also receive the leading R dims.
 // MFMA paths (bf16 storage).
 hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
-                              void* out, bool as_keys, int out_stride, hipStream_t st);
+                              void* out, bool as_keys, int out_stride, uint2* mm, hipStream_t st);
 // Fused scores + top-k into idx / bitmap (bf16, S <= kFusedMaxS).
 size_t score_select_lds_bytes(int Sp);
 hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,

@@ -78,8 +78,8 @@ template <int GT, int KS, bool KEYS>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restrict__ src,
                                                          const uint16_t* __restrict__ qsplit,
                                                          void* __restrict__ out, int out_stride,
-                                                         int Hq, int Hkv, int S, int d, int ld,
-                                                         int r, int SC) {
+                                                         uint2* __restrict__ mm, int Hq, int Hkv,
+                                                         int S, int d, int ld, int r, int SC) {
   constexpr int NGRP = (GT + 3) / 4;
   constexpr int UK = 8 / (KS * NGRP);
   constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
@@ -98,6 +98,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
       bv[grp][s] = q_operand(qsplit, head0, d, G, r, grp, m, 32 * s + 8 * q);
 
   const bf16_t* base = src + (size_t)bk * S * ld;
+  __shared__ uint32_t smn[GT], smx[GT];
+  if (KEYS && threadIdx.x < GT) { smn[threadIdx.x] = 0xffffffffu; smx[threadIdx.x] = 0u; }
+  uint32_t mn[NGRP], mx[NGRP];
+#pragma unroll
+  for (int grp = 0; grp < NGRP; ++grp) { mn[grp] = 0xffffffffu; mx[grp] = 0u; }
   for (int j0 = wave; t0 + 16 * j0 < t1; j0 += 4 * U) {
     uint4 a[U][KS];
 #pragma unroll
@@ -126,14 +131,19 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
           const size_t o = (head0 + g) * (size_t)out_stride + tb;
           if constexpr (KEYS) {
             uint32_t* ko = static_cast<uint32_t*>(out);
+            uint32_t key[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) key[v] = score_key(x[v]);
             if (tb + 3 < t1) {
-              *reinterpret_cast<uint4*>(ko + o) =
-                  make_uint4(score_key(x[0]), score_key(x[1]), score_key(x[2]), score_key(x[3]));
+              *reinterpret_cast<uint4*>(ko + o) = make_uint4(key[0], key[1], key[2], key[3]);
             } else {
 #pragma unroll
               for (int v = 0; v < 4; ++v)
-                if (tb + v < t1) ko[o + v] = score_key(x[v]);
+                if (tb + v < t1) ko[o + v] = key[v];
             }
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (tb + v < t1) { mn[grp] = min(mn[grp], key[v]); mx[grp] = max(mx[grp], key[v]); }
           } else {
             float* fo = static_cast<float*>(out);
 #pragma unroll
@@ -144,6 +154,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (KEYS && mm) {  // uniform: the chunk's min / max key per head
+    __syncthreads();
+#pragma unroll
+    for (int grp = 0; grp < NGRP; ++grp) {
+      const int g = 4 * grp + m;
+      if (m < 4 && g < G && mn[grp] <= mx[grp]) { atomicMin(&smn[g], mn[grp]); atomicMax(&smx[g], mx[grp]); }
+    }
+    __syncthreads();
+    if (threadIdx.x < G) mm[(head0 + threadIdx.x) * gridDim.x + blockIdx.x] = make_uint2(smn[threadIdx.x], smx[threadIdx.x]);
   }
 }
 
@@ -167,10 +187,11 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
   constexpr int NWV = kFusedThreads / 64;
   constexpr int UK = 8 / KS;
   constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
-  extern __shared__ __align__(16) uint32_t fdyn[];
+  constexpr int T = kFusedMaxS / kFusedThreads;  // keys per lane in the selection
+  extern __shared__ __align__(16) uint32_t lk[];  // [Sp] keys
+  __shared__ uint32_t sel[kNB];
+  __shared__ uint32_t take[kFusedMaxS / 32];
   __shared__ SelScratch<kFusedThreads> sh;
-  uint32_t* lk = fdyn;         // [Sp] keys
-  uint32_t* hist = fdyn + Sp;  // [kNB]
   const int G = Hq / Hkv;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int gh = slot % G, gi = (slot / G) * 8 + xcd;
@@ -193,7 +214,6 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
   for (int s = 0; s < KS; ++s) bv[s] = q_operand(qsplit, row, d, 1, r, 0, m, 32 * s + 8 * q);
 
   const bf16_t* base = src + (size_t)gi * S * ld;
-  uint32_t mn = 0xffffffffu, mx = 0u;
   for (int j0 = wave; 16 * j0 < S; j0 += NWV * U) {
     uint4 a[U][KS];
 #pragma unroll
@@ -223,24 +243,14 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
           for (int v = 0; v < 4; ++v)
             if (tb + v < S) lk[tb + v] = key[v];
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (tb + v < S) { mn = min(mn, key[v]); mx = max(mx, key[v]); }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mn = wave_min_u(mn);
-  mx = wave_max_u(mx);
-  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t lo = sh.red[0][0], hi = sh.red[1][0];
-    for (int w = 1; w < NWV; ++w) { lo = min(lo, sh.red[0][w]); hi = max(hi, sh.red[1][w]); }
-    sh.kmin = lo; sh.kmax = hi;
-  }
-  __syncthreads();
-  select_head<kFusedThreads, true>(nullptr, lk, hist, S, Sp, k, sh.kmin, sh.kmax, orow, brow, sh);
+  uint32_t key[T];  // the selection's register layout
+  load_regs<T>(lk, S, key);
+  select_regs<kFusedThreads, T>(key, sel, take, S, k, W, orow, brow, sh);
 }
 
 // ============================================================================
@@ -468,14 +478,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
 // ============================================================================
 template <int GT, bool KEYS>
 static hipError_t score_mfma_g(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
-                               void* out, int out_stride, hipStream_t st) {
+                               void* out, int out_stride, uint2* mm, hipStream_t st) {
   const dim3 grid(p.NSC, p.B * p.Hkv), block(256);
   const bf16_t* s = static_cast<const bf16_t*>(src);
   const int ks = (p.r + 31) / 32;
 #define LOKI_SM(K)                                                                                 \
   case K:                                                                                          \
     hipLaunchKernelGGL((score_mfma_kernel<GT, K, KEYS>), grid, block, 0, st, s, qsplit, out,       \
-                       out_stride, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                          \
+                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                      \
     break;
   switch (ks) {
     LOKI_SM(1)
@@ -489,12 +499,12 @@ static hipError_t score_mfma_g(const DecodePlan& p, const void* src, int ld, con
 }
 
 hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
-                              void* out, bool as_keys, int out_stride, hipStream_t st) {
+                              void* out, bool as_keys, int out_stride, uint2* mm, hipStream_t st) {
   if (p.dt != 1 || p.SC % 16 != 0) return hipErrorInvalidValue;
   auto go = [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
-    return as_keys ? score_mfma_g<GT, true>(p, src, ld, qsplit, out, out_stride, st)
-                   : score_mfma_g<GT, false>(p, src, ld, qsplit, out, out_stride, st);
+    return as_keys ? score_mfma_g<GT, true>(p, src, ld, qsplit, out, out_stride, mm, st)
+                   : score_mfma_g<GT, false>(p, src, ld, qsplit, out, out_stride, mm, st);
   };
   if (p.G <= 1) return go(std::integral_constant<int, 1>{});
   if (p.G <= 2) return go(std::integral_constant<int, 2>{});
@@ -504,7 +514,7 @@ hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, cons
 }
 
 size_t score_select_lds_bytes(int Sp) {
-  return ((size_t)Sp + kNB) * sizeof(uint32_t);
+  return (size_t)Sp * sizeof(uint32_t);
 }
 
 hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,

@@ -1,18 +1,26 @@
-// Per-query-head top-k selection, shared by the selection kernel (keys from
-// the workspace) and the fused score+select kernel (keys computed into LDS).
+// Per-query-head top-k selection, shared by the selection kernels (keys from
+// the workspace) and the fused score+select kernel (keys computed on chip).
 //
-// Given the order-preserving keys of one head (in LDS, or re-read from
-// global memory) and their min / max:
-// 1. histogram of the scores in kNB equal-width value bins over [min, max]
-//    (a monotone map, so bins order like keys);
-// 2. scan bins from the top to find the bin t holding the k-th largest;
-// 3. resolve the exact k-th key K* inside bin t: rank the (few) candidates
-//    of bin t by (key desc, index asc) in LDS; if bin t is too full (heavily
-//    tied or degenerate scores) run an exact 11/11/10-bit MSB radix select
-//    restricted to bin t instead;
-// 4. emit, in index order: key > K*, or key == K* among the first `quota`
-//    such tokens (lower index wins).  Each wave owns a 64-aligned token
-//    segment, so the kept-token bitmap words are written without atomics.
+// The scores of a head are mapped to order-preserving uint32 keys.  Then:
+// 1. histogram of the keys in kNB equal-width value bins over [min, max] (a
+//    monotone map, so bins order like keys); scan the bins from the top for
+//    the bin t holding the k-th largest key;
+// 2. one pass in index order: per 64-token step, a mask of the tokens above
+//    bin t (all kept), and the tokens of bin t (typically a few) collected;
+// 3. the need = k - |above| best tokens of bin t by (key desc, index asc)
+//    are marked taken: ranked pairwise when bin t is small; when it is
+//    crowded (heavy ties, degenerate scores) an exact 11/11/10-bit MSB radix
+//    select inside bin t finds the k-th key K* and its tie quota, and a pass
+//    in index order takes key > K* and the first `quota` keys equal to K*
+//    (lower index wins);
+// 4. emit kept = above | taken: per-step counts, a block prefix, indices
+//    compacted in ascending order, and the kept-token bitmap words.
+//
+// Two forms.  select_regs: the head's keys sit in registers (lane l of wave
+// w holds tokens w*64T + 64i + l, i < T), so every pass is a register pass
+// and each step's mask lives in one lane.  select_head: the keys stay in
+// global memory and are streamed once per pass (heads too long for
+// registers); the step masks go to global scratch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,33 +30,53 @@
 namespace loki {
 
 constexpr int kNB = 2048;      // value bins
-constexpr int kCap = 1024;     // candidates ranked in LDS (2 * kCap words alias the bins)
-constexpr int kRankLds = 256;  // rank limit when the keys themselves are in LDS
+constexpr int kCap = 1024;     // candidates collected (2 * kCap words alias the bins)
+constexpr int kRankMax = 256;  // candidates ranked pairwise; more go to the radix path
 
 template <int NTHR>
 struct SelScratch {
   static constexpr int NW = NTHR / 64;
   uint32_t red[2][NW];
   int scan[NW];
-  int wgt[NW], weq[NW], selb[NW], eqb[NW];
-  uint32_t kmin, kmax, kstar;
-  int t, above, quota, ccount;
+  int wsel[NW], weq[NW];
+  uint32_t kmin, kmax;
+  int t, above, ccount;
 };
 
-// Inclusive prefix sum over the block in thread order.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+
+// Inclusive prefix sum over a wave (DPP row shifts, then row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_i<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_i<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_i<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_i<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Sum of part[w] over the waves w below this one.
+template <int NTHR>
+__device__ __forceinline__ int waves_below(const int* part) {
+  const int wave = threadIdx.x >> 6;
+  int add = 0;
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) add += (w < wave) ? part[w] : 0;
+  return add;
+}
+
+// Inclusive prefix sum over the block in thread order.  sh.scan may be
+// reused only after a later barrier.
 template <int NTHR>
 __device__ __forceinline__ int block_incl_scan(int v, SelScratch<NTHR>& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  if (lane == 63) sh.scan[wave] = v;
+  v = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) sh.scan[threadIdx.x >> 6] = v;
   __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += sh.scan[w];
-  __syncthreads();
-  return v + add;
+  return v + waves_below<NTHR>(sh.scan);
 }
 
 // Find, scanning bins from the top, the bin holding the `want`-th largest key
@@ -86,13 +114,224 @@ struct Binner {
   }
 };
 
+// Block-wide min / max of per-thread partial extremes into sh.kmin / sh.kmax.
+template <int NTHR>
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelScratch<NTHR>& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
+  if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = sh.red[0][0], b = sh.red[1][0];
+    for (int w = 1; w < SelScratch<NTHR>::NW; ++w) { a = min(a, sh.red[0][w]); b = max(b, sh.red[1][w]); }
+    sh.kmin = a;
+    sh.kmax = b;
+  }
+  __syncthreads();
+}
+
+// Writes idx (ascending) and the kept-token bitmap when every token is kept.
+template <int NTHR>
+__device__ __forceinline__ void keep_all(int S, int W, int32_t* orow, uint32_t* brow) {
+  for (int j = threadIdx.x; j < S; j += NTHR) orow[j] = j;
+  for (int w = threadIdx.x; w < W; w += NTHR) {
+    const int lo = 32 * w;
+    brow[w] = (lo + 32 <= S) ? 0xffffffffu : (lo >= S ? 0u : ((1u << (S - lo)) - 1u));
+  }
+}
+
+// A copy of x that the compiler cannot match with earlier values, so that
+// cheap per-phase quantities (token numbers, validity) are recomputed rather
+// than kept live across the whole selection.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Ranks the nc collected candidates (ck, ci) by (key desc, index asc) and
+// calls set(index) for the `need` best.
+template <int NTHR, typename F>
+__device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32_t* ci, int nc, int need,
+                                                F&& set) {
+  for (int i = threadIdx.x; i < nc; i += NTHR) {
+    const uint32_t vi = ck[i], ii = ci[i];
+    int rank = 0;
+    for (int c = 0; c < nc; ++c) {
+      const uint32_t vc = ck[c], ic = ci[c];
+      rank += (vc > vi) || (vc == vi && ic < ii);
+    }
+    if (rank < need) set(ii);
+  }
+}
+
+// ============================================================================
+// Keys in registers.  Requires S <= NTHR * T and k < S.  lds: kNB words
+// (bins, candidates, then the index list when k <= kNB); take: W words of
+// LDS, W = 2 ceil(S / 64).  All threads of the block call it.
+// ============================================================================
+
+// Token of key[0] of this lane (key[i] is token tok0 + 64 i), and the number
+// of this lane's keys that are below S.
+template <int T>
+__device__ __forceinline__ int regs_tok0() {
+  return (int)(threadIdx.x >> 6) * 64 * T + (int)(threadIdx.x & 63);
+}
+template <int T>
+__device__ __forceinline__ int regs_valid(int S) {
+  const int left = S - regs_tok0<T>();
+  return left <= 0 ? 0 : min(T, (left + 63) >> 6);
+}
+
+// Loads a head's keys in the register layout; src[0..S) in LDS or global
+// memory.  Lanes past S read token S - 1 (always in bounds; never used).
+template <int T>
+__device__ __forceinline__ void load_regs(const uint32_t* src, int S, uint32_t (&key)[T]) {
+  const int tok0 = regs_tok0<T>();
+#pragma unroll
+  for (int i = 0; i < T; ++i) key[i] = src[min(tok0 + 64 * i, S - 1)];
+}
+
+template <int NTHR, int T>
+__device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* lds, uint32_t* take,
+                                            int S, int k, int W, int32_t* orow, uint32_t* brow,
+                                            SelScratch<NTHR>& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* hist = lds;
+
+  for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
+  for (int i = tid; i < W; i += NTHR) take[i] = 0u;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  int nv = opaque(regs_valid<T>(S));
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+    if (i < nv) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
+  block_minmax<NTHR>(mn, mx, sh);  // its barriers also order the zeroing
+  Binner bin;
+  bin.init(sh.kmin, sh.kmax);
+
+  // 1. histogram and threshold bin
+  nv = opaque(nv);
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+    if (i < nv) atomicAdd(&hist[bin(key[i])], 1u);
+  __syncthreads();
+  find_threshold<NTHR>(hist, k, sh);
+  const int tb = sh.t;
+  const int need = k - sh.above;  // 1 <= need <= hist[tb]
+  const int nc = (int)hist[tb];
+  const bool rank_path = nc <= kRankMax;
+  if (tid == 0) sh.ccount = 0;
+  __syncthreads();  // hist is reused below
+
+  // 2. above-masks (lane i keeps step i's) and bin tb's candidates
+  uint32_t* ck = lds;
+  uint32_t* ci = lds + kCap;
+  uint32_t klo = 0u, khi = 0u;
+  nv = opaque(nv);
+  const int tok0 = opaque(regs_tok0<T>());
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    const int j = tok0 + 64 * i;
+    const int bj = (i < nv) ? bin(key[i]) : -1;
+    const uint64_t mab = __ballot(bj > tb);
+    if (lane == i) { klo = (uint32_t)mab; khi = (uint32_t)(mab >> 32); }
+    if (rank_path && bj == tb) {
+      const int p = atomicAdd(&sh.ccount, 1);
+      ck[p] = key[i];
+      ci[p] = (uint32_t)j;
+    }
+  }
+  __syncthreads();
+
+  // 3. the need best tokens of bin tb
+  if (rank_path) {
+    rank_candidates<NTHR>(ck, ci, nc, need, [&](uint32_t ii) { atomicOr(&take[ii >> 5], 1u << (ii & 31)); });
+    __syncthreads();
+    const int st = wave * T + lane;
+    if (lane < T && 2 * st < W) { klo |= take[2 * st]; khi |= take[2 * st + 1]; }
+  } else {
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = need;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = shifts[pass];
+      const uint32_t dm = (1u << widths[pass]) - 1u;
+      for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
+      __syncthreads();
+      const int nvp = opaque(nv);
+#pragma unroll
+      for (int i = 0; i < T; ++i)
+        if (i < nvp && bin(key[i]) == tb && (key[i] & pmask) == prefix)
+          atomicAdd(&hist[(key[i] >> sft) & dm], 1u);
+      __syncthreads();
+      find_threshold<NTHR>(hist, rem, sh);
+      rem -= sh.above;
+      prefix |= (uint32_t)sh.t << sft;
+      pmask |= dm << sft;
+      __syncthreads();
+    }
+    const uint32_t kstar = prefix;  // a key of bin tb, so key == K* implies bin tb
+    const int quota = rem;          // ties at K* to take, lowest indices first
+    int neq = 0;
+    nv = opaque(nv);
+#pragma unroll
+    for (int i = 0; i < T; ++i) neq += __popcll(__ballot(i < nv && key[i] == kstar));
+    if (lane == 0) sh.weq[wave] = neq;
+    __syncthreads();
+    int eqrun = waves_below<NTHR>(sh.weq);
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const bool valid = i < nv;
+      const bool eq = valid && key[i] == kstar;
+      const uint64_t eqm = __ballot(eq);
+      const bool tk = (valid && key[i] > kstar && bin(key[i]) == tb) ||
+                      (eq && eqrun + bits_below(eqm) < quota);
+      const uint64_t tm = __ballot(tk);
+      if (lane == i) { klo |= (uint32_t)tm; khi |= (uint32_t)(tm >> 32); }
+      eqrun += __popcll(eqm);
+    }
+  }
+
+  // 4. emit: lane i < T holds the kept mask of step wave * T + i
+  const int cnt = (lane < T) ? __popc(klo) + __popc(khi) : 0;
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) sh.wsel[wave] = incl;
+  __syncthreads();  // also: every read of lds / take above is done
+  const int off = waves_below<NTHR>(sh.wsel) + incl - cnt;
+  auto emit = [&](int32_t* list) {
+    const int t0 = opaque(regs_tok0<T>());
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, i) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)klo, i);
+      const int o = __builtin_amdgcn_readlane(off, i);
+      if ((f >> lane) & 1ull) list[o + bits_below(f)] = t0 + 64 * i;
+    }
+  };
+  if (k <= kNB) emit(reinterpret_cast<int32_t*>(lds));
+  else emit(orow);
+  {
+    const int st = wave * T + lane;
+    if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow + 2 * st) = make_uint2(klo, khi);
+  }
+  if (k <= kNB) {
+    __syncthreads();
+    for (int i = tid; i < k; i += NTHR) orow[i] = reinterpret_cast<const int32_t*>(lds)[i];
+  }
+}
+
+// ============================================================================
+// Keys in global memory (heads longer than the register form holds).
+// ============================================================================
+
 // Calls f(j, key) for every token j < S (in no particular order): each thread
-// reads 4 consecutive keys per 16-byte load with UB loads in flight.
-template <int NTHR, bool IN_LDS, typename F>
-__device__ __forceinline__ void for_each_key(const uint32_t* rk, const uint32_t* lk, int S, int Sp,
-                                             F&& f) {
-  constexpr int UB = IN_LDS ? 4 : 8;
-  const uint4* src = reinterpret_cast<const uint4*>(IN_LDS ? lk : rk);
+// reads 4 consecutive keys per 16-byte load with 8 loads in flight.
+template <int NTHR, typename F>
+__device__ __forceinline__ void for_each_key(const uint32_t* rk, int S, int Sp, F&& f) {
+  constexpr int UB = 8;
+  const uint4* src = reinterpret_cast<const uint4*>(rk);
   const int n4 = Sp >> 2, tid = threadIdx.x;
   for (int base = 0; base < n4; base += NTHR * UB) {
     uint4 v[UB];
@@ -112,67 +351,75 @@ __device__ __forceinline__ void for_each_key(const uint32_t* rk, const uint32_t*
   }
 }
 
-// Writes idx (ascending) and the kept-token bitmap when every token is kept.
+// Steps 1-4 for one head with k < S, keys rk[0..S) in global memory and
+// mm[0..nmm) min / max pairs covering them.  hist: kNB words of LDS, zeroed
+// by the caller (a barrier inside orders it); masks: Sp / 16 words of global
+// scratch, per step {above lo, hi, taken lo, hi}.  All threads call it.
 template <int NTHR>
-__device__ __forceinline__ void keep_all(int S, int W, int32_t* orow, uint32_t* brow) {
-  for (int j = threadIdx.x; j < S; j += NTHR) orow[j] = j;
-  for (int w = threadIdx.x; w < W; w += NTHR) {
-    const int lo = 32 * w;
-    brow[w] = (lo + 32 <= S) ? 0xffffffffu : (lo >= S ? 0u : ((1u << (S - lo)) - 1u));
-  }
-}
-
-// Steps 1-4 for one head with k < S.  `hist` is kNB words of LDS (reused for
-// candidates); keys are lk[0..S) in LDS (IN_LDS) or rk[0..S) in global
-// memory; kmin / kmax are their extremes.  All threads of the block call it.
-template <int NTHR, bool IN_LDS>
-__device__ __forceinline__ void select_head(const uint32_t* rk, const uint32_t* lk, uint32_t* hist,
-                                            int S, int Sp, int k, uint32_t kmin, uint32_t kmax,
-                                            int32_t* orow, uint32_t* brow, SelScratch<NTHR>& sh) {
+__device__ __forceinline__ void select_head(const uint32_t* rk, const uint2* mm, int nmm, uint32_t* hist,
+                                            uint32_t* masks, int S, int Sp, int k, int32_t* orow,
+                                            uint32_t* brow, SelScratch<NTHR>& sh) {
   constexpr int NW = NTHR / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // 1. value histogram
-  for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
-  __syncthreads();
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int c = tid; c < nmm; c += NTHR) {
+    const uint2 v = mm[c];
+    mn = min(mn, v.x);
+    mx = max(mx, v.y);
+  }
+  block_minmax<NTHR>(mn, mx, sh);
   Binner bin;
-  bin.init(kmin, kmax);
-  for_each_key<NTHR, IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) { atomicAdd(&hist[bin(v)], 1u); });
+  bin.init(sh.kmin, sh.kmax);
+  for_each_key<NTHR>(rk, S, Sp, [&](int, uint32_t v) { atomicAdd(&hist[bin(v)], 1u); });
   __syncthreads();
 
-  // 2. threshold bin
+  // 1. threshold bin
   find_threshold<NTHR>(hist, k, sh);
   const int tb = sh.t;
   const int need = k - sh.above;  // 1 <= need <= hist[tb]
   const int nc = (int)hist[tb];
+  const bool rank_path = nc <= kRankMax;
+  if (tid == 0) sh.ccount = 0;
   __syncthreads();  // hist is reused below
 
-  // 3. exact k-th key inside bin tb.  Ranking costs nc^2 compares spread over
-  // the block; the radix passes cost three sweeps of the keys.
-  if (nc <= (IN_LDS ? kRankLds : kCap)) {
-    uint32_t* ck = hist;
-    uint32_t* ci = hist + kCap;
-    if (tid == 0) sh.ccount = 0;
-    __syncthreads();
-    for_each_key<NTHR, IN_LDS>(rk, lk, S, Sp, [&](int j, uint32_t v) {
-      if (bin(v) == tb) {
+  // 2. masks in index order; each wave owns a 64-aligned segment
+  constexpr int UE = 8;
+  const int SEG = (S + NW * 64 - 1) / (NW * 64) * 64;
+  const int wb = wave * SEG, we = min(S, wb + SEG);
+  uint32_t* ck = hist;
+  uint32_t* ci = hist + kCap;
+  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
+    uint32_t v[UE];
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int j = j0 + 64 * u + lane;
+      v[u] = (j < we) ? rk[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int js = j0 + 64 * u;
+      if (js >= we) break;  // uniform across the wave
+      const int j = js + lane;
+      const int bj = (j < we) ? bin(v[u]) : -1;
+      const uint64_t mab = __ballot(bj > tb);
+      if (lane == 0)
+        *reinterpret_cast<uint4*>(masks + 4 * (js >> 6)) =
+            make_uint4((uint32_t)mab, (uint32_t)(mab >> 32), 0u, 0u);
+      if (rank_path && bj == tb) {
         const int p = atomicAdd(&sh.ccount, 1);
-        ck[p] = v;
+        ck[p] = v[u];
         ci[p] = (uint32_t)j;
       }
-    });
-    __syncthreads();
-    for (int i = tid; i < nc; i += NTHR) {
-      const uint32_t vi = ck[i], ii = ci[i];
-      int gtc = 0, rank = 0;
-      for (int c = 0; c < nc; ++c) {
-        const uint32_t vc = ck[c], ic = ci[c];
-        gtc += (vc > vi);
-        rank += (vc > vi) || (vc == vi && ic < ii);
-      }
-      if (rank == need - 1) { sh.kstar = vi; sh.quota = need - gtc; }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+
+  // 3. the need best tokens of bin tb
+  if (rank_path) {
+    rank_candidates<NTHR>(ck, ci, nc, need, [&](uint32_t ii) {
+      atomicOr(&masks[4 * (ii >> 6) + 2 + ((ii >> 5) & 1)], 1u << (ii & 31));
+    });
   } else {
     uint32_t prefix = 0u, pmask = 0u;
     int rem = need;
@@ -183,7 +430,7 @@ __device__ __forceinline__ void select_head(const uint32_t* rk, const uint32_t* 
       const uint32_t dm = (1u << widths[pass]) - 1u;
       for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
       __syncthreads();
-      for_each_key<NTHR, IN_LDS>(rk, lk, S, Sp, [&](int, uint32_t v) {
+      for_each_key<NTHR>(rk, S, Sp, [&](int, uint32_t v) {
         if (bin(v) == tb && (v & pmask) == prefix) atomicAdd(&hist[(v >> sft) & dm], 1u);
       });
       __syncthreads();
@@ -193,75 +440,62 @@ __device__ __forceinline__ void select_head(const uint32_t* rk, const uint32_t* 
       pmask |= dm << sft;
       __syncthreads();
     }
-    if (tid == 0) { sh.kstar = prefix; sh.quota = rem; }
+    const uint32_t kstar = prefix;
+    const int quota = rem;
+    int neq = 0;
+    for (int j0 = wb; j0 < we; j0 += 64) {
+      const int j = j0 + lane;
+      neq += __popcll(__ballot(j < we && rk[j] == kstar));
+    }
+    if (lane == 0) sh.weq[wave] = neq;
     __syncthreads();
-  }
-  const uint32_t kstar = sh.kstar;
-  const int quota = sh.quota;
-
-  // 4. emit in index order; each wave owns a 64-aligned segment and reads
-  // UE 64-token steps ahead
-  constexpr int UE = 8;
-  const int SEG = (S + NW * 64 - 1) / (NW * 64) * 64;
-  const int wb = wave * SEG, we = min(S, wb + SEG);
-  auto KEY = [&](int j) -> uint32_t {
-    if constexpr (IN_LDS) return lk[j];
-    else return rk[j];
-  };
-  int ngt = 0, neq = 0;
-  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
-    uint32_t v[UE];
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int j = j0 + 64 * u + lane;
-      v[u] = (j < we) ? KEY(j) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const bool ok = j0 + 64 * u + lane < we;
-      ngt += __popcll(__ballot(ok && v[u] > kstar));
-      neq += __popcll(__ballot(ok && v[u] == kstar));
-    }
-  }
-  if (lane == 0) { sh.wgt[wave] = ngt; sh.weq[wave] = neq; }
-  __syncthreads();
-  if (tid == 0) {
-    int eqb = 0, selb = 0;
-    for (int w = 0; w < NW; ++w) {
-      sh.eqb[w] = eqb;
-      sh.selb[w] = selb;
-      const int take = min(max(quota - eqb, 0), sh.weq[w]);
-      selb += sh.wgt[w] + take;
-      eqb += sh.weq[w];
-    }
-  }
-  __syncthreads();
-  int selrun = sh.selb[wave], eqrun = sh.eqb[wave];
-  for (int j0 = wb; j0 < we; j0 += 64 * UE) {
-    uint32_t v[UE];
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int j = j0 + 64 * u + lane;
-      v[u] = (j < we) ? KEY(j) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int js = j0 + 64 * u;  // 64-aligned step start
-      if (js >= we) break;         // uniform across the wave
-      const int j = js + lane;
-      const bool ok = j < we;
-      const bool gt = ok && v[u] > kstar, eq = ok && v[u] == kstar;
+    int eqrun = waves_below<NTHR>(sh.weq);
+    for (int j0 = wb; j0 < we; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t v = (j < we) ? rk[j] : 0u;
+      const bool valid = j < we;
+      const bool eq = valid && v == kstar;
       const uint64_t eqm = __ballot(eq);
-      const bool take = gt || (eq && eqrun + bits_below(eqm) < quota);
-      const uint64_t sm = __ballot(take);
-      if (take) orow[selrun + bits_below(sm)] = j;
-      if (lane == 0) {
-        brow[js >> 5] = (uint32_t)sm;
-        brow[(js >> 5) + 1] = (uint32_t)(sm >> 32);
-      }
-      selrun += __popcll(sm);
+      const bool tk = (valid && v > kstar && bin(v) == tb) || (eq && eqrun + bits_below(eqm) < quota);
+      const uint64_t tm = __ballot(tk);
+      if (lane == 0)
+        *reinterpret_cast<uint2*>(masks + 4 * (j0 >> 6) + 2) = make_uint2((uint32_t)tm, (uint32_t)(tm >> 32));
       eqrun += __popcll(eqm);
     }
+  }
+  __syncthreads();
+
+  // 4. emit; lane i handles step s0 + 64 c + i of this wave's steps [s0, s1)
+  const int s0 = wb >> 6, s1 = (we + 63) >> 6;
+  int cnt = 0;
+  for (int s = s0 + lane; s < s1; s += 64) {
+    const uint4 m = *reinterpret_cast<const uint4*>(masks + 4 * s);
+    cnt += __popc(m.x | m.z) + __popc(m.y | m.w);
+  }
+  cnt = wave_incl_scan(cnt);
+  if (lane == 63) sh.wsel[wave] = cnt;
+  __syncthreads();
+  int pos = waves_below<NTHR>(sh.wsel);
+  for (int c = s0; c < s1; c += 64) {
+    const int s = c + lane;
+    uint32_t lo = 0u, hi = 0u;
+    if (s < s1) {
+      const uint4 m = *reinterpret_cast<const uint4*>(masks + 4 * s);
+      lo = m.x | m.z;
+      hi = m.y | m.w;
+      *reinterpret_cast<uint2*>(brow + 2 * s) = make_uint2(lo, hi);
+    }
+    const int n = __popc(lo) + __popc(hi);
+    const int incl = wave_incl_scan(n);
+    const int o = pos + incl - n;
+    const int ns = min(64, s1 - c);
+    for (int i = 0; i < ns; ++i) {
+      const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, i) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, i);
+      const int oi = __builtin_amdgcn_readlane(o, i);
+      if ((f >> lane) & 1ull) orow[oi + bits_below(f)] = 64 * (c + i) + lane;
+    }
+    pos += __builtin_amdgcn_readlane(incl, 63);
   }
 }
 
