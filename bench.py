@@ -121,7 +121,7 @@ def load_traffic(workload: str, kernel_name: str):
     if t.get("source_hash") != kernel_source_hash():
         return None
     for key, v in t.get("kernels", {}).items():
-        if key.split("|")[0].endswith(kernel_name) and v.get("fetch_bytes") is not None:
+        if key.split("|")[0].split("<")[0].endswith(kernel_name) and v.get("fetch_bytes") is not None:
             return v["fetch_bytes"] + (v.get("write_bytes") or 0.0)
     return None
 
