@@ -291,6 +291,89 @@ def run(args) -> dict:
     return res
 
 
+def run_project(args) -> dict:
+    """The key projection K_rot = K P (and the leading-dims copy K_lead) on the
+    prefill-plus-decode workload's cache: HBM GB/s, MFMA TFLOP/s."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(cfg, need_K=True)
+    P = x["P"].to(dev)
+    R = cfg.r if args.layout == "lead" else 0
+    bufs = []
+    for i in range(max(2, args.buffers)):
+        K = x["K"].to(dev)
+        Kr = torch.empty_like(K)
+        Kl = torch.empty(K.shape[:-1] + (R,), dtype=K.dtype, device=dev) if R else None
+        bufs.append((K, Kr, Kl))
+
+    def step(i):
+        K, Kr, Kl = bufs[i % len(bufs)]
+        rks.loki_project_keys(K, P, K_rot=Kr, R=R if R else None, K_lead=Kl)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    # the same calls between events on the current stream: the kernel's average duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    e = cfg.elem_bytes
+    rows = cfg.B * cfg.Hkv * cfg.S
+    by = 2 * rows * cfg.d * e + cfg.Hkv * cfg.d * cfg.d * e + rows * R * e
+    flop = 2.0 * rows * cfg.d * cfg.d
+    gbs = by / (us * 1e-6) / 1e9
+    tflops = flop / (us * 1e-6) / 1e12
+    # oracle on one (b, kv) slice, single-threaded, scaled to the whole cache
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t < min(args.cpu_seconds, 5.0):
+            oracle.project(x["K"][n % cfg.B:n % cfg.B + 1, :1], x["P"][:1])
+            n += 1
+        per_slice = (time.perf_counter() - t) / n
+    got = bufs[0][1][:1, :1].double().cpu().numpy()
+    want = oracle.project(x["K"][:1, :1], x["P"][:1])
+    ok = bool(np.max(np.abs(got - want)) <= 2e-2)
+    return {
+        "metric": "key projection K_rot = K P (+ leading-dims copy): achieved HBM GB/s",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} cache projection", "batch": cfg.B, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.d, "cached_tokens": cfg.S, "lead_dims": R, "buffers": len(bufs)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "project_bf16_kernel",
+                     "alg_bytes_per_launch": by, "avg_launch_us": round(us, 2)},
+        "mfma": {"tflops": round(tflops, 2), "peak_tflops": 2500.0, "util": round(tflops / 2500.0, 4),
+                 "flop_per_launch": flop},
+        "cpu_baseline": {"value": round(1.0 / (per_slice * cfg.B * cfg.Hkv), 4), "unit": "projections/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": f"{n} (b, kv) slices of {cfg.S}x{cfg.d} in float64, scaled to the cache",
+                         "gpu_matches_oracle_on_slice": ok},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +385,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--op", default="decode", choices=["decode", "project"],
+                    help="project: time the key projection instead (use --workload C5)")
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
@@ -323,7 +408,7 @@ def main() -> int:
         for _ in range(3):
             torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-    res = run(args)
+    res = run_project(args) if args.op == "project" else run(args)
     print(json.dumps(res))
     return 0
 
