@@ -168,7 +168,8 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     LOKI_HIP(launch_scores(p, src, ld, qrot, qsplit, keys, true, p.Sp, mm, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
     LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, mm, p.NSC, at<uint32_t>(workspace, p.off_masks),
-                           idx, bitmap, stream));
+                           idx, bitmap, stream, at<int32_t>(workspace, p.off_cidx),
+                           at<uint32_t>(workspace, p.off_ckey)));
   }
   if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
   LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
@@ -263,7 +264,8 @@ loki_status loki_select_topk(const float* scores, int32_t* idx, int32_t rows, in
     uint2* mm = at<uint2>(workspace, p.off_mm);
     LOKI_HIP(launch_scores_to_keys(scores, keys, mm, p.NMM, rows, S, p.Sp, stream));
     LOKI_HIP(launch_select(rows, S, p.Sp, k, p.W, keys, mm, p.NMM, at<uint32_t>(workspace, p.off_masks),
-                           idx, bitmap, stream));
+                           idx, bitmap, stream, at<int32_t>(workspace, p.off_cidx),
+                           at<uint32_t>(workspace, p.off_ckey)));
     return LOKI_OK;
   } catch (...) {
     return LOKI_ERR_INTERNAL;

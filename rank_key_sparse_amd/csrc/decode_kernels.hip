@@ -251,6 +251,50 @@ __global__ __launch_bounds__(kSelThreads, T <= 16 ? 8 : 4) void select_regs_kern
   select_regs<kSelThreads, T>(key, lds, take, S, k, W, orow, brow, sh);
 }
 
+// Long heads, two stages (exact: every token of the head's top-k is in the
+// top-k of its own chunk).  Stage 1: one block per (chunk of kSelChunk
+// tokens, head) keeps the chunk's top-k; its positions (made absolute) and
+// keys go to the candidate lists, chunk c at offset c k, ascending.  Stage 2:
+// one block per head selects the top-k of its candidate list (position order
+// is token order, so ties still go to the lower token) and maps positions
+// back to tokens; the bitmap is rebuilt from idx afterwards.
+__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_t* __restrict__ keys, int S,
+                                                                   int Sp, int k, int ldc,
+                                                                   int32_t* __restrict__ cidx,
+                                                                   uint32_t* __restrict__ ckey) {
+  constexpr int T = kSelChunk / kSelThreads;
+  __shared__ uint32_t lds[kNB];
+  __shared__ uint32_t take[kSelChunk / 32];
+  __shared__ SelScratch<kSelThreads> sh;
+  const int row = blockIdx.y, c = blockIdx.x, base = c * kSelChunk;
+  const int L = min(kSelChunk, S - base);
+  const uint32_t* rk = keys + (size_t)row * Sp + base;
+  int32_t* oi = cidx + (size_t)row * ldc + (size_t)c * k;
+  uint32_t* ok = ckey + (size_t)row * ldc + (size_t)c * k;
+  if (L <= k) {  // the whole chunk is a candidate
+    for (int j = threadIdx.x; j < L; j += kSelThreads) { oi[j] = base + j; ok[j] = rk[j]; }
+    return;
+  }
+  uint32_t key[T];
+  load_regs<T>(rk, L, key);
+  select_regs<kSelThreads, T>(key, lds, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base);
+}
+
+template <int T>
+__global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_t* __restrict__ ckey,
+                                                                   const int32_t* __restrict__ cidx,
+                                                                   int S2, int ldc, int k,
+                                                                   int32_t* __restrict__ idx) {
+  __shared__ uint32_t lds[kNB];
+  __shared__ uint32_t take[kSelThreads * T / 32];
+  __shared__ SelScratch<kSelThreads> sh;
+  const int row = blockIdx.x;
+  uint32_t key[T];
+  load_regs<T>(ckey + (size_t)row * ldc, S2, key);
+  select_regs<kSelThreads, T>(key, lds, take, S2, k, 2 * ((S2 + 63) / 64), idx + (size_t)row * k, nullptr, sh,
+                              cidx + (size_t)row * ldc);
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_global_kernel(const uint32_t* __restrict__ keys,
                                                                     const uint2* __restrict__ mm,
                                                                     int nmm, uint32_t* __restrict__ gmasks,
@@ -577,6 +621,9 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
   p.off_keys = off;   off = align_up(off + rows * (size_t)p.Sp * sizeof(uint32_t), 256);
   p.off_mm = off;     off = align_up(off + rows * (size_t)p.NSC * sizeof(uint2), 256);
   p.off_masks = off;  off = align_up(off + rows * (size_t)(p.Sp / 16) * sizeof(uint32_t), 256);
+  const size_t ldc = select_chunked_ldc(S, k);
+  p.off_cidx = off;   off = align_up(off + rows * ldc * sizeof(int32_t), 256);
+  p.off_ckey = off;   off = align_up(off + rows * ldc * sizeof(uint32_t), 256);
   p.off_bitmap = off; off = align_up(off + rows * (size_t)p.W * sizeof(uint32_t), 256);
   p.off_part = off;   off = align_up(off + rows * (size_t)p.NAC * (d + 2) * sizeof(float), 256);
   p.bytes = off;
@@ -593,6 +640,9 @@ bool make_select_plan(SelectPlan& p, int rows, int S, int k) {
   p.off_keys = off;   off = align_up(off + (size_t)rows * p.Sp * sizeof(uint32_t), 256);
   p.off_mm = off;     off = align_up(off + (size_t)rows * p.NMM * sizeof(uint2), 256);
   p.off_masks = off;  off = align_up(off + (size_t)rows * (p.Sp / 16) * sizeof(uint32_t), 256);
+  const size_t ldc = select_chunked_ldc(S, k);
+  p.off_cidx = off;   off = align_up(off + (size_t)rows * ldc * sizeof(int32_t), 256);
+  p.off_ckey = off;   off = align_up(off + (size_t)rows * ldc * sizeof(uint32_t), 256);
   p.off_bitmap = off; off = align_up(off + (size_t)rows * p.W * sizeof(uint32_t), 256);
   p.bytes = off;
   return true;
@@ -671,8 +721,35 @@ hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const flo
 
 bool select_needs_minmax(int S) { return S > kSelThreads * kSelRegMaxT; }
 
+size_t select_chunked_ldc(int S, int k) {
+  if (S <= kSelThreads * kSelRegMaxT || k > kSelChunk) return 0;
+  const int C = (S + kSelChunk - 1) / kSelChunk;
+  const int last = S - (C - 1) * kSelChunk;
+  const long long S2 = (long long)(C - 1) * k + (last < k ? last : k);
+  if (S2 > (long long)kSelThreads * kSelRegMaxT) return 0;
+  return (size_t)C * k;
+}
+
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
-                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st) {
+                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
+                         int32_t* cidx, uint32_t* ckey) {
+  const size_t ldc = select_chunked_ldc(S, k);
+  if (ldc && k < S) {
+    if (!cidx || !ckey) return hipErrorInvalidValue;
+    const int C = (S + kSelChunk - 1) / kSelChunk;
+    const int last = S - (C - 1) * kSelChunk;
+    const int S2 = (C - 1) * k + (last < k ? last : k);
+    hipLaunchKernelGGL(select_chunk_kernel, dim3(C, rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, (int)ldc,
+                       cidx, ckey);
+    if (S2 <= kSelThreads * 16)
+      hipLaunchKernelGGL((select_merge_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, S2,
+                         (int)ldc, k, idx);
+    else
+      hipLaunchKernelGGL((select_merge_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx,
+                         S2, (int)ldc, k, idx);
+    hipLaunchKernelGGL(idx_to_bitmap_kernel, dim3(rows), dim3(256), 0, st, idx, bitmap, S, k, W);
+    return hipGetLastError();
+  }
   if (S <= kSelThreads * 16) {
     hipLaunchKernelGGL((select_regs_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
                        idx, bitmap);

@@ -13,6 +13,7 @@ constexpr int kAttendMfmaTokens = 256;  // tokens per wave in the MFMA attention
 constexpr int kFusedThreads = 512;      // threads of the fused score+select kernel
 constexpr int kFusedMaxS = 16384;       // fused path: a head's keys fit in LDS and in 512 x 32 registers
 constexpr int kSelRegMaxT = 32;         // selection keeps up to 1024 x 32 keys of a head in registers
+constexpr int kSelChunk = 16384;        // long heads: tokens per first-stage selection block
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -26,7 +27,7 @@ struct DecodePlan {
   // workspace: q_rot, its bf16 split, keys [row][Sp], per-score-chunk key
   // extremes [row][NSC] (uint2 min, max), selection masks [row][Sp/16] (used
   // when a row's keys do not fit in LDS), bitmap [row][W], attention partials
-  size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_bitmap, off_part, bytes;
+  size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_cidx, off_ckey, off_bitmap, off_part, bytes;
 };
 
 // Fills `p` from the sizes; returns false if they are out of the supported range
@@ -37,7 +38,7 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
 struct SelectPlan {
   int rows, S, Sp, W, k;
   int NMM;  // key-conversion blocks per row (one min / max pair each)
-  size_t off_keys, off_mm, off_masks, off_bitmap, bytes;
+  size_t off_keys, off_mm, off_masks, off_cidx, off_ckey, off_bitmap, bytes;
 };
 bool make_select_plan(SelectPlan& p, int rows, int S, int k);
 
@@ -55,9 +56,15 @@ hipError_t launch_scores(const DecodePlan& p, const void* src, int ld, const flo
 // Top-k of each key row.  Rows longer than the register form
 // (select_needs_minmax) also need mm[row][0..nmm), min / max pairs covering
 // the row, and gmasks (rows * Sp / 16 words of scratch); else both may be null.
+// Heads longer than the register form with k <= kSelChunk and a short enough
+// candidate list are selected in two stages (per chunk, then over the chunk
+// winners) and need candidate lists cidx / ckey of rows * select_chunked_ldc
+// entries (0: not this path).
 bool select_needs_minmax(int S);
+size_t select_chunked_ldc(int S, int k);
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
-                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st);
+                         int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
+                         int32_t* cidx = nullptr, uint32_t* ckey = nullptr);
 hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, uint2* mm, int nmm, int rows,
                                  int S, int Sp, hipStream_t st);
 hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,

@@ -169,6 +169,9 @@ __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32
 // Keys in registers.  Requires S <= NTHR * T and k < S.  lds: kNB words
 // (bins, candidates, then the index list when k <= kNB); take: W words of
 // LDS, W = 2 ceil(S / 64).  All threads of the block call it.
+// Output: orow[0..k) = the kept positions p, ascending, written as map[p]
+// when map is given, else as p + tok_base; with okeys, okeys[i] receives the
+// key of orow[i]; with brow, the kept-position bitmap (W words).
 // ============================================================================
 
 // Token of key[0] of this lane (key[i] is token tok0 + 64 i), and the number
@@ -195,7 +198,8 @@ __device__ __forceinline__ void load_regs(const uint32_t* src, int S, uint32_t (
 template <int NTHR, int T>
 __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* lds, uint32_t* take,
                                             int S, int k, int W, int32_t* orow, uint32_t* brow,
-                                            SelScratch<NTHR>& sh) {
+                                            SelScratch<NTHR>& sh, const int32_t* map = nullptr,
+                                            uint32_t* okeys = nullptr, int tok_base = 0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* hist = lds;
 
@@ -300,25 +304,33 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   if (lane == 63) sh.wsel[wave] = incl;
   __syncthreads();  // also: every read of lds / take above is done
   const int off = waves_below<NTHR>(sh.wsel) + incl - cnt;
-  auto emit = [&](int32_t* list) {
+  const bool via_lds = k <= kNB && !okeys;  // uniform
+  auto emit = [&](int32_t* list, bool final_values) {
     const int t0 = opaque(regs_tok0<T>());
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, i) << 32) |
                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)klo, i);
       const int o = __builtin_amdgcn_readlane(off, i);
-      if ((f >> lane) & 1ull) list[o + bits_below(f)] = t0 + 64 * i;
+      if ((f >> lane) & 1ull) {
+        const int pos = o + bits_below(f), t = t0 + 64 * i;
+        list[pos] = final_values ? (map ? map[t] : t + tok_base) : t;
+        if (okeys) okeys[pos] = key[i];
+      }
     }
   };
-  if (k <= kNB) emit(reinterpret_cast<int32_t*>(lds));
-  else emit(orow);
-  {
+  if (via_lds) emit(reinterpret_cast<int32_t*>(lds), false);
+  else emit(orow, true);
+  if (brow) {
     const int st = wave * T + lane;
     if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow + 2 * st) = make_uint2(klo, khi);
   }
-  if (k <= kNB) {
+  if (via_lds) {
     __syncthreads();
-    for (int i = tid; i < k; i += NTHR) orow[i] = reinterpret_cast<const int32_t*>(lds)[i];
+    for (int i = tid; i < k; i += NTHR) {
+      const int t = reinterpret_cast<const int32_t*>(lds)[i];
+      orow[i] = map ? map[t] : t + tok_base;
+    }
   }
 }
 

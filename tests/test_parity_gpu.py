@@ -131,6 +131,13 @@ def _score_rows():
     c[:, 1000:30000] = -0.25
     rows["big_crowded"] = c
     rows["S1"] = np.array([[3.0], [-1.0]], dtype=np.float32)
+    # long rows selected per 16384-token chunk, then over the chunk winners:
+    # a block of equal top values straddles a chunk boundary, and integer
+    # ties spread over every chunk
+    t = g.standard_normal((2, 50000)).astype(np.float32)
+    t[:, 12000:22000] = 3.0
+    rows["chunk_ties"] = t
+    rows["chunk_int_ties"] = g.integers(-3, 4, size=(2, 50000)).astype(np.float32)
     return rows
 
 
@@ -263,7 +270,8 @@ EDGE = [
     ("G16", 1, 16, 1, 1500, 128, "bf16", 32, 64),
     ("G8_f32_d128", 1, 16, 2, 1111, 128, "f32", 24, 128),
     ("d64_bf16_r64", 3, 8, 8, 640, 64, "bf16", 64, 64),
-    ("global_select", 1, 4, 2, 40000, 128, "bf16", 32, 1500),
+    ("chunked_select", 1, 4, 2, 40000, 128, "bf16", 32, 1500),
+    ("global_select", 1, 2, 1, 40000, 64, "bf16", 16, 20000),
     # fused score+select path (MHA, >= 256 heads, S <= 16384)
     ("fused_ragged_r24", 16, 16, 16, 1000, 128, "bf16", 24, 77),
     ("fused_d64_r40", 32, 8, 8, 3001, 64, "bf16", 40, 300),
