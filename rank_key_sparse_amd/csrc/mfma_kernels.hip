@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 //           before any is used;
 //           exact scores of all G heads from MFMA, scaled to log2 units,
 //           -inf where a head did not keep the token, into LDS;
-//   per head: m = max, w = 2^(e - m), l = sum w;
+//   per head: m = max (kept by the score lanes during pass 1), then one
+//           pass over the (token, head) entries: w = 2^(e - m), l = sum w;
 //   pass 2: V rows (16-byte granules, RL lanes per row), up to UV row
 //           passes in flight; acc += w V on the vector ALUs.
 // Each pass holds only its own buffers, which keeps the register file small
@@ -293,6 +294,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   __shared__ uint16_t s_hm[4][NT];
   __shared__ __align__(16) float s_e[4][NT * GT];
   __shared__ float s_m[4][GT], s_l[4][GT];
+  __shared__ float s_mx[4][GT];
   __shared__ __align__(16) float s_acc[4][GT][D];
 
   const int G = Hq / Hkv;
@@ -341,6 +343,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   // pass 1: exact scores.  k-step s covers dims [32 s, 32 s + 32), lane
   // quarter q the 8 dims from 32 s + 8 q, so one load instruction reads 64
   // contiguous bytes of each of the tile's 16 rows.
+  float mloc[NGRP];
+#pragma unroll
+  for (int grp = 0; grp < NGRP; ++grp) mloc[grp] = -INFINITY;
   {
     bf16x8_t bv[NGRP][KS];
 #pragma unroll
@@ -370,8 +375,11 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
           for (int v = 0; v < 4; ++v) {
             const float x = add_split_columns(sacc[v]);
             const int p = p0 + 16 * tl + 4 * q + v, g = 4 * grp + m;
-            if (m < 4 && g < GT && p < n)
-              e[p * GT + g] = (g < G && ((hmk[p] >> g) & 1)) ? x * scale_log2 : -INFINITY;
+            if (m < 4 && g < GT && p < n) {
+              const float sc = (g < G && ((hmk[p] >> g) & 1)) ? x * scale_log2 : -INFINITY;
+              e[p * GT + g] = sc;
+              mloc[grp] = fmaxf(mloc[grp], sc);
+            }
           }
         }
       }
@@ -381,24 +389,38 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // per-head softmax statistics of the span
-  float mreg[GT], lreg[GT];
+  // per-head softmax statistics of the span: the max from the score lanes
+  // (lane 16 q + m holds head 4 grp + m), then one pass over the (token,
+  // head) entries in which lane % GT is the head: weights in place, sums
 #pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    float mx = -INFINITY, sum = 0.f;
-    if (g < G) {
-      for (int p = lane; p < n; p += 64) mx = fmaxf(mx, e[p * GT + g]);
-      mx = wave_max(mx);
-      for (int p = lane; p < n; p += 64) {
-        const float v = e[p * GT + g];
-        const float w = (v == -INFINITY) ? 0.f : exp2f(v - mx);
-        e[p * GT + g] = w;
-        sum += w;
-      }
-      sum = wave_sum(sum);
+  for (int grp = 0; grp < NGRP; ++grp) {
+    float v = mloc[grp];
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    const int g = 4 * grp + m;
+    if (q == 0 && m < 4 && g < GT) s_mx[wave][g] = v;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float mreg[GT], lreg[GT];
+  {
+    const int gl = lane % GT;
+    const float mg = s_mx[wave][gl];
+    float lp = 0.f;
+    for (int i = lane; i < n * GT; i += 64) {
+      const float v = e[i];
+      const float w = (v == -INFINITY) ? 0.f : exp2f(v - mg);
+      e[i] = w;
+      lp += w;
     }
-    mreg[g] = mx;
-    lreg[g] = sum;
+#pragma unroll
+    for (int o = GT; o < 64; o <<= 1) lp += __shfl_xor(lp, o);
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      mreg[g] = s_mx[wave][g];
+      lreg[g] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), g));
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -438,7 +460,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       float v = acc[g][i];
-      for (int o = RL; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      // lane ^ 8 and lane ^ 16 by ds_swizzle (bit-mask mode, no address), lane ^ 32 by bpermute
+      if constexpr (RL <= 8) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+      v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+      v += __shfl_xor(v, 32);
       acc[g][i] = v;
     }
 
