@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 // (m, l, acc) by log-sum-exp and writes one partial per (head, block).
 // ============================================================================
 template <int D, int GT>
-__global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restrict__ K_rot,
+__global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const bf16_t* __restrict__ K_rot,
                                                           const bf16_t* __restrict__ V,
                                                           const uint16_t* __restrict__ qsplit,
                                                           const uint32_t* __restrict__ bitmap,
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   constexpr int RL = D / 8;          // lanes per V row
   constexpr int RPW = 64 / RL;       // V rows per wave pass
   constexpr int KT = 16 / KS;        // K tiles in flight (16 loads per lane)
-  constexpr int UV = 16;             // V row passes in flight
+  constexpr int UV = 8;              // V row passes in flight
   constexpr int NT = kAttendMfmaTokens;
   constexpr int NSTEP = NT / 64;
   constexpr int NW = NT / 32;        // bitmap words per head
@@ -389,6 +389,21 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // the first batch of V rows is requested now (the K tiles' registers are
+  // free), so that the weights pass below runs while the rows travel
+  const int lg = lane / RL, li = lane % RL;
+  auto load_v = [&](int p0, uint4 (&vb)[UV]) {
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int p = p0 + RPW * u + lg;
+      vb[u] = (p < n) ? ldg16(V + cb + (size_t)tok[p] * D + li * EPL) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 vb[UV];
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(0, vb);
+  __builtin_amdgcn_sched_barrier(0);
+
   // per-head softmax statistics of the span: the max from the score lanes
   // (lane 16 q + m holds head 4 grp + m), then one pass over the (token,
   // head) entries in which lane % GT is the head: weights in place, sums
@@ -427,19 +442,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const bf16_t* __restri
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // pass 2: weighted value sum
-  const int lg = lane / RL, li = lane % RL;
   float acc[GT][EPL];
 #pragma unroll
   for (int g = 0; g < GT; ++g)
 #pragma unroll
     for (int i = 0; i < EPL; ++i) acc[g][i] = 0.f;
   for (int p0 = 0; p0 < n; p0 += RPW * UV) {
-    uint4 vb[UV];
-#pragma unroll
-    for (int u = 0; u < UV; ++u) {
-      const int p = p0 + RPW * u + lg;
-      vb[u] = (p < n) ? ldg16(V + cb + (size_t)tok[p] * D + li * EPL) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    if (p0 > 0) load_v(p0, vb);
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
       if (p0 + RPW * u >= n) break;  // uniform across the wave
