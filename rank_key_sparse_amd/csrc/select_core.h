@@ -39,8 +39,7 @@ struct SelScratch {
   uint32_t red[2][NW];
   int scan[NW];
   int wsel[NW], weq[NW];
-  uint32_t kmin, kmax;
-  int t, above, ccount;
+  int t, above, nt, ccount;
 };
 
 template <int CTRL, int ROWMASK>
@@ -80,7 +79,8 @@ __device__ __forceinline__ int block_incl_scan(int v, SelScratch<NTHR>& sh) {
 }
 
 // Find, scanning bins from the top, the bin holding the `want`-th largest key
-// (1-based).  Sets sh.t to that bin and sh.above to the count in higher bins.
+// (1-based).  Sets sh.t to that bin, sh.above to the count in higher bins and
+// sh.nt to the count in bin t (so that callers need not read hist again).
 // Thread i owns bins kNB-1-BPT*i down to kNB-BPT*(i+1).
 template <int NTHR>
 __device__ __forceinline__ void find_threshold(const uint32_t* hist, int want, SelScratch<NTHR>& sh) {
@@ -92,7 +92,7 @@ __device__ __forceinline__ void find_threshold(const uint32_t* hist, int want, S
   int above = block_incl_scan<NTHR>(mine, sh) - mine;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
-    if (above < want && above + h[i] >= want) { sh.t = top - i; sh.above = above; }
+    if (above < want && above + h[i] >= want) { sh.t = top - i; sh.above = above; sh.nt = h[i]; }
     above += h[i];
   }
   __syncthreads();
@@ -114,21 +114,21 @@ struct Binner {
   }
 };
 
-// Block-wide min / max of per-thread partial extremes into sh.kmin / sh.kmax.
+// Block-wide min / max of per-thread partial extremes (one barrier: every
+// thread then reduces the per-wave values itself).
 template <int NTHR>
-__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelScratch<NTHR>& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelScratch<NTHR>& sh, uint32_t& kmin,
+                                             uint32_t& kmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   mn = wave_min_u(mn);
   mx = wave_max_u(mx);
   if (lane == 0) { sh.red[0][wave] = mn; sh.red[1][wave] = mx; }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t a = sh.red[0][0], b = sh.red[1][0];
-    for (int w = 1; w < SelScratch<NTHR>::NW; ++w) { a = min(a, sh.red[0][w]); b = max(b, sh.red[1][w]); }
-    sh.kmin = a;
-    sh.kmax = b;
-  }
-  __syncthreads();
+  uint32_t a = sh.red[0][0], b = sh.red[1][0];
+#pragma unroll
+  for (int w = 1; w < SelScratch<NTHR>::NW; ++w) { a = min(a, sh.red[0][w]); b = max(b, sh.red[1][w]); }
+  kmin = a;
+  kmax = b;
 }
 
 // Writes idx (ascending) and the kept-token bitmap when every token is kept.
@@ -167,8 +167,8 @@ __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32
 
 // ============================================================================
 // Keys in registers.  Requires S <= NTHR * T and k < S.  lds: kNB words
-// (bins, candidates, then the index list when k <= kNB); take: W words of
-// LDS, W = 2 ceil(S / 64).  All threads of the block call it.
+// (bins, then candidates); take: W words of LDS, W = 2 ceil(S / 64).  All
+// threads of the block call it.
 // Output: orow[0..k) = the kept positions p, ascending, written as map[p]
 // when map is given, else as p + tok_base; with okeys, okeys[i] receives the
 // key of orow[i]; with brow, the kept-position bitmap (W words).
@@ -205,14 +205,16 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 
   for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
   for (int i = tid; i < W; i += NTHR) take[i] = 0u;
+  if (tid == 0) sh.ccount = 0;
   uint32_t mn = 0xffffffffu, mx = 0u;
   int nv = opaque(regs_valid<T>(S));
 #pragma unroll
   for (int i = 0; i < T; ++i)
     if (i < nv) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
-  block_minmax<NTHR>(mn, mx, sh);  // its barriers also order the zeroing
+  uint32_t kmin, kmax;
+  block_minmax<NTHR>(mn, mx, sh, kmin, kmax);  // its barrier also orders the zeroing
   Binner bin;
-  bin.init(sh.kmin, sh.kmax);
+  bin.init(kmin, kmax);
 
   // 1. histogram and threshold bin
   nv = opaque(nv);
@@ -220,13 +222,11 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   for (int i = 0; i < T; ++i)
     if (i < nv) atomicAdd(&hist[bin(key[i])], 1u);
   __syncthreads();
-  find_threshold<NTHR>(hist, k, sh);
+  find_threshold<NTHR>(hist, k, sh);  // its trailing barrier ends every read of hist
   const int tb = sh.t;
-  const int need = k - sh.above;  // 1 <= need <= hist[tb]
-  const int nc = (int)hist[tb];
+  const int need = k - sh.above;  // 1 <= need <= nc
+  const int nc = sh.nt;
   const bool rank_path = nc <= kRankMax;
-  if (tid == 0) sh.ccount = 0;
-  __syncthreads();  // hist is reused below
 
   // 2. above-masks (lane i keeps step i's) and bin tb's candidates
   uint32_t* ck = lds;
@@ -304,8 +304,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   if (lane == 63) sh.wsel[wave] = incl;
   __syncthreads();  // also: every read of lds / take above is done
   const int off = waves_below<NTHR>(sh.wsel) + incl - cnt;
-  const bool via_lds = k <= kNB && !okeys;  // uniform
-  auto emit = [&](int32_t* list, bool final_values) {
+  {
     const int t0 = opaque(regs_tok0<T>());
 #pragma unroll
     for (int i = 0; i < T; ++i) {
@@ -314,23 +313,14 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
       const int o = __builtin_amdgcn_readlane(off, i);
       if ((f >> lane) & 1ull) {
         const int pos = o + bits_below(f), t = t0 + 64 * i;
-        list[pos] = final_values ? (map ? map[t] : t + tok_base) : t;
+        orow[pos] = map ? map[t] : t + tok_base;
         if (okeys) okeys[pos] = key[i];
       }
     }
-  };
-  if (via_lds) emit(reinterpret_cast<int32_t*>(lds), false);
-  else emit(orow, true);
+  }
   if (brow) {
     const int st = wave * T + lane;
     if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow + 2 * st) = make_uint2(klo, khi);
-  }
-  if (via_lds) {
-    __syncthreads();
-    for (int i = tid; i < k; i += NTHR) {
-      const int t = reinterpret_cast<const int32_t*>(lds)[i];
-      orow[i] = map ? map[t] : t + tok_base;
-    }
   }
 }
 
@@ -380,9 +370,10 @@ __device__ __forceinline__ void select_head(const uint32_t* rk, const uint2* mm,
     mn = min(mn, v.x);
     mx = max(mx, v.y);
   }
-  block_minmax<NTHR>(mn, mx, sh);
+  uint32_t kmin, kmax;
+  block_minmax<NTHR>(mn, mx, sh, kmin, kmax);  // its barrier also orders the caller's zeroing
   Binner bin;
-  bin.init(sh.kmin, sh.kmax);
+  bin.init(kmin, kmax);
   for_each_key<NTHR>(rk, S, Sp, [&](int, uint32_t v) { atomicAdd(&hist[bin(v)], 1u); });
   __syncthreads();
 
