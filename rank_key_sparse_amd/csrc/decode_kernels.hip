@@ -19,25 +19,6 @@
 
 namespace loki {
 
-// Global -> LDS copy of n16 16-byte words by nthr threads with 8 loads per
-// thread in flight before the first LDS store (a plain loop would wait for
-// each load in turn).
-__device__ __forceinline__ void copy16_to_lds(uint4* __restrict__ dst, const uint4* __restrict__ src,
-                                              int n16, int tid, int nthr) {
-  for (int base = 0; base < n16; base += nthr * 8) {
-    uint4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * nthr + tid;
-      v[u] = (i < n16) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + u * nthr + tid;
-      if (i < n16) dst[i] = v[u];
-    }
-  }
-}
 
 // ============================================================================
 // q rotation: q_rot[b, kv*G+g, c] = sum_j q[b, kv*G+g, j] * P[kv, j, c]
@@ -49,57 +30,64 @@ __device__ __forceinline__ void copy16_to_lds(uint4* __restrict__ dst, const uin
 constexpr int kQrotSlices = 8;
 
 template <typename T, int GT>
-__global__ __launch_bounds__(1024) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
-                                                    float* __restrict__ qrot,
-                                                    bf16_t* __restrict__ qsplit, int Hq, int Hkv,
-                                                    int d) {
-  extern __shared__ __align__(16) unsigned char qrot_lds[];
-  T* sP = reinterpret_cast<T*>(qrot_lds);                                     // [d][d]
-  float* qs = reinterpret_cast<float*>(qrot_lds + (size_t)d * d * sizeof(T));  // [GT][d]
-  float* red = qs + GT * d;                                                   // [slices][GT][d]
+__global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
+                                                   float* __restrict__ qrot,
+                                                   bf16_t* __restrict__ qsplit, int Hq, int Hkv,
+                                                   int d) {
+  // Block = (b, kv) group x 32 columns of P, staged in LDS with 16-byte
+  // loads; thread = (column, j-slice).  Each column is kQrotSlices FMA chains
+  // over consecutive j-ranges, added in range order.
+  constexpr int CB = 32;
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = CB / EPC;             // chunks per staged row
+  __shared__ __align__(16) T sP[128 * CB];
+  __shared__ float qs[GT * 128];
+  __shared__ float red[kQrotSlices][GT][CB];
   const int G = Hq / Hkv;
   const int bk = blockIdx.x, b = bk / Hkv, kv = bk % Hkv;
+  const int c0 = blockIdx.y * CB;
   const size_t qbase = ((size_t)b * Hq + (size_t)kv * G) * d;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  copy16_to_lds(reinterpret_cast<uint4*>(sP), reinterpret_cast<const uint4*>(P + (size_t)kv * d * d),
-                d * d * (int)sizeof(T) / 16, tid, nthr);
-  for (int i = tid; i < GT * d; i += nthr) qs[i] = (i < G * d) ? to_f32(q[qbase + i]) : 0.f;
+  const int tid = threadIdx.x;
+  const T* Pk = P + (size_t)kv * d * d + c0;
+  for (int i = tid; i < d * CPR; i += 256) {
+    const int j = i / CPR, c8 = i - j * CPR;
+    *reinterpret_cast<uint4*>(sP + j * CB + c8 * EPC) = ldg16(Pk + (size_t)j * d + c8 * EPC);
+  }
+  for (int i = tid; i < GT * d; i += 256) qs[i] = (i < G * d) ? to_f32(q[qbase + i]) : 0.f;
   __syncthreads();
+  const int cc = tid % CB, js = tid / CB;
   const int J = d / kQrotSlices;
-  const int c = tid % d, js = tid / d, j0 = js * J;
   float acc[GT];
 #pragma unroll
   for (int g = 0; g < GT; ++g) acc[g] = 0.f;
-#pragma unroll 8
   for (int jj = 0; jj < J; ++jj) {
-    const int j = j0 + jj;
-    const float pj = to_f32(sP[j * d + c]);
+    const int j = js * J + jj;
+    const float pj = to_f32(sP[j * CB + cc]);
 #pragma unroll
     for (int g = 0; g < GT; ++g) acc[g] = fmaf(qs[g * d + j], pj, acc[g]);
   }
 #pragma unroll
-  for (int g = 0; g < GT; ++g) red[(js * GT + g) * d + c] = acc[g];
+  for (int g = 0; g < GT; ++g) red[js][g][cc] = acc[g];
   __syncthreads();
-  if (js == 0) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      if (g >= G) break;
-      float v = red[g * d + c];
-      for (int t = 1; t < kQrotSlices; ++t) v += red[(t * GT + g) * d + c];
-      qrot[qbase + (size_t)g * d + c] = v;
-      if (qsplit) {
-        // three-way bf16 split v = h + m + l (each residual exact in fp32),
-        // plus a zero row, as MFMA operands: qsplit[row][part][c]
-        bf16_t* o = qsplit + (qbase + (size_t)g * d) * 4 + c;
-        const bf16_t h = f32_to_bf16(v);
-        const float r1 = v - to_f32(h);
-        const bf16_t mid = f32_to_bf16(r1);
-        const bf16_t lo = f32_to_bf16(r1 - to_f32(mid));
-        o[0] = h;
-        o[d] = mid;
-        o[2 * d] = lo;
-        o[3 * d] = 0;
-      }
+  for (int o = tid; o < GT * CB; o += 256) {
+    const int g = o / CB, cl = o - g * CB;
+    if (g >= G) continue;
+    float v = red[0][g][cl];
+    for (int t = 1; t < kQrotSlices; ++t) v += red[t][g][cl];
+    const int col = c0 + cl;
+    qrot[qbase + (size_t)g * d + col] = v;
+    if (qsplit) {
+      // three-way bf16 split v = h + m + l (each residual exact in fp32),
+      // plus a zero row, as MFMA operands: qsplit[row][part][c]
+      bf16_t* o4 = qsplit + (qbase + (size_t)g * d) * 4 + col;
+      const bf16_t h = f32_to_bf16(v);
+      const float r1 = v - to_f32(h);
+      const bf16_t mid = f32_to_bf16(r1);
+      const bf16_t lo = f32_to_bf16(r1 - to_f32(mid));
+      o4[0] = h;
+      o4[d] = mid;
+      o4[2 * d] = lo;
+      o4[3 * d] = 0;
     }
   }
 }
@@ -662,15 +650,8 @@ static hipError_t qrot_t(const DecodePlan& p, const void* q, const void* P, floa
                          bf16_t* qsplit, hipStream_t st) {
   return dispatch_group(p.G, [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
-    // LDS: P[kv], the queries, and the slice sums
-    const size_t lds = (size_t)p.d * p.d * sizeof(T) + (size_t)GT * p.d * sizeof(float) * (1 + kQrotSlices);
-    if (lds > 65536 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&qrot_kernel<T, GT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return hipGetLastError();
-    hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv), dim3(kQrotSlices * p.d), lds, st,
-                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, p.Hq,
-                       p.Hkv, p.d);
+    hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv, p.d / 32), dim3(256), 0, st,
+                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, p.Hq, p.Hkv, p.d);
     return hipGetLastError();
   });
 }
