@@ -12,6 +12,7 @@ constexpr int kMaxGroup = 16;        // largest supported Hq/Hkv
 constexpr int kAttendMfmaTokens = 256;  // tokens per wave in the MFMA attention kernel
 constexpr int kFusedThreads = 512;      // threads of the fused score+select kernel
 constexpr int kFusedMaxS = 16384;       // fused path: a head's keys fit in LDS and in 512 x 32 registers
+constexpr int kPairThreads = 1024;      // threads of the fused kernel for pairs of grouped heads
 constexpr int kSelRegMaxT = 32;         // selection keeps up to 1024 x 32 keys of a head in registers
 constexpr int kSelChunk = 16384;        // long heads: tokens per first-stage selection block
 
@@ -81,6 +82,10 @@ hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, cons
 size_t score_select_lds_bytes(int Sp);
 hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
                                int32_t* idx, uint32_t* bitmap, hipStream_t st);
+// Fused scores + top-k for pairs of heads of a group (bf16, G even, S <= kFusedMaxS).
+bool score_select_pair_fits(const DecodePlan& p);
+hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                                    int32_t* idx, uint32_t* bitmap, hipStream_t st);
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
                               const uint16_t* qsplit, const uint32_t* bitmap, float* part,
                               hipStream_t st);

@@ -66,6 +66,36 @@ __device__ __forceinline__ bf16x8_t q_operand(const uint16_t* __restrict__ qspli
   return as_bf16x8(v);
 }
 
+// A operand of the transposed product (heads in rows, tokens in columns):
+// row m = 4 h + part holds split part `part` of head head0 + h (part 3 is the
+// zero row), for the 8 dims starting at dim0; one 16-byte load.  Rows of
+// heads >= NH and dims >= r are zero.  Lane l of the result then holds, in
+// its four accumulators, the split partial products of head l / 16 for token
+// (column) l % 16, so one lane finishes one score with two adds.
+__device__ __forceinline__ bf16x8_t q_rows(const uint16_t* __restrict__ qsplit, size_t head0, int d, int NH,
+                                           int r, int m, int dim0) {
+  const int h = m >> 2, part = m & 3;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (h < NH && dim0 < r) v = ldg16(qsplit + ((head0 + h) * 4 + part) * (size_t)d + dim0);
+  const int valid = r - dim0;
+  if (valid < 8) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t keep = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
+      w[e] &= keep;
+    }
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return as_bf16x8(v);
+}
+
+// The score of a lane's (head, token) from the split partial products:
+// (h + m) + (l + 0), the same grouping as add_split_columns.
+__device__ __forceinline__ float sum_split_rows(const floatx4_t& acc) {
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // ============================================================================
 // Approximate scores, bf16 source (K_rot with ld = d, or K_lead with ld = R).
 // Each wave takes 16-token tiles of the block's chunk; for k-step s a lane
@@ -251,6 +281,94 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
   uint32_t key[T];  // the selection's register layout
   load_regs<T>(lk, S, key);
   select_regs<kFusedThreads, T>(key, sel, take, S, k, W, orow, brow, sh);
+}
+
+// ============================================================================
+// Fused approximate scores + top-k for grouped heads (G even): one block of
+// 1024 threads per pair of query heads of a (b, kv) group, one block per CU.
+// A CU's vector-memory path, not HBM, limits a kernel in which each query
+// head re-reads its group's source, so the pair shares one read: the MFMA B
+// operand carries both heads' split columns (n % 4 = head of the pair), the
+// two heads' keys (2 x S words) go to LDS, and the two selections follow one
+// another.  The G / 2 pairs of a group get block ids with the same value
+// mod 8 (one XCD) and consecutive dispatch order, so their reads of the
+// group's source share L2.
+// ============================================================================
+template <int KS, int U>
+__global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
+    const bf16_t* __restrict__ src, int ld, const uint16_t* __restrict__ qsplit, int B, int Hq,
+    int Hkv, int S, int Sp, int d, int r, int k, int W, int32_t* __restrict__ idx,
+    uint32_t* __restrict__ bitmap) {
+  constexpr int NWV = kPairThreads / 64;
+  constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
+  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] keys
+  __shared__ uint32_t sel[kNB];
+  __shared__ uint32_t take[kFusedMaxS / 32];
+  __shared__ SelScratch<kPairThreads> sh;
+  const int G = Hq / Hkv, NP = G / 2;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
+  if (gi >= B * Hkv) return;  // padding block (uniform)
+  const int b = gi / Hkv, kv = gi - b * Hkv;
+  const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, q = lane >> 4;
+
+  if (k >= S) {
+    keep_all<kPairThreads>(S, W, idx + row0 * k, bitmap + row0 * W);
+    keep_all<kPairThreads>(S, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
+    return;
+  }
+
+  // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qa[s] = q_rows(qsplit, row0, d, 2, r, m, 32 * s + 8 * q);
+
+  // Wave w takes tiles w + NWV i (16 tokens each) in batches of U, double
+  // buffered: the next batch is in flight while this one is multiplied.
+  // Loads are unconditional (token clamped to S - 1, dims to the row) so
+  // that each tile waits only for its own data; dims >= r are zeroed at the
+  // MFMA, tiles past S are dropped at the store.
+  const bf16_t* base = src + (size_t)gi * S * ld;
+  const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
+  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
+    }
+  };
+  auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 x = 32 * s + 8 * q < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
+      }
+      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q
+      if (q < 2 && t < S) lk[q * Sp + t] = score_key(sum_split_rows(acc));
+    }
+  };
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);
+  for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
+    load_batch(bi + 1, a1);
+    score_batch(bi, a0);
+    load_batch(bi + 2, a0);
+    score_batch(bi + 1, a1);
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    if (h) __syncthreads();  // the first selection is done with sel / take / sh
+    uint32_t key[T];
+    load_regs<T>(lk + h * Sp, S, key);
+    select_regs<kPairThreads, T>(key, sel, take, S, k, W, idx + (row0 + h) * k, bitmap + (row0 + h) * W, sh);
+  }
 }
 
 // ============================================================================
@@ -576,6 +694,38 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
     default: return hipErrorInvalidValue;
   }
 #undef LOKI_SS
+  return hipGetLastError();
+}
+
+bool score_select_pair_fits(const DecodePlan& p) {
+  return p.dt == 1 && p.G >= 2 && p.G % 2 == 0 && p.S <= kFusedMaxS && p.r <= 128;
+}
+
+hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                                    int32_t* idx, uint32_t* bitmap, hipStream_t st) {
+  if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
+  const size_t lds = 2 * (size_t)p.Sp * sizeof(uint32_t);
+  const int ngroups = p.B * p.Hkv;
+  const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  const int ks = (p.r + 31) / 32;
+  hipError_t e = hipSuccess;
+#define LOKI_SP(K)                                                                                      \
+  case K:                                                                                               \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_pair_kernel<K, 8 / K>),        \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
+    if (e != hipSuccess) return e;                                                                      \
+    hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K>), grid, block, lds, st, s, ld, qsplit, p.B, \
+                       p.Hq, p.Hkv, p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap);                       \
+    break;
+  switch (ks) {
+    LOKI_SP(1)
+    LOKI_SP(2)
+    LOKI_SP(3)
+    LOKI_SP(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOKI_SP
   return hipGetLastError();
 }
 

@@ -278,6 +278,13 @@ EDGE = [
     ("fused_r128_k1", 8, 32, 32, 777, 128, "bf16", 128, 1),
     ("fused_S16384", 4, 64, 64, 16384, 128, "bf16", 32, 700),
     ("many_heads_G4", 16, 16, 4, 1000, 128, "bf16", 24, 77),
+    # fused path for pairs of grouped heads (G even, >= 512 query heads, S <= 16384)
+    ("pair_ragged_r24", 16, 32, 8, 1000, 128, "bf16", 24, 77),
+    ("pair_G2_d64_r40", 32, 16, 8, 3001, 64, "bf16", 40, 300),
+    ("pair_G8_r128_k1", 16, 32, 4, 777, 128, "bf16", 128, 1),
+    ("pair_k_eq_S", 8, 64, 16, 300, 128, "bf16", 16, 300),
+    ("pair_G16_r1", 32, 16, 1, 2049, 64, "bf16", 1, 500),
+    ("pair_S16384", 8, 64, 16, 16384, 128, "bf16", 32, 700),
 ]
 
 
@@ -343,6 +350,20 @@ def test_fused_matches_two_kernel_path(gpu_lib):
                                          r=cfg.r, k=cfg.k)
     assert torch.equal(i_all[:4], i_half)
     assert torch.equal(o_all[:4].view(torch.int16), o_half.view(torch.int16))
+
+
+def test_pair_fused_matches_two_kernel_path(gpu_lib):
+    # grouped heads: 512 query heads (one fused block per pair of heads) against
+    # the first 256 of them (scores and selection in two kernels)
+    cfg = cfg_case("C3", S=4096, B=16)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    Kl = Kr[..., :cfg.r].contiguous()
+    o_all, i_all = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k, K_lead=Kl)
+    o_half, i_half = gpu_lib.loki_decode(q[:8].contiguous(), P, Kr[:8].contiguous(), V[:8].contiguous(),
+                                         r=cfg.r, k=cfg.k, K_lead=Kl[:8].contiguous())
+    assert torch.equal(i_all[:8], i_half)
+    assert torch.equal(o_all[:8].view(torch.int16), o_half.view(torch.int16))
 
 
 def test_decode_deterministic(gpu_lib):
