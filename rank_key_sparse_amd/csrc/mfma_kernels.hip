@@ -7,11 +7,15 @@
 // v_mfma_f32_16x16x32_bf16 they cost a few instructions per 16 tokens.
 //
 // q_rot is fp32 and must not be rounded to bf16: the rotation kernel splits
-// it into three bf16 parts q = h + m + l (|q - h - m - l| <= 2^-27 |q|),
-// placed here in separate B columns (column n = head (n % 4) + 4 * split, n = 12..15 zero), so that
-// one MFMA yields the three partial products of four heads with exact
-// bf16 x bf16 products and fp32 accumulation; two DPP row shifts then add
-// each head's three columns.
+// it into three bf16 parts q = h + m + l (|q - h - m - l| <= 2^-27 |q|).
+// One MFMA yields the three partial products of four heads with exact
+// bf16 x bf16 products and fp32 accumulation.  The approximate-score kernels
+// put the heads in A rows (row 4 h + split, tokens in B columns): lane l
+// ends with head l / 16's three partials for token l % 16 and adds them
+// itself, so every lane carries a result.  The exact-score pass of the
+// attention kernel puts them in B columns (column n = head (n % 4) + 4 split)
+// and adds each head's three columns with two DPP row shifts.  Both add the
+// parts as (h + m) + (l + 0), so the two layouts give identical scores.
 //
 // Operand layout of v_mfma_f32_16x16x32_bf16 (lane l, element i):
 //   A[m][k] : m = l % 16, k = 8 (l / 16) + i
@@ -98,11 +102,13 @@ __device__ __forceinline__ float sum_split_rows(const floatx4_t& acc) {
 
 // ============================================================================
 // Approximate scores, bf16 source (K_rot with ld = d, or K_lead with ld = R).
-// Each wave takes 16-token tiles of the block's chunk; for k-step s a lane
-// loads dims [32 s + 8 (l/16), +8) of token l % 16, so one load instruction
-// covers 16 tokens x 64 contiguous bytes of a dense K_lead.  Lanes n < 4 of
-// each row end with the scores of 4 consecutive tokens for head 4 grp + n
-// and store them with one 16-byte write.
+// Block = SC tokens of one (b, kv) group; wave w takes the chunk's 16-token
+// tiles w + 4 i in batches of U, double buffered.  For k-step s a lane loads
+// dims [32 s + 8 (l/16), +8) of token l % 16 (the B operand), so one load
+// instruction covers 16 tokens x 64 contiguous bytes of a dense K_lead;
+// loads are unconditional (token clamped into the chunk, dims into the row)
+// so that a tile waits only for its own data.  The heads sit in A rows, four
+// per MFMA: lane l ends with the score of head 4 grp + l / 16 for token l % 16.
 // ============================================================================
 template <int GT, int KS, bool KEYS>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restrict__ src,
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
                                                          int S, int d, int ld, int r, int SC) {
   constexpr int NGRP = (GT + 3) / 4;
   constexpr int UK = 8 / (KS * NGRP);
-  constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
+  constexpr int U = UK < 1 ? 1 : UK;  // tiles per batch and wave
   const int G = Hq / Hkv;
   const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
   const int t0 = blockIdx.x * SC, t1 = min(S, t0 + SC);
@@ -120,12 +126,12 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
   const int m = lane & 15, q = lane >> 4;
   const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
 
-  bf16x8_t bv[NGRP][KS];
+  bf16x8_t qa[NGRP][KS];
 #pragma unroll
   for (int grp = 0; grp < NGRP; ++grp)
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      bv[grp][s] = q_operand(qsplit, head0, d, G, r, grp, m, 32 * s + 8 * q);
+      qa[grp][s] = q_rows(qsplit, head0 + 4 * grp, d, G - 4 * grp, r, m, 32 * s + 8 * q);
 
   const bf16_t* base = src + (size_t)bk * S * ld;
   __shared__ uint32_t smn[GT], smx[GT];
@@ -133,64 +139,57 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
   uint32_t mn[NGRP], mx[NGRP];
 #pragma unroll
   for (int grp = 0; grp < NGRP; ++grp) { mn[grp] = 0xffffffffu; mx[grp] = 0u; }
-  for (int j0 = wave; t0 + 16 * j0 < t1; j0 += 4 * U) {
-    uint4 a[U][KS];
+  const int nbat = ((t1 - t0 + 15) / 16 + 4 * U - 1) / (4 * U);
+  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + 16 * (j0 + 4 * u) + m;
+      const int t = min(t0 + 16 * (wave + 4 * (bi * U + u)) + m, t1 - 1);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int dim0 = 32 * s + 8 * q;
-        a[u][s] = (t < t1 && dim0 < r) ? ldg16(base + (size_t)t * ld + dim0) : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
     }
+  };
+  auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int tb = t0 + 16 * (j0 + 4 * u) + 4 * q;  // this lane's 4 output tokens
+      const int t = t0 + 16 * (wave + 4 * (bi * U + u)) + m;  // this lane's token
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][s]), bv[grp][s], acc, 0, 0, 0);
-        float x[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = add_split_columns(acc[v]);
-        const int g = 4 * grp + m;
-        if (m < 4 && g < G && tb < t1) {
-          const size_t o = (head0 + g) * (size_t)out_stride + tb;
+        for (int s = 0; s < KS; ++s) {
+          const uint4 x = 32 * s + 8 * q < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[grp][s], as_bf16x8(x), acc, 0, 0, 0);
+        }
+        const float x = sum_split_rows(acc);
+        const int g = 4 * grp + q;
+        if (g < G && t < t1) {
+          const size_t o = (head0 + g) * (size_t)out_stride + t;
           if constexpr (KEYS) {
-            uint32_t* ko = static_cast<uint32_t*>(out);
-            uint32_t key[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) key[v] = score_key(x[v]);
-            if (tb + 3 < t1) {
-              *reinterpret_cast<uint4*>(ko + o) = make_uint4(key[0], key[1], key[2], key[3]);
-            } else {
-#pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (tb + v < t1) ko[o + v] = key[v];
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (tb + v < t1) { mn[grp] = min(mn[grp], key[v]); mx[grp] = max(mx[grp], key[v]); }
+            const uint32_t key = score_key(x);
+            static_cast<uint32_t*>(out)[o] = key;
+            mn[grp] = min(mn[grp], key);
+            mx[grp] = max(mx[grp], key);
           } else {
-            float* fo = static_cast<float*>(out);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (tb + v < t1) fo[o + v] = x[v];
+            static_cast<float*>(out)[o] = x;
           }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);
+  for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
+    load_batch(bi + 1, a1);
+    score_batch(bi, a0);
+    load_batch(bi + 2, a0);
+    score_batch(bi + 1, a1);
   }
   if (KEYS && mm) {  // uniform: the chunk's min / max key per head
     __syncthreads();
 #pragma unroll
     for (int grp = 0; grp < NGRP; ++grp) {
-      const int g = 4 * grp + m;
-      if (m < 4 && g < G && mn[grp] <= mx[grp]) { atomicMin(&smn[g], mn[grp]); atomicMax(&smx[g], mx[grp]); }
+      const int g = 4 * grp + q;
+      if (g < G && mn[grp] <= mx[grp]) { atomicMin(&smn[g], mn[grp]); atomicMax(&smx[g], mx[grp]); }
     }
     __syncthreads();
     if (threadIdx.x < G) mm[(head0 + threadIdx.x) * gridDim.x + blockIdx.x] = make_uint2(smn[threadIdx.x], smx[threadIdx.x]);
@@ -238,44 +237,43 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
     return;
   }
 
-  // B operands: this head alone (column n = split n / 4 when n % 4 == 0)
-  bf16x8_t bv[KS];
+  // A operands: this head's splits in rows 0..3
+  bf16x8_t qa[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) bv[s] = q_operand(qsplit, row, d, 1, r, 0, m, 32 * s + 8 * q);
+  for (int s = 0; s < KS; ++s) qa[s] = q_rows(qsplit, row, d, 1, r, m, 32 * s + 8 * q);
 
+  // tiles of 16 tokens, wave w takes tiles w + NWV i in double-buffered
+  // batches of U; unconditional loads as in score_mfma_kernel
   const bf16_t* base = src + (size_t)gi * S * ld;
-  for (int j0 = wave; 16 * j0 < S; j0 += NWV * U) {
-    uint4 a[U][KS];
+  const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
+  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = 16 * (j0 + NWV * u) + m;
+      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int dim0 = 32 * s + 8 * q;
-        a[u][s] = (t < S && dim0 < r) ? ldg16(base + (size_t)t * ld + dim0) : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
     }
+  };
+  auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][s]), bv[s], acc, 0, 0, 0);
-      uint32_t key[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) key[v] = score_key(add_split_columns(acc[v]));
-      const int tb = 16 * (j0 + NWV * u) + 4 * q;  // this lane's 4 tokens
-      if (m == 0 && tb < S) {
-        if (tb + 3 < S) {
-          *reinterpret_cast<uint4*>(lk + tb) = make_uint4(key[0], key[1], key[2], key[3]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (tb + v < S) lk[tb + v] = key[v];
-        }
+      for (int s = 0; s < KS; ++s) {
+        const uint4 x = 32 * s + 8 * q < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token (lanes 0..15)
+      if (q == 0 && t < S) lk[t] = score_key(sum_split_rows(acc));
     }
+  };
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);
+  for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
+    load_batch(bi + 1, a1);
+    score_batch(bi, a0);
+    load_batch(bi + 2, a0);
+    score_batch(bi + 1, a1);
   }
   __syncthreads();
   uint32_t key[T];  // the selection's register layout
@@ -426,7 +424,18 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
   float* e = s_e[wave];
   uint32_t* bits = s_bits[wave];
 
-  // union list of the span
+  // A operands of pass 1 (the group's heads in rows), requested together
+  // with the bitmap words so that one wait covers both
+  bf16x8_t qa[NGRP][KS];
+#pragma unroll
+  for (int grp = 0; grp < NGRP; ++grp)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qa[grp][s] = q_rows(qsplit, head0 + 4 * grp, D, G - 4 * grp, D, m, 32 * s + 8 * q);
+
+  // union list of the span; tok[0] starts as a valid row so that the clamped
+  // V loads below stay in bounds when the list is empty
+  if (lane == 0) tok[0] = min(t0, S - 1);
   if (lane < G * NW) {
     const int g = lane / NW, w = lane - g * NW;
     const int t = t0 + 32 * w;
@@ -460,44 +469,38 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
 
   // pass 1: exact scores.  k-step s covers dims [32 s, 32 s + 32), lane
   // quarter q the 8 dims from 32 s + 8 q, so one load instruction reads 64
-  // contiguous bytes of each of the tile's 16 rows.
+  // contiguous bytes of each of the tile's 16 rows (the B operand; rows past
+  // the list repeat its last row and are dropped).  The heads sit in A rows:
+  // lane l ends with the score of head 4 grp + l / 16 for row l % 16.
   float mloc[NGRP];
 #pragma unroll
   for (int grp = 0; grp < NGRP; ++grp) mloc[grp] = -INFINITY;
   {
-    bf16x8_t bv[NGRP][KS];
-#pragma unroll
-    for (int grp = 0; grp < NGRP; ++grp)
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-        bv[grp][s] = q_operand(qsplit, head0, D, G, D, grp, m, 32 * s + 8 * q);
     for (int p0 = 0; p0 < n; p0 += 16 * KT) {
       uint4 ka[KT][KS];
 #pragma unroll
       for (int tl = 0; tl < KT; ++tl) {
-        const int p = p0 + 16 * tl + m;
-        const bf16_t* row = K_rot + cb + (size_t)(p < n ? tok[p] : 0) * D + 8 * q;
+        const int p = min(p0 + 16 * tl + m, n - 1);
+        const bf16_t* row = K_rot + cb + (size_t)tok[p] * D + 8 * q;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) ka[tl][s] = (p < n) ? ldg16(row + 32 * s) : make_uint4(0u, 0u, 0u, 0u);
+        for (int s = 0; s < KS; ++s) ka[tl][s] = ldg16(row + 32 * s);
       }
 #pragma unroll
       for (int tl = 0; tl < KT; ++tl) {
         if (p0 + 16 * tl >= n) break;  // uniform across the wave
+        const int p = p0 + 16 * tl + m;
 #pragma unroll
         for (int grp = 0; grp < NGRP; ++grp) {
           floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KS; ++s)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[tl][s]), bv[grp][s], sacc, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float x = add_split_columns(sacc[v]);
-            const int p = p0 + 16 * tl + 4 * q + v, g = 4 * grp + m;
-            if (m < 4 && g < GT && p < n) {
-              const float sc = (g < G && ((hmk[p] >> g) & 1)) ? x * scale_log2 : -INFINITY;
-              e[p * GT + g] = sc;
-              mloc[grp] = fmaxf(mloc[grp], sc);
-            }
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[grp][s], as_bf16x8(ka[tl][s]), sacc, 0, 0, 0);
+          const float x = sum_split_rows(sacc);
+          const int g = 4 * grp + q;
+          if (g < GT && p < n) {
+            const float sc = (g < G && ((hmk[p] >> g) & 1)) ? x * scale_log2 : -INFINITY;
+            e[p * GT + g] = sc;
+            mloc[grp] = fmaxf(mloc[grp], sc);
           }
         }
       }
@@ -508,13 +511,15 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // the first batch of V rows is requested now (the K tiles' registers are
-  // free), so that the weights pass below runs while the rows travel
+  // free), so that the weights pass below runs while the rows travel.  Rows
+  // past the list repeat its last row (tok[0] if it is empty; weight 0), so
+  // every load is unconditional and waits only where its data is used.
   const int lg = lane / RL, li = lane % RL;
   auto load_v = [&](int p0, uint4 (&vb)[UV]) {
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
-      const int p = p0 + RPW * u + lg;
-      vb[u] = (p < n) ? ldg16(V + cb + (size_t)tok[p] * D + li * EPL) : make_uint4(0u, 0u, 0u, 0u);
+      const int p = max(min(p0 + RPW * u + lg, n - 1), 0);
+      vb[u] = ldg16(V + cb + (size_t)tok[p] * D + li * EPL);
     }
   };
   uint4 vb[UV];
@@ -523,15 +528,18 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
   __builtin_amdgcn_sched_barrier(0);
 
   // per-head softmax statistics of the span: the max from the score lanes
-  // (lane 16 q + m holds head 4 grp + m), then one pass over the (token,
-  // head) entries in which lane % GT is the head: weights in place, sums
+  // (the 16 lanes 16 q .. 16 q + 15 hold head 4 grp + q), then one pass over
+  // the (token, head) entries in which lane % GT is the head: weights in
+  // place, sums
 #pragma unroll
   for (int grp = 0; grp < NGRP; ++grp) {
     float v = mloc[grp];
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    const int g = 4 * grp + m;
-    if (q == 0 && m < 4 && g < GT) s_mx[wave][g] = v;
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F)));  // lane ^ 1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F)));  // lane ^ 2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F)));  // lane ^ 4
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F)));  // lane ^ 8
+    const int g = 4 * grp + q;
+    if (m == 0 && g < GT) s_mx[wave][g] = v;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
