@@ -176,6 +176,21 @@ def cpu_baseline(x, cfg, out_gpu, idx_gpu, seconds: float):
             "gpu_matches_oracle_on_sample": ok}
 
 
+def score_stage_kernel(cfg) -> str:
+    """The kernel that runs the score stage of a bf16 decode (the library's
+    dispatch rule): scores and selection fused, one block per query head, when
+    every query head has its own key head; fused per pair of query heads of a
+    group when the group size is even; otherwise the score kernel alone (the
+    selection then runs as its own stage)."""
+    G = cfg.Hq // cfg.Hkv
+    if cfg.dtype == "bf16" and cfg.S <= 16384:
+        if cfg.Hq == cfg.Hkv and cfg.B * cfg.Hq >= 256:
+            return "score_select_kernel"
+        if G % 2 == 0 and cfg.B * cfg.Hq >= 512 and cfg.r <= 128:
+            return "score_select_pair_kernel"
+    return "score_mfma_kernel"
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -248,7 +263,7 @@ def run(args) -> dict:
         + cfg.B * cfg.Hq * cfg.k * 4
     per_kernel_bytes = {"scores": by_prefix, "attend": by_gather}
     dom = max(("scores", "attend"), key=lambda s: stage_us[s])
-    dom_kernel = {"scores": "score_mfma_kernel", "attend": "attend_mfma_kernel"}[dom]
+    dom_kernel = {"scores": score_stage_kernel(cfg), "attend": "attend_mfma_kernel"}[dom]
     achieved = per_kernel_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(args.workload, dom_kernel)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
