@@ -285,12 +285,12 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 // Fused approximate scores + top-k for grouped heads (G even): one block of
 // 1024 threads per pair of query heads of a (b, kv) group, one block per CU.
 // A CU's vector-memory path, not HBM, limits a kernel in which each query
-// head re-reads its group's source, so the pair shares one read: the MFMA B
-// operand carries both heads' split columns (n % 4 = head of the pair), the
-// two heads' keys (2 x S words) go to LDS, and the two selections follow one
-// another.  The G / 2 pairs of a group get block ids with the same value
-// mod 8 (one XCD) and consecutive dispatch order, so their reads of the
-// group's source share L2.
+// head re-reads its group's source, so the pair shares one read: the MFMA A
+// operand carries both heads' split rows, the two heads' keys (2 x S words)
+// go to LDS, and one two-head selection (select_regs2) keeps the k best of
+// each.  The G / 2 pairs of a group get block ids with the same value mod 8
+// (one XCD) and consecutive dispatch order, so their reads of the group's
+// source share L2.
 // ============================================================================
 template <int KS, int U>
 __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
@@ -300,9 +300,10 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   constexpr int NWV = kPairThreads / 64;
   constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
   extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] keys
-  __shared__ uint32_t sel[kNB];
-  __shared__ uint32_t take[kFusedMaxS / 32];
-  __shared__ SelScratch<kPairThreads> sh;
+  __shared__ __align__(16) uint32_t sel[2][kNB];
+  __shared__ uint32_t take[2][kFusedMaxS / 32];
+  __shared__ SelScratch<kPairThreads> sh[2];
+  __shared__ uint32_t smm[2][2];  // per head {min, max} key
   const int G = Hq / Hkv, NP = G / 2;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
@@ -338,6 +339,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
     }
   };
+  // the key range of each head, gathered while the keys are made (the
+  // selection then needs no pass of its own for it)
+  uint32_t kmn = 0xffffffffu, kmx = 0u;
   auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -348,25 +352,51 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
       }
       const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q
-      if (q < 2 && t < S) lk[q * Sp + t] = score_key(sum_split_rows(acc));
+      if (q < 2 && t < S) {
+        const uint32_t key = score_key(sum_split_rows(acc));
+        lk[q * Sp + t] = key;
+        kmn = min(kmn, key);
+        kmx = max(kmx, key);
+      }
     }
   };
   uint4 a0[U][KS], a1[U][KS];
   load_batch(0, a0);
+  // the selection's scratch is cleared now, under the score phase
+  for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
+  for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
+  if (tid < 2) {
+    smm[tid][0] = 0xffffffffu;
+    smm[tid][1] = 0u;
+    sh[tid].ccount = 0;
+  }
+  __syncthreads();  // orders the initialisation before the atomics below
   for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
     load_batch(bi + 1, a1);
     score_batch(bi, a0);
     load_batch(bi + 2, a0);
     score_batch(bi + 1, a1);
   }
-  __syncthreads();
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    if (h) __syncthreads();  // the first selection is done with sel / take / sh
-    uint32_t key[T];
-    load_regs<T>(lk + h * Sp, S, key);
-    select_regs<kPairThreads, T>(key, sel, take, S, k, W, idx + (row0 + h) * k, bitmap + (row0 + h) * W, sh);
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) {  // over the 16 lanes of a head's row
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, x));
   }
+  if (m == 0 && q < 2) {
+    atomicMin(&smm[q][0], kmn);
+    atomicMax(&smm[q][1], kmx);
+  }
+  __syncthreads();
+  uint32_t key[2][T];
+  load_regs<T>(lk, S, key[0]);
+  load_regs<T>(lk + Sp, S, key[1]);
+  uint32_t* const lds2[2] = {sel[0], sel[1]};
+  uint32_t* const take2[2] = {take[0], take[1]};
+  int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
+  uint32_t* const brow2[2] = {bitmap + row0 * W, bitmap + (row0 + 1) * W};
+  SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
+  const uint32_t* const kmm2[2] = {smm[0], smm[1]};
+  select_regs2<kPairThreads, T>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
 }
 
 // ============================================================================

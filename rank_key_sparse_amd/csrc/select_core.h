@@ -149,18 +149,28 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Ranks the nc collected candidates (ck, ci) by (key desc, index asc) and
-// calls set(index) for the `need` best.
+// Ranks the nc collected candidates (ck, ci; both 16-byte aligned) by (key
+// desc, index asc) and calls set(index) for the `need` best.  The candidates
+// are read four at a time, eight in flight, so that the loop is not a chain
+// of dependent LDS round trips.
 template <int NTHR, typename F>
 __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32_t* ci, int nc, int need,
                                                 F&& set) {
+  auto beats = [](uint32_t vc, uint32_t ic, uint32_t vi, uint32_t ii) {
+    return (int)((vc > vi) || (vc == vi && ic < ii));
+  };
   for (int i = threadIdx.x; i < nc; i += NTHR) {
     const uint32_t vi = ck[i], ii = ci[i];
     int rank = 0;
-    for (int c = 0; c < nc; ++c) {
-      const uint32_t vc = ck[c], ic = ci[c];
-      rank += (vc > vi) || (vc == vi && ic < ii);
+    const int n4 = nc & ~3;
+#pragma unroll 2
+    for (int c = 0; c < n4; c += 4) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(ck + c);
+      const uint4 iv = *reinterpret_cast<const uint4*>(ci + c);
+      rank += beats(kv.x, iv.x, vi, ii) + beats(kv.y, iv.y, vi, ii) + beats(kv.z, iv.z, vi, ii) +
+              beats(kv.w, iv.w, vi, ii);
     }
+    for (int c = n4; c < nc; ++c) rank += beats(ck[c], ci[c], vi, ii);
     if (rank < need) set(ii);
   }
 }
@@ -172,6 +182,10 @@ __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32
 // Output: orow[0..k) = the kept positions p, ascending, written as map[p]
 // when map is given, else as p + tok_base; with okeys, okeys[i] receives the
 // key of orow[i]; with brow, the kept-position bitmap (W words).
+// kmm: when given, {min, max} of the keys (e.g. gathered while the keys were
+// made), readable by every thread after one barrier; the min / max pass is
+// then skipped.  KB: keep each key's bin in registers from the histogram to
+// the mask pass instead of computing it twice (T more registers).
 // ============================================================================
 
 // Token of key[0] of this lane (key[i] is token tok0 + 64 i), and the number
@@ -195,32 +209,44 @@ __device__ __forceinline__ void load_regs(const uint32_t* src, int S, uint32_t (
   for (int i = 0; i < T; ++i) key[i] = src[min(tok0 + 64 * i, S - 1)];
 }
 
-template <int NTHR, int T>
+template <int NTHR, int T, bool KB = false>
 __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* lds, uint32_t* take,
                                             int S, int k, int W, int32_t* orow, uint32_t* brow,
                                             SelScratch<NTHR>& sh, const int32_t* map = nullptr,
-                                            uint32_t* okeys = nullptr, int tok_base = 0) {
+                                            uint32_t* okeys = nullptr, int tok_base = 0,
+                                            const uint32_t* kmm = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* hist = lds;
 
   for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
   for (int i = tid; i < W; i += NTHR) take[i] = 0u;
   if (tid == 0) sh.ccount = 0;
-  uint32_t mn = 0xffffffffu, mx = 0u;
   int nv = opaque(regs_valid<T>(S));
-#pragma unroll
-  for (int i = 0; i < T; ++i)
-    if (i < nv) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
   uint32_t kmin, kmax;
-  block_minmax<NTHR>(mn, mx, sh, kmin, kmax);  // its barrier also orders the zeroing
+  if (kmm) {  // uniform
+    __syncthreads();  // orders the zeroing
+    kmin = kmm[0];
+    kmax = kmm[1];
+  } else {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      if (i < nv) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
+    block_minmax<NTHR>(mn, mx, sh, kmin, kmax);  // its barrier also orders the zeroing
+  }
   Binner bin;
   bin.init(kmin, kmax);
 
   // 1. histogram and threshold bin
+  int kb[KB ? T : 1];
   nv = opaque(nv);
 #pragma unroll
   for (int i = 0; i < T; ++i)
-    if (i < nv) atomicAdd(&hist[bin(key[i])], 1u);
+    if (i < nv) {
+      const int b = bin(key[i]);
+      if constexpr (KB) kb[i] = b;
+      atomicAdd(&hist[b], 1u);
+    }
   __syncthreads();
   find_threshold<NTHR>(hist, k, sh);  // its trailing barrier ends every read of hist
   const int tb = sh.t;
@@ -237,7 +263,12 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const int j = tok0 + 64 * i;
-    const int bj = (i < nv) ? bin(key[i]) : -1;
+    int bj = -1;
+    if constexpr (KB) {
+      if (i < nv) bj = kb[i];
+    } else {
+      if (i < nv) bj = bin(key[i]);
+    }
     const uint64_t mab = __ballot(bj > tb);
     if (lane == i) { klo = (uint32_t)mab; khi = (uint32_t)(mab >> 32); }
     if (rank_path && bj == tb) {
@@ -321,6 +352,181 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   if (brow) {
     const int st = wave * T + lane;
     if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow + 2 * st) = make_uint2(klo, khi);
+  }
+}
+
+// ============================================================================
+// Two heads at once (same S, k, W; keys in registers as for select_regs):
+// every step handles both heads between shared barriers, so a pair costs
+// the barriers and latencies of one selection.  Both histograms go through
+// one block scan with the two counts packed in 16-bit halves, which needs
+// S < 65536.  The caller zeroes hist[h] (kNB words) and take[h] (W words),
+// sets sh[h].ccount = 0 and provides kmm[h] = {min, max} of head h's keys,
+// all ordered before the call by a barrier.  lds[h] / take[h] / sh[h] are
+// separate per head.  Output per head as for select_regs (no map / okeys).
+// ============================================================================
+template <int NTHR, int T>
+__device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32_t* const (&lds)[2],
+                                             uint32_t* const (&take)[2], int S, int k, int W,
+                                             int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
+                                             SelScratch<NTHR>* const (&sh)[2],
+                                             const uint32_t* const (&kmm)[2]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Binner bin[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) bin[h].init(kmm[h][0], kmm[h][1]);
+
+  // 1. both histograms; each key's bin stays in a register for step 2
+  int kb[2][T];
+  int nv = opaque(regs_valid<T>(S));
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      if (i < nv) {
+        kb[h][i] = bin[h](key[h][i]);
+        atomicAdd(&lds[h][kb[h][i]], 1u);
+      }
+  __syncthreads();
+
+  // threshold bins: one scan of (count0 | count1 << 16) from the top bin
+  {
+    constexpr int BPT = kNB / NTHR;
+    const int top = kNB - 1 - BPT * tid;
+    int hv[2][BPT];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      hv[0][i] = (int)lds[0][top - i];
+      hv[1][i] = (int)lds[1][top - i];
+      mine += hv[0][i] | (hv[1][i] << 16);
+    }
+    const int above = block_incl_scan<NTHR>(mine, *sh[0]) - mine;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int a = (above >> (16 * h)) & 0xffff;
+#pragma unroll
+      for (int i = 0; i < BPT; ++i) {
+        if (a < k && a + hv[h][i] >= k) { sh[h]->t = top - i; sh[h]->above = a; sh[h]->nt = hv[h][i]; }
+        a += hv[h][i];
+      }
+    }
+    __syncthreads();  // ends every read of the histograms
+  }
+  int tb[2], need[2], nc[2];
+  bool rank_path[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    tb[h] = sh[h]->t;
+    need[h] = k - sh[h]->above;
+    nc[h] = sh[h]->nt;
+    rank_path[h] = nc[h] <= kRankMax;
+  }
+
+  // 2. above-masks and threshold-bin candidates of both heads
+  uint32_t klo[2] = {0u, 0u}, khi[2] = {0u, 0u};
+  nv = opaque(nv);
+  const int tok0 = opaque(regs_tok0<T>());
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t* ck = lds[h];
+    uint32_t* ci = lds[h] + kCap;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const int bj = (i < nv) ? kb[h][i] : -1;
+      const uint64_t mab = __ballot(bj > tb[h]);
+      if (lane == i) { klo[h] = (uint32_t)mab; khi[h] = (uint32_t)(mab >> 32); }
+      if (rank_path[h] && bj == tb[h]) {
+        const int p = atomicAdd(&sh[h]->ccount, 1);
+        ck[p] = key[h][i];
+        ci[p] = (uint32_t)(tok0 + 64 * i);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. the need best tokens of each threshold bin
+  if (rank_path[0] || rank_path[1]) {  // uniform
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (rank_path[h]) {
+        uint32_t* tk = take[h];
+        rank_candidates<NTHR>(lds[h], lds[h] + kCap, nc[h], need[h],
+                              [&](uint32_t ii) { atomicOr(&tk[ii >> 5], 1u << (ii & 31)); });
+      }
+    __syncthreads();
+    const int st = wave * T + lane;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (rank_path[h] && lane < T && 2 * st < W) { klo[h] |= take[h][2 * st]; khi[h] |= take[h][2 * st + 1]; }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (rank_path[h]) continue;  // uniform
+    // crowded threshold bin: exact radix select inside it (as in select_regs)
+    uint32_t* hist = lds[h];
+    uint32_t prefix = 0u, pmask = 0u;
+    int rem = need[h];
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int sft = shifts[pass];
+      const uint32_t dm = (1u << widths[pass]) - 1u;
+      for (int i = tid; i < kNB; i += NTHR) hist[i] = 0u;
+      __syncthreads();
+      const int nvp = opaque(nv);
+#pragma unroll
+      for (int i = 0; i < T; ++i)
+        if (i < nvp && kb[h][i] == tb[h] && (key[h][i] & pmask) == prefix)
+          atomicAdd(&hist[(key[h][i] >> sft) & dm], 1u);
+      __syncthreads();
+      find_threshold<NTHR>(hist, rem, *sh[h]);
+      rem -= sh[h]->above;
+      prefix |= (uint32_t)sh[h]->t << sft;
+      pmask |= dm << sft;
+      __syncthreads();
+    }
+    const uint32_t kstar = prefix;
+    const int quota = rem;
+    int neq = 0;
+    const int nve = opaque(nv);
+#pragma unroll
+    for (int i = 0; i < T; ++i) neq += __popcll(__ballot(i < nve && key[h][i] == kstar));
+    if (lane == 0) sh[h]->weq[wave] = neq;
+    __syncthreads();
+    int eqrun = waves_below<NTHR>(sh[h]->weq);
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const bool valid = i < nve;
+      const bool eq = valid && key[h][i] == kstar;
+      const uint64_t eqm = __ballot(eq);
+      const bool tk = (valid && key[h][i] > kstar && kb[h][i] == tb[h]) ||
+                      (eq && eqrun + bits_below(eqm) < quota);
+      const uint64_t tm = __ballot(tk);
+      if (lane == i) { klo[h] |= (uint32_t)tm; khi[h] |= (uint32_t)(tm >> 32); }
+      eqrun += __popcll(eqm);
+    }
+  }
+
+  // 4. emit both heads: one scan of (count0 | count1 << 16)
+  const int cnt = (lane < T) ? ((__popc(klo[0]) + __popc(khi[0])) | ((__popc(klo[1]) + __popc(khi[1])) << 16)) : 0;
+  const int incl = wave_incl_scan(cnt);
+  if (lane == 63) sh[0]->wsel[wave] = incl;
+  __syncthreads();  // also: every read of lds / take above is done
+  const int offp = waves_below<NTHR>(sh[0]->wsel) + incl - cnt;
+  const int t0 = opaque(regs_tok0<T>());
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int off = (offp >> (16 * h)) & 0xffff;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi[h], i) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)klo[h], i);
+      const int o = __builtin_amdgcn_readlane(off, i);
+      if ((f >> lane) & 1ull) orow[h][o + bits_below(f)] = t0 + 64 * i;
+    }
+    const int st = wave * T + lane;
+    if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow[h] + 2 * st) = make_uint2(klo[h], khi[h]);
   }
 }
 

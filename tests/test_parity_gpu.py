@@ -352,6 +352,36 @@ def test_fused_matches_two_kernel_path(gpu_lib):
     assert torch.equal(o_all[:4].view(torch.int16), o_half.view(torch.int16))
 
 
+def test_pair_fused_rank_and_radix_heads(gpu_lib):
+    # pair-fused path (512 grouped query heads) with every even head's query
+    # zero: its scores all tie (threshold bin crowded, radix tie path, lowest
+    # indices kept) while the odd head of the same pair ranks a few candidates
+    cfg = cfg_case("C3", S=2048, B=16)
+    x = make_inputs(cfg)
+    x = dict(x)
+    q = x["q"].clone()
+    q[:, 0::2, :] = 0
+    x["q"] = q
+    _, idx_g, _ = run_decode(gpu_lib, x, cfg.r, cfg.k, R=cfg.r)
+    ig = idx_g.cpu().numpy()
+    assert np.array_equal(ig[:, 0::2], np.broadcast_to(np.arange(cfg.k), ig[:, 0::2].shape))
+
+
+def test_decode_all_equal_keys_pair(gpu_lib):
+    B, Hq, Hkv, S, d = 16, 32, 8, 2000, 128  # 512 grouped heads: pair-fused path
+    Kr = torch.ones((B, Hkv, S, d), dtype=torch.bfloat16)
+    g = torch.Generator().manual_seed(2)
+    V = torch.randn((B, Hkv, S, d), generator=g).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g).to(torch.bfloat16)
+    P = torch.eye(d).expand(Hkv, d, d).contiguous().to(torch.bfloat16)
+    k = 700
+    out_g, idx_g = gpu_lib.loki_decode(dev(q), dev(P), dev(Kr), dev(V), r=32, k=k,
+                                       K_lead=dev(Kr[..., :32].contiguous()))
+    assert np.array_equal(idx_g.cpu().numpy(), np.broadcast_to(np.arange(k), (B, Hq, k)))
+    out_o = oracle.attend(q, P, Kr, V, np.broadcast_to(np.arange(k), (B, Hq, k)))
+    assert max_abs(out_g, out_o) <= OUT_TOL[torch.bfloat16]
+
+
 def test_pair_fused_matches_two_kernel_path(gpu_lib):
     # grouped heads: 512 query heads (one fused block per pair of heads) against
     # the first 256 of them (scores and selection in two kernels)
