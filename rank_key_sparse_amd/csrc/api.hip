@@ -150,20 +150,21 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
   uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
   float* part = at<float>(workspace, p.off_part);
-  if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
-  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
-  if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
   const void* src = K_lead ? K_lead : K_rot;
   const int ld = K_lead ? R : d;
   // bf16, a head's keys small enough for LDS and enough blocks to fill the
   // chip: scores and selection in one kernel, one block per query head when
   // each query head has its own key head, one block per pair of query heads
-  // of a group otherwise; else two kernels with the keys in the workspace
+  // of a group otherwise (that kernel also rotates its queries, so the
+  // rotation stage is empty); else two kernels with the keys in the workspace
   const bool fused = dt == LOKI_BF16 && Hq == Hkv && S <= kFusedMaxS && (int64_t)B * Hq >= 256;
   const bool pair = !fused && score_select_pair_fits(p) && (int64_t)B * Hq >= 2 * 256;
+  if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
+  if (!pair) LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
+  if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
   if (fused || pair) {
     if (fused) LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
-    else LOKI_HIP(launch_score_select_pair(p, src, ld, qsplit, idx, bitmap, stream));
+    else LOKI_HIP(launch_score_select_pair(p, src, ld, q, P, qrot, qsplit, idx, bitmap, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
   } else {
     uint2* mm = select_needs_minmax(S) ? at<uint2>(workspace, p.off_mm) : nullptr;

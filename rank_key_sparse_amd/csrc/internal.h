@@ -84,8 +84,11 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
                                int32_t* idx, uint32_t* bitmap, hipStream_t st);
 // Fused scores + top-k for pairs of heads of a group (bf16, G even, S <= kFusedMaxS).
 bool score_select_pair_fits(const DecodePlan& p);
-hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
-                                    int32_t* idx, uint32_t* bitmap, hipStream_t st);
+// The pair kernel also rotates its two query heads (q_rot and the split to
+// the workspace), so no rotation kernel runs before it.
+hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
+                                    hipStream_t st);
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
                               const uint16_t* qsplit, const uint32_t* bitmap, float* part,
                               hipStream_t st);

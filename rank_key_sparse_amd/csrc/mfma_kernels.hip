@@ -294,16 +294,17 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 // ============================================================================
 template <int KS, int U>
 __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
-    const bf16_t* __restrict__ src, int ld, const uint16_t* __restrict__ qsplit, int B, int Hq,
-    int Hkv, int S, int Sp, int d, int r, int k, int W, int32_t* __restrict__ idx,
-    uint32_t* __restrict__ bitmap) {
+    const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P,
+    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int S, int Sp, int d,
+    int r, int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap) {
   constexpr int NWV = kPairThreads / 64;
   constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
-  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] keys
+  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] keys (first: rotation scratch)
   __shared__ __align__(16) uint32_t sel[2][kNB];
   __shared__ uint32_t take[2][kFusedMaxS / 32];
   __shared__ SelScratch<kPairThreads> sh[2];
   __shared__ uint32_t smm[2][2];  // per head {min, max} key
+  __shared__ __align__(16) uint16_t sqs[2 * 4 * 128];  // the pair's split rows [h][part][d]
   const int G = Hq / Hkv, NP = G / 2;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
@@ -311,18 +312,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   const int b = gi / Hkv, kv = gi - b * Hkv;
   const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 15, q = lane >> 4;
-
-  if (k >= S) {
-    keep_all<kPairThreads>(S, W, idx + row0 * k, bitmap + row0 * W);
-    keep_all<kPairThreads>(S, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
-    return;
-  }
-
-  // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
-  bf16x8_t qa[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) qa[s] = q_rows(qsplit, row0, d, 2, r, m, 32 * s + 8 * q);
+  const int m = lane & 15, q4 = lane >> 4;
 
   // Wave w takes tiles w + NWV i (16 tokens each) in batches of U, double
   // buffered: the next batch is in flight while this one is multiplied.
@@ -336,9 +326,74 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     for (int u = 0; u < U; ++u) {
       const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q4, ld - 8));
     }
   };
+  // the pair's query rotation q_rot = q P[kv], with the arithmetic of
+  // qrot_kernel (d / 8-term FMA chains over eight j-slices, added in slice
+  // order): q_rot and its split go to the workspace for the attention, the
+  // split rows also to LDS as this block's A operands.  The P column slice
+  // and q are requested first, together, then the first K batch.
+  const int J = d / 8, pc = tid % d, js = tid / d;
+  bf16_t pv[16];  // P[kv][js J + jj][pc], J <= 16
+  {
+    const bf16_t* Pc = P + (size_t)kv * d * d + pc;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) pv[jj] = Pc[(size_t)min(js * J + jj, d - 1) * d];  // clamped: always in bounds
+  }
+  float* sq = reinterpret_cast<float*>(lk);  // [2][d]
+  float* sred = sq + 2 * d;                  // [8][2][d]
+  if (tid < 2 * d) sq[tid] = to_f32(q[row0 * d + tid]);  // the pair's heads are adjacent rows
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);  // in flight during the rotation
+  {
+    __syncthreads();
+    if (js < 8) {
+      float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        if (jj < J) {
+          const int j = js * J + jj;
+          const float pj = to_f32(pv[jj]);
+          r0 = fmaf(sq[j], pj, r0);
+          r1 = fmaf(sq[d + j], pj, r1);
+        }
+      }
+      const int c = pc;
+      sred[(2 * js) * d + c] = r0;
+      sred[(2 * js + 1) * d + c] = r1;
+    }
+    __syncthreads();
+    if (tid < 2 * d) {
+      const int h = tid / d, cc = tid - h * d;
+      float v = sred[h * d + cc];
+      for (int t = 1; t < 8; ++t) v += sred[(2 * t + h) * d + cc];
+      qrot[(row0 + h) * d + cc] = v;
+      const bf16_t hi = f32_to_bf16(v);
+      const float e1 = v - to_f32(hi);
+      const bf16_t mid = f32_to_bf16(e1);
+      const bf16_t lo = f32_to_bf16(e1 - to_f32(mid));
+      const bf16_t part[4] = {hi, mid, lo, 0};
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        qsplit[((row0 + h) * 4 + pt) * d + cc] = part[pt];
+        sqs[(h * 4 + pt) * d + cc] = part[pt];
+      }
+    }
+    __syncthreads();
+  }
+
+  if (k >= S) {
+    keep_all<kPairThreads>(S, W, idx + row0 * k, bitmap + row0 * W);
+    keep_all<kPairThreads>(S, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
+    return;
+  }
+
+  // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qa[s] = q_rows(sqs, 0, d, 2, r, m, 32 * s + 8 * q4);
+
   // the key range of each head, gathered while the keys are made (the
   // selection then needs no pass of its own for it)
   uint32_t kmn = 0xffffffffu, kmx = 0u;
@@ -348,20 +403,18 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const uint4 x = 32 * s + 8 * q < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+        const uint4 x = 32 * s + 8 * q4 < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
       }
-      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q
-      if (q < 2 && t < S) {
+      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
+      if (q4 < 2 && t < S) {
         const uint32_t key = score_key(sum_split_rows(acc));
-        lk[q * Sp + t] = key;
+        lk[q4 * Sp + t] = key;
         kmn = min(kmn, key);
         kmx = max(kmx, key);
       }
     }
   };
-  uint4 a0[U][KS], a1[U][KS];
-  load_batch(0, a0);
   // the selection's scratch is cleared now, under the score phase
   for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
   for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
@@ -382,9 +435,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
     kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, x));
   }
-  if (m == 0 && q < 2) {
-    atomicMin(&smm[q][0], kmn);
-    atomicMax(&smm[q][1], kmx);
+  if (m == 0 && q4 < 2) {
+    atomicMin(&smm[q4][0], kmn);
+    atomicMax(&smm[q4][1], kmx);
   }
   __syncthreads();
   uint32_t key[2][T];
@@ -736,13 +789,15 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
 }
 
 bool score_select_pair_fits(const DecodePlan& p) {
-  return p.dt == 1 && p.G >= 2 && p.G % 2 == 0 && p.S <= kFusedMaxS && p.r <= 128;
+  return p.dt == 1 && p.G >= 2 && p.G % 2 == 0 && p.S <= kFusedMaxS && p.r <= 128 && p.d <= 128 && p.d % 8 == 0;
 }
 
-hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
-                                    int32_t* idx, uint32_t* bitmap, hipStream_t st) {
+hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
+                                    hipStream_t st) {
   if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
-  const size_t lds = 2 * (size_t)p.Sp * sizeof(uint32_t);
+  // keys [2][Sp], at least the rotation scratch [2 + 16][d] words
+  const size_t lds = (size_t)max(2 * p.Sp, 18 * p.d) * sizeof(uint32_t);
   const int ngroups = p.B * p.Hkv;
   const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
   const bf16_t* s = static_cast<const bf16_t*>(src);
@@ -753,7 +808,8 @@ hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_pair_kernel<K, 8 / K>),        \
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
     if (e != hipSuccess) return e;                                                                      \
-    hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K>), grid, block, lds, st, s, ld, qsplit, p.B, \
+    hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K>), grid, block, lds, st, s, ld,                \
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B,  \
                        p.Hq, p.Hkv, p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap);                       \
     break;
   switch (ks) {
