@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 // 1024 threads per pair of query heads of a (b, kv) group, one block per CU.
 // A CU's vector-memory path, not HBM, limits a kernel in which each query
 // head re-reads its group's source, so the pair shares one read: the MFMA A
-// operand carries both heads' split rows, the two heads' keys (2 x S words)
+// operand carries both heads' split rows, the two heads' scores (2 x S words)
 // go to LDS, and one two-head selection (select_regs2) keeps the k best of
 // each.  The G / 2 pairs of a group get block ids with the same value mod 8
 // (one XCD) and consecutive dispatch order, so their reads of the group's
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     int r, int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap) {
   constexpr int NWV = kPairThreads / 64;
   constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
-  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] keys (first: rotation scratch)
+  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
   __shared__ __align__(16) uint32_t sel[2][kNB];
   __shared__ uint32_t take[2][kFusedMaxS / 32];
   __shared__ SelScratch<kPairThreads> sh[2];
@@ -408,8 +408,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       }
       const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
       if (q4 < 2 && t < S) {
-        const uint32_t key = score_key(sum_split_rows(acc));
-        lk[q4 * Sp + t] = key;
+        const float sc = sum_split_rows(acc);
+        const uint32_t key = score_key(sc);
+        lk[q4 * Sp + t] = __float_as_uint(sc);  // the selection bins the value itself
         kmn = min(kmn, key);
         kmx = max(kmx, key);
       }

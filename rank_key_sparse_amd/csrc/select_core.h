@@ -107,11 +107,14 @@ struct Binner {
     scale = (float)kNB / range;
     degenerate = !(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f);
   }
-  __device__ __forceinline__ int operator()(uint32_t key) const {
+  // bin of a score value (the same map as of its key: key_score(score_key(s))
+  // is s, with -0 read as +0, which bins alike)
+  __device__ __forceinline__ int of_score(float s) const {
     if (degenerate) return 0;
-    const int b = (int)((key_score(key) - fmin) * scale);
+    const int b = (int)((s - fmin) * scale);
     return b < kNB - 1 ? b : kNB - 1;
   }
+  __device__ __forceinline__ int operator()(uint32_t key) const { return of_score(key_score(key)); }
 };
 
 // Block-wide min / max of per-thread partial extremes (one barrier: every
@@ -356,7 +359,10 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 }
 
 // ============================================================================
-// Two heads at once (same S, k, W; keys in registers as for select_regs):
+// Two heads at once (same S, k, W; scores in registers as for select_regs,
+// but as raw fp32 bits: bins come straight from the value, and the
+// order-preserving key is formed only where a total order is needed, for
+// the threshold bin's candidates and the radix tie path):
 // every step handles both heads between shared barriers, so a pair costs
 // the barriers and latencies of one selection.  Both histograms go through
 // one block scan with the two counts packed in 16-bit halves, which needs
@@ -366,7 +372,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 // separate per head.  Output per head as for select_regs (no map / okeys).
 // ============================================================================
 template <int NTHR, int T>
-__device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32_t* const (&lds)[2],
+__device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint32_t* const (&lds)[2],
                                              uint32_t* const (&take)[2], int S, int k, int W,
                                              int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
                                              SelScratch<NTHR>* const (&sh)[2],
@@ -375,8 +381,9 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32
   Binner bin[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) bin[h].init(kmm[h][0], kmm[h][1]);
+  auto key = [&](int h, int i) { return score_key(__uint_as_float(sbits[h][i])); };
 
-  // 1. both histograms; each key's bin stays in a register for step 2
+  // 1. both histograms; each score's bin stays in a register for step 2
   int kb[2][T];
   int nv = opaque(regs_valid<T>(S));
 #pragma unroll
@@ -384,7 +391,7 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32
 #pragma unroll
     for (int i = 0; i < T; ++i)
       if (i < nv) {
-        kb[h][i] = bin[h](key[h][i]);
+        kb[h][i] = bin[h].of_score(__uint_as_float(sbits[h][i]));
         atomicAdd(&lds[h][kb[h][i]], 1u);
       }
   __syncthreads();
@@ -438,7 +445,7 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32
       if (lane == i) { klo[h] = (uint32_t)mab; khi[h] = (uint32_t)(mab >> 32); }
       if (rank_path[h] && bj == tb[h]) {
         const int p = atomicAdd(&sh[h]->ccount, 1);
-        ck[p] = key[h][i];
+        ck[p] = key(h, i);
         ci[p] = (uint32_t)(tok0 + 64 * i);
       }
     }
@@ -477,8 +484,8 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32
       const int nvp = opaque(nv);
 #pragma unroll
       for (int i = 0; i < T; ++i)
-        if (i < nvp && kb[h][i] == tb[h] && (key[h][i] & pmask) == prefix)
-          atomicAdd(&hist[(key[h][i] >> sft) & dm], 1u);
+        if (i < nvp && kb[h][i] == tb[h] && (key(h, i) & pmask) == prefix)
+          atomicAdd(&hist[(key(h, i) >> sft) & dm], 1u);
       __syncthreads();
       find_threshold<NTHR>(hist, rem, *sh[h]);
       rem -= sh[h]->above;
@@ -491,16 +498,16 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&key)[2][T], uint32
     int neq = 0;
     const int nve = opaque(nv);
 #pragma unroll
-    for (int i = 0; i < T; ++i) neq += __popcll(__ballot(i < nve && key[h][i] == kstar));
+    for (int i = 0; i < T; ++i) neq += __popcll(__ballot(i < nve && key(h, i) == kstar));
     if (lane == 0) sh[h]->weq[wave] = neq;
     __syncthreads();
     int eqrun = waves_below<NTHR>(sh[h]->weq);
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       const bool valid = i < nve;
-      const bool eq = valid && key[h][i] == kstar;
+      const bool eq = valid && key(h, i) == kstar;
       const uint64_t eqm = __ballot(eq);
-      const bool tk = (valid && key[h][i] > kstar && kb[h][i] == tb[h]) ||
+      const bool tk = (valid && key(h, i) > kstar && kb[h][i] == tb[h]) ||
                       (eq && eqrun + bits_below(eqm) < quota);
       const uint64_t tm = __ballot(tk);
       if (lane == i) { klo[h] |= (uint32_t)tm; khi[h] |= (uint32_t)(tm >> 32); }
