@@ -229,11 +229,28 @@ def run(args) -> dict:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    headline = step
+    if args.graph:
+        # one HIP graph per cache copy (its kernels in one launch), replayed in turn
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for i in range(len(bufs)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(gr, stream=side):
+                    step(i)
+            graphs.append(gr)
+        torch.cuda.current_stream().wait_stream(side)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        headline = lambda i: graphs[i % len(graphs)].replay()  # noqa: E731
 
     # region A: the headline
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i)
+        headline(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
@@ -289,7 +306,8 @@ def run(args) -> dict:
         "config": {"workload": f"{cfg.name}: Llama-3-8B-shaped GQA decode" if cfg.name == "C3" else cfg.name,
                    "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.d,
                    "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k, "score_source":
-                   f"K_lead (R={R})" if R else "K_rot rows", "cache_copies_rotated": args.buffers},
+                   f"K_lead (R={R})" if R else "K_rot rows", "cache_copies_rotated": args.buffers,
+                   "launch": "HIP graph per step" if args.graph else "one call per step"},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "alg_bytes_per_step": by_step,
@@ -389,6 +407,102 @@ def run_project(args) -> dict:
     }
 
 
+def run_append(args) -> dict:
+    """One decode step's cache append (loki_append_kv): the new key of every
+    (b, kv) rotated into the basis and written with its value and lead dims
+    at the sequence's position, on the workload's caches."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(cfg)
+    P = x["P"].to(dev)
+    Kr, V = x["K_rot"].to(dev), x["V"].to(dev)
+    R = cfg.r if args.layout == "lead" else 0
+    Kl = Kr[..., :R].contiguous() if R else None
+    g = torch.Generator().manual_seed(9)
+    tdt = Kr.dtype
+    k_new = torch.randn((cfg.B, cfg.Hkv, cfg.d), generator=g).to(tdt).to(dev)
+    v_new = torch.randn((cfg.B, cfg.Hkv, cfg.d), generator=g).to(tdt).to(dev)
+    # each sequence appends at its own position (a ragged batch)
+    pos = torch.tensor([cfg.S - 1 - (b % 7) for b in range(cfg.B)], dtype=torch.int32, device=dev)
+
+    def step(i):
+        rks.loki_append_kv(k_new, v_new, P, pos, Kr, V, Kl)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # host-inclusive: one Python call per append (the launch, not the kernel, sets the pace)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    # device throughput: `steps` appends captured in one HIP graph, one replay timed by events
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(args.steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / args.steps
+    e = cfg.elem_bytes
+    rows = cfg.B * cfg.Hkv
+    # read k_new, v_new, P, pos; write the K_rot, V and K_lead rows
+    by = 2 * rows * cfg.d * e + cfg.Hkv * cfg.d * cfg.d * e + cfg.B * 4 + rows * (2 * cfg.d + R) * e
+    gbs = by / (us * 1e-6) / 1e9
+    # oracle: the same rotations in float64, single-threaded
+    import oracle
+    from threadpoolctl import threadpool_limits
+    kn, vn = k_new.cpu(), v_new.cpu()
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        n = 0
+        while n == 0 or time.perf_counter() - t < min(args.cpu_seconds, 3.0):
+            oracle.project(kn[:, :, None, :], x["P"])
+            n += 1
+        per_call = (time.perf_counter() - t) / n
+    want = oracle.project(kn[:, :, None, :], x["P"])[:, :, 0, :]
+    got = torch.stack([Kr[b, :, int(pos[b])] for b in range(cfg.B)]).double().cpu().numpy()
+    ok = bool(np.max(np.abs(got - want)) <= 2e-2) and bool(
+        torch.equal(torch.stack([V[b, :, int(pos[b])] for b in range(cfg.B)]).cpu(), vn))
+    return {
+        "metric": "cache append per decode step (rotated key, value, lead dims): appends/ms on the device",
+        "value": round(1e3 / us, 1), "unit": "appends/ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us * 1e-3, 5), "host_call_ms": round(ms, 5),
+        "timing": "one HIP graph of `steps` appends, replay timed by events", "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} cache append", "batch": cfg.B, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.d, "cached_tokens": cfg.S, "lead_dims": R},
+        "roofline": {"bound": "latency", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "append_kv_kernel",
+                     "alg_bytes_per_launch": by, "avg_launch_us": round(us, 2)},
+        "cpu_baseline": {"value": round(1e-3 / per_call, 4), "unit": "appends/ms", "cores": 1, "kind": "oracle",
+                         "sample": f"{n} calls of the float64 projection of the {rows} new keys",
+                         "gpu_matches_oracle": ok},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,8 +514,11 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--op", default="decode", choices=["decode", "project"],
-                    help="project: time the key projection instead (use --workload C5)")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: time steps replayed from HIP graphs (one launch per step)")
+    ap.add_argument("--op", default="decode", choices=["decode", "project", "append"],
+                    help="project: time the key projection instead (use --workload C5); "
+                         "append: time one decode step's cache append")
     ap.add_argument("--summarize-trace", metavar="DB")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
@@ -423,7 +540,7 @@ def main() -> int:
         for _ in range(3):
             torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-    res = run_project(args) if args.op == "project" else run(args)
+    res = {"project": run_project, "append": run_append}.get(args.op, run)(args)
     print(json.dumps(res))
     return 0
 

@@ -110,6 +110,29 @@ loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, vo
                                    loki_dtype dt, hipStream_t stream);
 
 /*
+ * Cache append for one decode step, the step before loki_decode in a decode
+ * loop (the AQUA page's preliminaries, eqs. 1-2: the new token's key and
+ * value join the cache before the scores; the Loki page keeps the cache in
+ * the rotated basis).  For every (b, kv) whose position is inside the cache:
+ *   K_rot[b,kv,pos[b],:]    = k_new[b,kv,:] P[kv]   (fp32 accumulation, one rounding)
+ *   V[b,kv,pos[b],:]        = v_new[b,kv,:]
+ *   K_lead[b,kv,pos[b],:R]  = the leading R dims of that K_rot row (if K_lead)
+ *   k_new, v_new [B, Hkv, d]; P [Hkv, d, d]; K_rot, V [B, Hkv, S, d];
+ *   K_lead [B, Hkv, S, R] or NULL (then R is ignored; else R as for
+ *   loki_project_keys_lead).
+ *   pos    DEVICE array of B int32 positions, one per sequence, so sequences
+ *          of different lengths each append at their own end.  A position
+ *          outside [0, S) writes nothing for that sequence (it is read on
+ *          the device, so it cannot be reported as an error).
+ * No other cache row is touched.  The rotated row equals loki_project_keys's
+ * up to the order of the fp32 additions.  No workspace.
+ */
+loki_status loki_append_kv(const void* k_new, const void* v_new, const void* P, const int32_t* pos,
+                           void* K_rot, void* V, void* K_lead, int32_t R,
+                           int32_t B, int32_t Hkv, int32_t S, int32_t d, loki_dtype dt,
+                           hipStream_t stream);
+
+/*
  * Bytes of device workspace needed by loki_decode, loki_decode_lead, loki_scores and
  * loki_attend for these sizes (0 if the sizes are invalid).  The same
  * workspace may be reused by successive calls on one stream.

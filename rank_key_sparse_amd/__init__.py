@@ -5,6 +5,7 @@ torch supplies device memory and the current HIP stream.  The entry points
 mirror the C ABI (``include/loki.h``) name for name:
 
 * :func:`loki_project_keys` -- ``K_rot = K P`` per key/value head;
+* :func:`loki_append_kv` -- one decode step's new key (rotated) and value written into the caches;
 * :func:`loki_decode` -- one Loki decode step -> ``(out, idx)``;
 * :func:`loki_scores`, :func:`loki_select_topk`, :func:`loki_attend` -- the
   decode stages alone (same kernels), for stage-level checks.
@@ -49,6 +50,7 @@ _SIGS = {
     "loki_status_str": ([ctypes.c_int], ctypes.c_char_p),
     "loki_project_keys": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P], ctypes.c_int),
     "loki_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I, ctypes.c_int], _Z),
+    "loki_append_kv": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P], ctypes.c_int),
     "loki_project_keys_lead": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int, _P], ctypes.c_int),
     "loki_decode": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
                     ctypes.c_int),
@@ -146,6 +148,34 @@ def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | No
     _check(lib.loki_project_keys_lead(_ptr(K), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, B, Hkv, S, d,
                                       _dtype_code(K), _stream(K)))
     return K_rot, K_lead
+
+
+def loki_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, P: torch.Tensor, pos: torch.Tensor,
+                   K_rot: torch.Tensor, V: torch.Tensor, K_lead: torch.Tensor | None = None) -> None:
+    """Writes one new token per (b, kv) into the caches in place:
+    ``K_rot[b, kv, pos[b]] = k_new[b, kv] @ P[kv]``, ``V[b, kv, pos[b]] = v_new[b, kv]``
+    and, with ``K_lead``, its leading ``R = K_lead.shape[-1]`` dims.  ``pos`` is an int32
+    device tensor [B]; positions outside [0, S) write nothing."""
+    _need(k_new, "k_new", ndim=3)
+    dev = k_new.device
+    _need(v_new, "v_new", dtype=k_new.dtype, ndim=3, device=dev)
+    _need(P, "P", dtype=k_new.dtype, ndim=3, device=dev)
+    _need(pos, "pos", dtype=torch.int32, ndim=1, device=dev)
+    _need(K_rot, "K_rot", dtype=k_new.dtype, ndim=4, device=dev)
+    _need(V, "V", dtype=k_new.dtype, ndim=4, device=dev)
+    B, Hkv, d = k_new.shape
+    S = K_rot.shape[2]
+    if tuple(v_new.shape) != (B, Hkv, d) or tuple(P.shape) != (Hkv, d, d) or tuple(pos.shape) != (B,) \
+            or tuple(K_rot.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d):
+        raise ValueError("shape mismatch: k_new, v_new [B,Hkv,d], P [Hkv,d,d], pos [B], K_rot, V [B,Hkv,S,d]")
+    R = 0
+    if K_lead is not None:
+        _need(K_lead, "K_lead", dtype=k_new.dtype, ndim=4, device=dev)
+        R = K_lead.shape[-1]
+        if tuple(K_lead.shape) != (B, Hkv, S, R):
+            raise ValueError("K_lead must be [B, Hkv, S, R]")
+    _check(load_library().loki_append_kv(_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(pos), _ptr(K_rot), _ptr(V),
+                                         _ptr(K_lead), R, B, Hkv, S, d, _dtype_code(k_new), _stream(k_new)))
 
 
 def loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dtype) -> int:

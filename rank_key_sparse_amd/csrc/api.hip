@@ -120,6 +120,21 @@ loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, vo
   }
 }
 
+loki_status loki_append_kv(const void* k_new, const void* v_new, const void* P, const int32_t* pos,
+                           void* K_rot, void* V, void* K_lead, int32_t R, int32_t B, int32_t Hkv, int32_t S,
+                           int32_t d, loki_dtype dt, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_project(k_new, P, K_rot, B, Hkv, S, d, dt));
+    if (!v_new || !pos || !V) return LOKI_ERR_NULL;
+    if (!aligned16(v_new) || !aligned16(V)) return LOKI_ERR_ALIGN;
+    if (K_lead) LOKI_TRY(check_lead(K_lead, R, d, 0, dt));
+    return from_hip(launch_append_kv(k_new, v_new, P, pos, K_rot, V, K_lead, K_lead ? R : 0, B, Hkv, S, d, (int)dt,
+                                     stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
 size_t loki_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
                                    int32_t r, int32_t k, loki_dtype dt) {
   if (check_dtype(dt) != LOKI_OK || check_sizes(B, Hq, Hkv, S, d) != LOKI_OK) return 0;

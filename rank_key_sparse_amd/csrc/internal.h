@@ -92,6 +92,9 @@ hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
                               const uint16_t* qsplit, const uint32_t* bitmap, float* part,
                               hipStream_t st);
+// Cache append: rotated key, value and lead dims of one new token per (b, kv).
+hipError_t launch_append_kv(const void* k_new, const void* v_new, const void* P, const int32_t* pos, void* K_rot,
+                            void* V, void* K_lead, int R, int B, int Hkv, int S, int d, int dt, hipStream_t st);
 hipError_t launch_project(const void* K, const void* P, void* K_rot, void* K_lead, int R, int B,
                           int Hkv, int S, int d, int dt, hipStream_t st);
 

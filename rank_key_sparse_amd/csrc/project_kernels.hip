@@ -166,6 +166,68 @@ static int blocks_per_group(long long groups, int tiles) {
   return (int)want;
 }
 
+// ============================================================================
+// Cache append for one decode step: the new key of every (b, kv) is rotated
+// into the basis and written at the sequence's position, with its value row
+// and lead dims.  One block of 1024 threads per (b, kv): thread (c, js)
+// sums k_new[j] P[kv][j][c] over the j-slice js (d / 8 terms, its P loads
+// issued together), the eight slice sums of column c are added in order, and
+// the row is rounded once.  Rows at other positions are not touched; a
+// position outside [0, S) writes nothing.
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(1024) void append_kv_kernel(const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                         const T* __restrict__ P, const int32_t* __restrict__ pos,
+                                                         T* __restrict__ K_rot, T* __restrict__ V,
+                                                         T* __restrict__ K_lead, int R, int Hkv, int S, int d) {
+  const int bk = blockIdx.x, b = bk / Hkv, kv = bk - b * Hkv;
+  const int p = pos[b];
+  if (p < 0 || p >= S) return;  // uniform over the block
+  __shared__ float sk[128];
+  __shared__ float sred[8][128];
+  const int tid = threadIdx.x, c = tid % d, js = tid / d, J = d / 8;
+  T pv[16];  // P[kv][js J + jj][c], clamped into the matrix (J <= 16)
+  const T* Pc = P + (size_t)kv * d * d + c;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) pv[jj] = Pc[(size_t)min(js * J + jj, d - 1) * d];
+  if (tid < d) sk[tid] = to_f32(k_new[(size_t)bk * d + tid]);
+  __syncthreads();
+  if (js < 8) {
+    float acc = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      if (jj < J) acc = fmaf(sk[js * J + jj], to_f32(pv[jj]), acc);
+    sred[js][c] = acc;
+  }
+  __syncthreads();
+  if (tid < d) {
+    float v = sred[0][tid];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) v += sred[t][tid];
+    const size_t row = (size_t)bk * S + p;
+    const T kr = from_f32<T>(v);
+    K_rot[row * d + tid] = kr;
+    V[row * d + tid] = v_new[(size_t)bk * d + tid];
+    if (K_lead && tid < R) K_lead[row * R + tid] = kr;
+  }
+}
+
+hipError_t launch_append_kv(const void* k_new, const void* v_new, const void* P, const int32_t* pos, void* K_rot,
+                            void* V, void* K_lead, int R, int B, int Hkv, int S, int d, int dt, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hkv)), block(1024);
+  if (dt == 1)
+    hipLaunchKernelGGL((append_kv_kernel<bf16_t>), grid, block, 0, st, static_cast<const bf16_t*>(k_new),
+                       static_cast<const bf16_t*>(v_new), static_cast<const bf16_t*>(P), pos,
+                       static_cast<bf16_t*>(K_rot), static_cast<bf16_t*>(V), static_cast<bf16_t*>(K_lead), R, Hkv,
+                       S, d);
+  else
+    hipLaunchKernelGGL((append_kv_kernel<float>), grid, block, 0, st, static_cast<const float*>(k_new),
+                       static_cast<const float*>(v_new), static_cast<const float*>(P), pos,
+                       static_cast<float*>(K_rot), static_cast<float*>(V), static_cast<float*>(K_lead), R, Hkv, S,
+                       d);
+  return hipGetLastError();
+}
+
 hipError_t launch_project(const void* K, const void* P, void* K_rot, void* K_lead, int R, int B,
                           int Hkv, int S, int d, int dt, hipStream_t st) {
   const long long groups = (long long)B * Hkv;

@@ -77,6 +77,25 @@ def test_project_rejects(lib):
     assert f(A, A, A, 1, 1, 8, 128, 3, NULLP) == DTYPE
 
 
+def test_append_rejects(lib):
+    f = lib.loki_append_kv
+    # (k_new, v_new, P, pos, K_rot, V, K_lead, R, B, Hkv, S, d, dt, stream)
+    for i in range(6):
+        args = [A] * 6
+        args[i] = NULLP
+        assert f(*args, NULLP, 0, 2, 2, 64, 128, BF16, NULLP) == NULL, i
+    assert f(A, A, A, A, A, A, NULLP, 0, 0, 2, 64, 128, BF16, NULLP) == SHAPE
+    assert f(A, A, A, A, A, A, NULLP, 0, 2, 2, 0, 128, BF16, NULLP) == SHAPE
+    assert f(A, A, A, A, A, A, NULLP, 0, 2, 2, 64, 96, BF16, NULLP) == UNSUPPORTED
+    assert f(A, MIS, A, A, A, A, NULLP, 0, 2, 2, 64, 128, BF16, NULLP) == ALIGN
+    assert f(A, A, A, A, A, MIS, NULLP, 0, 2, 2, 64, 128, BF16, NULLP) == ALIGN
+    assert f(A, A, A, A, A, A, A, 0, 2, 2, 64, 128, BF16, NULLP) == RANGE
+    assert f(A, A, A, A, A, A, A, 129, 2, 2, 64, 128, BF16, NULLP) == RANGE
+    assert f(A, A, A, A, A, A, A, 12, 2, 2, 64, 128, BF16, NULLP) == UNSUPPORTED
+    assert f(A, A, A, A, A, A, MIS, 32, 2, 2, 64, 128, BF16, NULLP) == ALIGN
+    assert f(A, A, A, A, A, A, NULLP, 0, 2, 2, 64, 128, 7, NULLP) == DTYPE
+
+
 def test_stage_entry_points_reject(lib):
     assert lib.loki_scores(A, A, A, NULLP, 1, 1, 1, 8, 64, 4, F32, A2, 1 << 20, NULLP) == NULL
     assert lib.loki_scores(A, A, A, A, 1, 1, 1, 8, 64, 65, F32, A2, 1 << 20, NULLP) == RANGE

@@ -224,6 +224,115 @@ def test_project_keys(gpu_lib, dt, d, kind):
     assert np.all(np.abs(g - exact) <= tol)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("lead", [False, True])
+def test_append_kv(gpu_lib, dt, d, lead):
+    # one decode step's new tokens written into the caches in place, at a
+    # per-sequence position; the last sequence's position is outside the cache
+    B, Hkv, S, R = 4, 3, 300, 32
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = torch.Generator().manual_seed(11 + d)
+    K_rot = torch.randn((B, Hkv, S, d), generator=g).to(tdt)
+    V = torch.randn((B, Hkv, S, d), generator=g).to(tdt)
+    k_new = torch.randn((B, Hkv, d), generator=g).to(tdt)
+    v_new = torch.randn((B, Hkv, d), generator=g).to(tdt)
+    from loki_inputs import make_basis
+    P = torch.from_numpy(np.stack([make_basis(d, 61, kv) for kv in range(Hkv)])).to(tdt)
+    pos = torch.tensor([0, 137, S - 1, S], dtype=torch.int32)
+    Kd, Vd = dev(K_rot), dev(V)
+    Ld = dev(K_rot[..., :R].contiguous()) if lead else None
+    gpu_lib.loki_append_kv(dev(k_new), dev(v_new), dev(P), dev(pos), Kd, Vd, Ld)
+    Kg, Vg = Kd.cpu(), Vd.cpu()
+    written = torch.zeros((B, Hkv, S), dtype=torch.bool)
+    for b in range(B):
+        if 0 <= int(pos[b]) < S:
+            written[b, :, int(pos[b])] = True
+    bits = (lambda t: t.view(torch.int16)) if dt == "bf16" else (lambda t: t)
+    # every other row is untouched, bit for bit
+    assert torch.equal(bits(Kg)[~written], bits(K_rot)[~written])
+    assert torch.equal(bits(Vg)[~written], bits(V)[~written])
+    exact = oracle.project(k_new[:, :, None, :], P)[:, :, 0, :]
+    acc_err = 2.0 * (d + 2) * U * oracle.project(k_new.abs()[:, :, None, :], P.abs())[:, :, 0, :]
+    tol = 2.0 ** -8 * (np.abs(exact) + acc_err) + acc_err if dt == "bf16" else acc_err + 1e-30
+    for b in range(B):
+        p = int(pos[b])
+        if not 0 <= p < S:
+            continue
+        got = Kg[b, :, p].double().numpy()
+        assert np.all(np.abs(got - exact[b]) <= tol[b])
+        assert torch.equal(bits(Vg[b, :, p]), bits(v_new[b]))
+    if lead:
+        assert torch.equal(bits(Ld.cpu()), bits(Kg[..., :R].contiguous()))
+
+
+def test_append_then_decode(gpu_lib):
+    # a short decode loop on a C3-shaped cache: append the step's token at the
+    # end of each sequence's filled prefix, then decode over the cache; every
+    # step agrees with the oracle on the cache the GPU wrote
+    cfg = cfg_case("C3", S=1024, B=2)
+    x = make_inputs(cfg)
+    q, P = dev(x["q"]), dev(x["P"])
+    Kd, Vd = dev(x["K_rot"]), dev(x["V"])
+    Ld = Kd[..., :cfg.r].contiguous()
+    g = torch.Generator().manual_seed(5)
+    for step in range(3):
+        k_new = torch.randn((cfg.B, cfg.Hkv, cfg.d), generator=g).to(torch.bfloat16)
+        v_new = torch.randn((cfg.B, cfg.Hkv, cfg.d), generator=g).to(torch.bfloat16)
+        pos = torch.tensor([cfg.S - 3 + step, cfg.S - 5 + step], dtype=torch.int32)
+        gpu_lib.loki_append_kv(dev(k_new), dev(v_new), P, dev(pos), Kd, Vd, Ld)
+        y = dict(x)
+        y["K_rot"], y["V"] = Kd.cpu(), Vd.cpu()
+        assert torch.equal(Ld.cpu(), y["K_rot"][..., :cfg.r].contiguous())
+        run_decode(gpu_lib, y, cfg.r, cfg.k, R=cfg.r)
+
+
+@pytest.mark.parametrize("shape", [
+    ("pair", "C3", dict(S=2048, B=16)),        # rotation + scores + selection fused per pair of heads
+    ("two_kernel", "C3", dict(S=4096, B=2)),   # rotation, scores, selection, attention kernels
+    ("mha_fused", "C2", dict(S=2048, B=8)),    # one block per MHA head for scores + selection
+], ids=lambda c: c[0])
+def test_decode_graph_replay(gpu_lib, shape):
+    # one decode step captured in a HIP graph: every replay equals the eager
+    # call, also after a new query is written into the captured input and
+    # with eager work on the outputs between replays
+    _, name, kw = shape
+    cfg = cfg_case(name, **kw)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    Kl = Kr[..., :cfg.r].contiguous()
+    nbytes = gpu_lib.loki_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.d, cfg.r, cfg.k, q.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    idx = torch.empty((cfg.B, cfg.Hq, cfg.k), dtype=torch.int32, device="cuda")
+    g = torch.Generator().manual_seed(21)
+    q2 = dev(torch.randn(q.shape, generator=g).to(q.dtype))
+    want = {}
+    for tag, qq in (("q", q.clone()), ("q2", q2)):
+        o, i = gpu_lib.loki_decode(qq, P, Kr, V, cfg.r, cfg.k, K_lead=Kl)
+        want[tag] = (o.clone(), i.clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, K_lead=Kl)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    q_orig = q.clone()
+    for rep, tag in enumerate(("q", "q", "q2", "q", "q2")):
+        q.copy_(q_orig if tag == "q" else q2)
+        out.zero_()
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o, i = want[tag]
+        assert torch.equal(idx, i), (rep, tag)
+        assert torch.equal(out.view(torch.int16), o.view(torch.int16)), (rep, tag)
+
+
 def test_project_then_decode_c5_shape(gpu_lib):
     # the prefill-plus-decode workload: the GPU projection agrees with the
     # oracle's projection element-wise, and decode over the oracle's
