@@ -11,5 +11,5 @@ attention, brute-force top-k on tiny inputs, closed forms); see the test file
 of oracle pins.
 """
 
-from .loki import (approx_scores, attend, decode, dense, project,  # noqa: F401
+from .loki import (approx_scores, attend, decode, decode_varlen, dense, project,  # noqa: F401
                    rotate_queries, select, topk_indices)

@@ -18,7 +18,8 @@ What is computed, and where the pages say so:
   resulting approximate scores rank the cached tokens, the best ones are kept
   for this step only (nothing is evicted), and attention runs over the kept
   tokens.  :func:`approx_scores`, :func:`select`, :func:`attend`,
-  :func:`decode`.
+  :func:`decode`; :func:`decode_varlen` for a batch of sequences of
+  different lengths (each one a decode over its own prefix).
 
 Readings taken where the pages leave a step open (each is listed with its
 reason in the design notes):
@@ -176,6 +177,34 @@ def decode(q, P, K_rot, V, r: int, k: int):
     """
     idx = select(q, P, K_rot, r, k)
     return attend(q, P, K_rot, V, idx), idx
+
+
+def decode_varlen(q, P, K_rot, V, lens, r: int, k: int, return_scores: bool = False):
+    """One Loki decode step over a ragged batch.
+
+    Sequence ``b`` holds only its first ``len_b`` cached tokens (``lens[b]``
+    clamped into ``[1, S]``); the rest of its cache rows are unused capacity
+    and take no part.  Each sequence is an ordinary decode over its own prefix
+    (the AQUA page's eqs. 1-5 on a cache of ``len_b`` tokens, Loki's selection
+    on it): the kept set is its ``min(k, len_b)`` best tokens, and ``idx``
+    rows of sequences shorter than ``k`` end with ``-1``.
+
+    Returns ``(out [B,Hq,d], idx [B,Hq,k])`` and, with ``return_scores``, the
+    approximate scores ``[B,Hq,S]`` with ``-inf`` past each sequence's end.
+    """
+    B, Hq, Hkv, S, d, G = _shapes(q, K_rot)
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    idx = np.full((B, Hq, k), -1, dtype=np.int64)
+    scores = np.full((B, Hq, S), -np.inf) if return_scores else None
+    for b in range(B):
+        L = min(max(int(lens[b]), 1), S)
+        kb = min(k, L)
+        sel, s = select(q[b:b + 1], P, K_rot[b:b + 1, :, :L], r, kb, return_scores=True)
+        out[b] = attend(q[b:b + 1], P, K_rot[b:b + 1, :, :L], V[b:b + 1, :, :L], sel)[0]
+        idx[b, :, :kb] = sel[0]
+        if return_scores:
+            scores[b, :, :L] = s[0]
+    return (out, idx, scores) if return_scores else (out, idx)
 
 
 def dense(q, K, V) -> np.ndarray:

@@ -271,3 +271,76 @@ def test_attend_closed_form_two_kept_tokens():
     w0 = 1.0 / (1.0 + math.exp(e2 - e0))
     want = np.array([w0, 1.0 - w0])
     assert np.max(np.abs(out[0, 0] - want)) <= 1e-15
+
+
+# ---------------------------------------------------------------- ragged batches
+# decode_varlen: each sequence of a batch is a decode over its own prefix of
+# the cache (the AQUA page's eqs. 1-5 on a cache of that many tokens).
+
+
+def test_varlen_keeping_everything_is_dense_on_each_prefix():
+    # k >= len_b: sequence b is dense attention over its first len_b tokens of
+    # the UNROTATED cache (eqs. 3-5 on the prefix); idx lists them, then -1.
+    # Catches attending over the whole capacity and wrong padding.
+    B, Hkv, G, S, d = 3, 2, 2, 20, 16
+    P = np.stack([make_basis(d, 31, kv) for kv in range(Hkv)])
+    q = _rand((B, Hkv * G, d), 40)
+    K = _rand((B, Hkv, S, d), 41)
+    V = _rand((B, Hkv, S, d), 42)
+    lens = [5, 20, 1]
+    k = 20
+    out, idx = oracle.decode_varlen(q, P, oracle.project(K, P), V, lens, r=4, k=k)
+    for b, L in enumerate(lens):
+        want = oracle.dense(q[b:b + 1], K[b:b + 1, :, :L], V[b:b + 1, :, :L])[0]
+        assert np.max(np.abs(out[b] - want)) <= 1e-12
+        assert np.array_equal(idx[b, :, :L], np.broadcast_to(np.arange(L), (Hkv * G, L)))
+        assert np.all(idx[b, :, L:] == -1)
+
+
+def test_varlen_ignores_rows_past_each_end():
+    # rows past a sequence's length are unused capacity: filling them with
+    # huge values changes nothing.  Catches scoring or attending past the end.
+    B, Hkv, G, S, d = 2, 1, 3, 40, 16
+    P = np.stack([make_basis(d, 32, kv) for kv in range(Hkv)])
+    q = _rand((B, Hkv * G, d), 43)
+    Kr = oracle.project(_rand((B, Hkv, S, d), 44), P)
+    V = _rand((B, Hkv, S, d), 45)
+    lens = [17, 33]
+    out1, idx1 = oracle.decode_varlen(q, P, Kr, V, lens, r=5, k=6)
+    Kr2, V2 = Kr.copy(), V.copy()
+    for b, L in enumerate(lens):
+        Kr2[b, :, L:] = 1e6 * _rand(Kr2[b, :, L:].shape, 46 + b)
+        V2[b, :, L:] = -1e6
+    out2, idx2 = oracle.decode_varlen(q, P, Kr2, V2, lens, r=5, k=6)
+    assert np.array_equal(idx1, idx2)
+    assert np.array_equal(out1, out2)
+
+
+def test_varlen_selection_is_brute_force_top_k_of_the_prefix():
+    # tiny prefix: the kept set is the subset of the prefix with the largest
+    # sum of leading-r scores (ties to lower indices), found by enumeration,
+    # with scores computed here from the definition q_rot[:r] . K_rot[j, :r]
+    d, r, S, L, k = 8, 3, 12, 7, 3
+    P = make_basis(d, 33, 0)[None]
+    q = _rand((1, 1, d), 47)
+    Kr = oracle.project(_rand((1, 1, S, d), 48), P)
+    Kr[0, 0, 2, :r] = Kr[0, 0, 5, :r]  # a planted exact tie inside the prefix
+    qr = q[0, 0] @ P[0]
+    s = [float(qr[:r] @ Kr[0, 0, j, :r]) for j in range(L)]
+    best = max(itertools.combinations(range(L), k), key=lambda c: (sum(s[j] for j in c), [-j for j in c]))
+    _, idx = oracle.decode_varlen(q, P, Kr, _rand((1, 1, S, d), 49), [L], r=r, k=k)
+    assert list(idx[0, 0]) == sorted(best)
+
+
+def test_varlen_full_lengths_equal_decode_and_lengths_are_clamped():
+    B, Hkv, G, S, d = 2, 2, 2, 25, 16
+    P = np.stack([make_basis(d, 34, kv) for kv in range(Hkv)])
+    q = _rand((B, Hkv * G, d), 50)
+    Kr = oracle.project(_rand((B, Hkv, S, d), 51), P)
+    V = _rand((B, Hkv, S, d), 52)
+    out, idx = oracle.decode(q, P, Kr, V, r=4, k=6)
+    out2, idx2 = oracle.decode_varlen(q, P, Kr, V, [S, S + 100], r=4, k=6)
+    assert np.array_equal(idx, idx2) and np.max(np.abs(out - out2)) <= 1e-12
+    out3, idx3 = oracle.decode_varlen(q, P, Kr, V, [0, -5], r=4, k=6)  # clamped to one token
+    assert np.all(idx3[:, :, 0] == 0) and np.all(idx3[:, :, 1:] == -1)
+    assert np.max(np.abs(out3 - V[:, np.repeat(np.arange(Hkv), G), 0])) <= 1e-15
