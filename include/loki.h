@@ -174,6 +174,26 @@ loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, co
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * loki_decode over a ragged batch: sequence b holds only its first lens[b]
+ * cached tokens (K_rot / K_lead / V rows past that are unused capacity and
+ * are neither read for scores nor kept).  Each sequence is a decode over its
+ * own prefix: its query heads keep their min(k, lens[b]) best tokens, and
+ * idx rows of sequences shorter than k end with -1 entries.
+ *   lens  DEVICE array of B int32 lengths, each clamped into [1, S] (read on
+ *         the device, so out-of-range values cannot be reported as errors).
+ *   K_lead may be NULL (scores from K_rot's rows; R ignored), else as for
+ *   loki_decode_lead.  S is the cache capacity; 1 <= k <= S as for
+ *   loki_decode.  Other arguments, workspace and errors as for
+ *   loki_decode_lead.  With every lens[b] = S the results are those of
+ *   loki_decode_lead (or loki_decode).
+ */
+loki_status loki_decode_varlen(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                               int32_t R, const void* V, const int32_t* lens, void* out, int32_t* idx,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
+                               int32_t r, int32_t k, loki_dtype dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Instrumented decode for measurement: exactly the work of loki_decode
  * (K_lead == NULL) or loki_decode_lead, plus hipEventRecord(events[i],
  * stream) at the stage boundaries:

@@ -56,6 +56,8 @@ _SIGS = {
                     ctypes.c_int),
     "loki_decode_lead": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
                           _P, _Z, _P], ctypes.c_int),
+    "loki_decode_varlen": ([_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
+                            _P, _Z, _P], ctypes.c_int),
     "loki_decode_profiled": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                               ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
     "loki_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
@@ -201,13 +203,15 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=None, K_lead=None,
-                events=None):
+                events=None, lens=None):
     """One Loki decode step.  Returns ``(out [B,Hq,d], idx [B,Hq,k] int32 ascending)``.
 
     With ``K_lead`` ([B,Hkv,S,R], the leading R >= r dims of K_rot) the
     approximate scores stream from it instead of from K_rot's rows.  With
     ``events`` (six recorded-once torch.cuda.Event objects) the instrumented
-    entry point records them at the stage boundaries.
+    entry point records them at the stage boundaries.  With ``lens`` (int32
+    [B] on the device) sequence b holds only its first ``lens[b]`` cached
+    tokens; idx rows of sequences shorter than k end with -1.
     """
     B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
     _need(V, "V", dtype=q.dtype, ndim=4, device=q.device)
@@ -227,7 +231,16 @@ def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=No
         _need(K_lead, "K_lead", dtype=q.dtype, ndim=4, device=q.device)
         if tuple(K_lead.shape[:3]) != (B, Hkv, S):
             raise ValueError("K_lead must be [B, Hkv, S, R]")
-    if events is not None:
+    if lens is not None:
+        _need(lens, "lens", dtype=torch.int32, ndim=1, device=q.device)
+        if lens.shape[0] != B:
+            raise ValueError("lens must be [B] int32")
+        if events is not None:
+            raise ValueError("lens and events cannot be combined")
+        _check(lib.loki_decode_varlen(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead),
+                                      0 if K_lead is None else K_lead.shape[3], _ptr(V), _ptr(lens), _ptr(out),
+                                      _ptr(idx), B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(), _stream(q)))
+    elif events is not None:
         if len(events) != 6:
             raise ValueError("events must hold 6 torch.cuda.Event objects")
         arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])

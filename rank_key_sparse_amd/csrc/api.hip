@@ -148,7 +148,8 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
                                int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
                                int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
                                loki_dtype dt, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream, hipEvent_t* ev = nullptr) {
+                               hipStream_t stream, hipEvent_t* ev = nullptr,
+                               const int32_t* lens = nullptr) {
   LOKI_TRY(check_dtype(dt));
   if (!q || !P || !K_rot || !V || !out || !idx) return LOKI_ERR_NULL;
   LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
@@ -160,6 +161,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   DecodePlan p;
   if (!make_decode_plan(p, B, Hq, Hkv, S, d, r, k, (int)dt)) return LOKI_ERR_INTERNAL;
   LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+  p.lens = lens;
   float* qrot = at<float>(workspace, p.off_qrot);
   uint16_t* qsplit = at<uint16_t>(workspace, p.off_qsplit);
   uint32_t* keys = at<uint32_t>(workspace, p.off_keys);
@@ -187,7 +189,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
     LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, mm, p.NSC, at<uint32_t>(workspace, p.off_masks),
                            idx, bitmap, stream, at<int32_t>(workspace, p.off_cidx),
-                           at<uint32_t>(workspace, p.off_ckey)));
+                           at<uint32_t>(workspace, p.off_ckey), lens, Hq));
   }
   if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
   LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
@@ -216,6 +218,20 @@ loki_status loki_decode_lead(const void* q, const void* P, const void* K_rot, co
     if (!K_lead) return LOKI_ERR_NULL;
     return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
                        workspace_bytes, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_varlen(const void* q, const void* P, const void* K_rot, const void* K_lead,
+                               int32_t R, const void* V, const int32_t* lens, void* out, int32_t* idx,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r,
+                               int32_t k, loki_dtype dt, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  try {
+    if (!lens) return LOKI_ERR_NULL;
+    return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream, nullptr, lens);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

@@ -50,6 +50,14 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
 
+// ---------------------------------------------------------------- ragged batches
+
+// Cached tokens of sequence b: its length clamped into [1, S], or the whole
+// capacity S when no lengths are given.
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int S) {
+  return lens ? min(max(lens[b], 1), S) : S;
+}
+
 // ---------------------------------------------------------------- score keys
 
 // Order-preserving map fp32 -> uint32: a < b (as reals) iff key(a) < key(b).

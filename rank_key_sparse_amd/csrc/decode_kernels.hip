@@ -109,13 +109,13 @@ __global__ __launch_bounds__(256) void score_kernel(const T* __restrict__ src,
                                                     void* __restrict__ out, int as_keys,
                                                     int out_stride, uint2* __restrict__ mm,
                                                     int Hq, int Hkv, int S, int d, int ld, int r,
-                                                    int SC) {
+                                                    int SC, const int32_t* __restrict__ lens) {
   constexpr int EPL = Gran<T>::N;
   constexpr int TPI = 256 / LPT;  // tokens per block pass
   constexpr int U = 8;            // passes whose loads are in flight together
   const int G = Hq / Hkv;
   const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
-  const int t0 = blockIdx.x * SC, t1 = min(S, t0 + SC);
+  const int t0 = blockIdx.x * SC, t1 = min(seq_len(lens, b, S), t0 + SC);  // tokens past the sequence: none
   const int gran = threadIdx.x % LPT, tsub = threadIdx.x / LPT;
 
   float qv[GT][EPL];
@@ -220,18 +220,20 @@ constexpr int kSelThreads = 1024;
 // T = 16 is held to 64 VGPRs so that two blocks share a CU.
 template <int T>
 __global__ __launch_bounds__(kSelThreads, T <= 16 ? 8 : 4) void select_regs_kernel(const uint32_t* __restrict__ keys,
-                                                                  int S, int Sp, int k, int W,
+                                                                  int Scap, int Sp, int k, int W,
                                                                   int32_t* __restrict__ idx,
-                                                                  uint32_t* __restrict__ bitmap) {
+                                                                  uint32_t* __restrict__ bitmap,
+                                                                  const int32_t* __restrict__ lens, int Hq) {
   __shared__ uint32_t lds[kNB];
   __shared__ uint32_t take[kSelThreads * T / 32];
   __shared__ SelScratch<kSelThreads> sh;
   const int row = blockIdx.x;
+  const int S = seq_len(lens, row / Hq, Scap);  // this head's tokens
   const uint32_t* rk = keys + (size_t)row * Sp;
   int32_t* orow = idx + (size_t)row * k;
   uint32_t* brow = bitmap + (size_t)row * W;
   if (k >= S) {
-    keep_all<kSelThreads>(S, W, orow, brow);
+    keep_all<kSelThreads>(S, k, W, orow, brow);
     return;
   }
   uint32_t key[T];
@@ -246,21 +248,26 @@ __global__ __launch_bounds__(kSelThreads, T <= 16 ? 8 : 4) void select_regs_kern
 // one block per head selects the top-k of its candidate list (position order
 // is token order, so ties still go to the lower token) and maps positions
 // back to tokens; the bitmap is rebuilt from idx afterwards.
-__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_t* __restrict__ keys, int S,
+__global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_t* __restrict__ keys, int Scap,
                                                                    int Sp, int k, int ldc,
                                                                    int32_t* __restrict__ cidx,
-                                                                   uint32_t* __restrict__ ckey) {
+                                                                   uint32_t* __restrict__ ckey,
+                                                                   const int32_t* __restrict__ lens, int Hq) {
   constexpr int T = kSelChunk / kSelThreads;
   __shared__ uint32_t lds[kNB];
   __shared__ uint32_t take[kSelChunk / 32];
   __shared__ SelScratch<kSelThreads> sh;
   const int row = blockIdx.y, c = blockIdx.x, base = c * kSelChunk;
-  const int L = min(kSelChunk, S - base);
+  const int S = seq_len(lens, row / Hq, Scap);  // this head's tokens
+  const int L = min(kSelChunk, S - base);        // may be <= 0 past the head's end
   const uint32_t* rk = keys + (size_t)row * Sp + base;
   int32_t* oi = cidx + (size_t)row * ldc + (size_t)c * k;
   uint32_t* ok = ckey + (size_t)row * ldc + (size_t)c * k;
-  if (L <= k) {  // the whole chunk is a candidate
-    for (int j = threadIdx.x; j < L; j += kSelThreads) { oi[j] = base + j; ok[j] = rk[j]; }
+  if (L <= k) {  // the whole chunk is a candidate; free slots get key 0, below every score's key
+    for (int j = threadIdx.x; j < k; j += kSelThreads) {
+      oi[j] = j < L ? base + j : -1;
+      ok[j] = j < L ? rk[j] : 0u;
+    }
     return;
   }
   uint32_t key[T];
@@ -272,11 +279,20 @@ template <int T>
 __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_t* __restrict__ ckey,
                                                                    const int32_t* __restrict__ cidx,
                                                                    int S2, int ldc, int k,
-                                                                   int32_t* __restrict__ idx) {
+                                                                   int32_t* __restrict__ idx,
+                                                                   const int32_t* __restrict__ lens, int Hq,
+                                                                   int Scap) {
   __shared__ uint32_t lds[kNB];
   __shared__ uint32_t take[kSelThreads * T / 32];
   __shared__ SelScratch<kSelThreads> sh;
   const int row = blockIdx.x;
+  const int S = seq_len(lens, row / Hq, Scap);
+  if (k >= S) {  // a short head keeps all its tokens (the bitmap is built from idx)
+    for (int j = threadIdx.x; j < k; j += kSelThreads) idx[(size_t)row * k + j] = j < S ? j : -1;
+    return;
+  }
+  // every chunk filled its k slots (free ones with key 0, below every score's
+  // key), and the head has more than k real candidates: none is chosen
   uint32_t key[T];
   load_regs<T>(ckey + (size_t)row * ldc, S2, key);
   select_regs<kSelThreads, T>(key, lds, take, S2, k, 2 * ((S2 + 63) / 64), idx + (size_t)row * k, nullptr, sh,
@@ -286,21 +302,25 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_
 __global__ __launch_bounds__(kSelThreads) void select_global_kernel(const uint32_t* __restrict__ keys,
                                                                     const uint2* __restrict__ mm,
                                                                     int nmm, uint32_t* __restrict__ gmasks,
-                                                                    int S, int Sp, int k, int W,
+                                                                    int Scap, int Sp, int k, int W,
                                                                     int32_t* __restrict__ idx,
-                                                                    uint32_t* __restrict__ bitmap) {
+                                                                    uint32_t* __restrict__ bitmap,
+                                                                    const int32_t* __restrict__ lens, int Hq) {
   __shared__ uint32_t hist[kNB];
   __shared__ SelScratch<kSelThreads> sh;
   const int row = blockIdx.x;
+  const int S = seq_len(lens, row / Hq, Scap);  // this head's tokens
   int32_t* orow = idx + (size_t)row * k;
   uint32_t* brow = bitmap + (size_t)row * W;
   if (k >= S) {
-    keep_all<kSelThreads>(S, W, orow, brow);
+    keep_all<kSelThreads>(S, k, W, orow, brow);
     return;
   }
   for (int i = threadIdx.x; i < kNB; i += kSelThreads) hist[i] = 0u;
   select_head<kSelThreads>(keys + (size_t)row * Sp, mm + (size_t)row * nmm, nmm, hist,
                            gmasks + (size_t)row * (Sp / 16), S, Sp, k, orow, brow, sh);
+  // bitmap words past the head's last 64-token step (a shorter sequence)
+  for (int w = 2 * ((S + 63) >> 6) + threadIdx.x; w < W; w += kSelThreads) brow[w] = 0u;
 }
 
 // Caller-given kept sets -> bitmap (stand-alone attention entry point).
@@ -674,7 +694,7 @@ static hipError_t scores_tg(const DecodePlan& p, const void* src, int ld, const 
 #define LOKI_SCORE(L)                                                                         \
   case L:                                                                                     \
     hipLaunchKernelGGL((score_kernel<T, L, GT>), grid, block, 0, st, K, qrot, out, ak,       \
-                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                     \
+                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC, p.lens);             \
     break;
   switch (lpt) {
     LOKI_SCORE(1)
@@ -705,42 +725,41 @@ bool select_needs_minmax(int S) { return S > kSelThreads * kSelRegMaxT; }
 size_t select_chunked_ldc(int S, int k) {
   if (S <= kSelThreads * kSelRegMaxT || k > kSelChunk) return 0;
   const int C = (S + kSelChunk - 1) / kSelChunk;
-  const int last = S - (C - 1) * kSelChunk;
-  const long long S2 = (long long)(C - 1) * k + (last < k ? last : k);
+  const long long S2 = (long long)C * k;  // every chunk fills k candidate slots
   if (S2 > (long long)kSelThreads * kSelRegMaxT) return 0;
-  return (size_t)C * k;
+  return (size_t)S2;
 }
 
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
                          int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
-                         int32_t* cidx, uint32_t* ckey) {
+                         int32_t* cidx, uint32_t* ckey, const int32_t* lens, int Hq) {
+  if (!lens) Hq = 1;  // any divisor: without lengths every row has S tokens
   const size_t ldc = select_chunked_ldc(S, k);
   if (ldc && k < S) {
     if (!cidx || !ckey) return hipErrorInvalidValue;
     const int C = (S + kSelChunk - 1) / kSelChunk;
-    const int last = S - (C - 1) * kSelChunk;
-    const int S2 = (C - 1) * k + (last < k ? last : k);
+    const int S2 = (int)ldc;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(C, rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, (int)ldc,
-                       cidx, ckey);
+                       cidx, ckey, lens, Hq);
     if (S2 <= kSelThreads * 16)
       hipLaunchKernelGGL((select_merge_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, S2,
-                         (int)ldc, k, idx);
+                         (int)ldc, k, idx, lens, Hq, S);
     else
       hipLaunchKernelGGL((select_merge_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx,
-                         S2, (int)ldc, k, idx);
+                         S2, (int)ldc, k, idx, lens, Hq, S);
     hipLaunchKernelGGL(idx_to_bitmap_kernel, dim3(rows), dim3(256), 0, st, idx, bitmap, S, k, W);
     return hipGetLastError();
   }
   if (S <= kSelThreads * 16) {
     hipLaunchKernelGGL((select_regs_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
-                       idx, bitmap);
+                       idx, bitmap, lens, Hq);
   } else if (S <= kSelThreads * kSelRegMaxT) {
     hipLaunchKernelGGL((select_regs_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, keys, S,
-                       Sp, k, W, idx, bitmap);
+                       Sp, k, W, idx, bitmap, lens, Hq);
   } else {
     if (!mm || !gmasks) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_global_kernel, dim3(rows), dim3(kSelThreads), 0, st, keys, mm, nmm, gmasks,
-                       S, Sp, k, W, idx, bitmap);
+                       S, Sp, k, W, idx, bitmap, lens, Hq);
   }
   return hipGetLastError();
 }

@@ -29,6 +29,9 @@ struct DecodePlan {
   // extremes [row][NSC] (uint2 min, max), selection masks [row][Sp/16] (used
   // when a row's keys do not fit in LDS), bitmap [row][W], attention partials
   size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_cidx, off_ckey, off_bitmap, off_part, bytes;
+  // per-sequence lengths [B] on the device (each clamped into [1, S]), or
+  // null: every sequence holds S tokens
+  const int32_t* lens = nullptr;
 };
 
 // Fills `p` from the sizes; returns false if they are out of the supported range
@@ -65,7 +68,8 @@ bool select_needs_minmax(int S);
 size_t select_chunked_ldc(int S, int k);
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
                          int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
-                         int32_t* cidx = nullptr, uint32_t* ckey = nullptr);
+                         int32_t* cidx = nullptr, uint32_t* ckey = nullptr, const int32_t* lens = nullptr,
+                         int Hq = 1);
 hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, uint2* mm, int nmm, int rows,
                                  int S, int Sp, hipStream_t st);
 hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,

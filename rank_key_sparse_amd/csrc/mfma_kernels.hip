@@ -115,13 +115,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
                                                          const uint16_t* __restrict__ qsplit,
                                                          void* __restrict__ out, int out_stride,
                                                          uint2* __restrict__ mm, int Hq, int Hkv,
-                                                         int S, int d, int ld, int r, int SC) {
+                                                         int S, int d, int ld, int r, int SC,
+                                                         const int32_t* __restrict__ lens) {
   constexpr int NGRP = (GT + 3) / 4;
   constexpr int UK = 8 / (KS * NGRP);
   constexpr int U = UK < 1 ? 1 : UK;  // tiles per batch and wave
   const int G = Hq / Hkv;
   const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
-  const int t0 = blockIdx.x * SC, t1 = min(S, t0 + SC);
+  // tokens of this chunk that the sequence holds (none past its end: the
+  // clamped loads below then repeat its last token and nothing is stored)
+  const int t0 = blockIdx.x * SC, t1 = min(seq_len(lens, b, S), t0 + SC);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
@@ -139,11 +142,11 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
   uint32_t mn[NGRP], mx[NGRP];
 #pragma unroll
   for (int grp = 0; grp < NGRP; ++grp) { mn[grp] = 0xffffffffu; mx[grp] = 0u; }
-  const int nbat = ((t1 - t0 + 15) / 16 + 4 * U - 1) / (4 * U);
+  const int nbat = t1 > t0 ? ((t1 - t0 + 15) / 16 + 4 * U - 1) / (4 * U) : 0;
   auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = min(t0 + 16 * (wave + 4 * (bi * U + u)) + m, t1 - 1);
+      const int t = min(t0 + 16 * (wave + 4 * (bi * U + u)) + m, t1 - 1);  // t1 >= 1
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
     }
@@ -211,8 +214,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
 template <int KS>
 __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
     const bf16_t* __restrict__ src, int ld, const uint16_t* __restrict__ qsplit, int B, int Hq,
-    int Hkv, int S, int Sp, int d, int r, int k, int W, int32_t* __restrict__ idx,
-    uint32_t* __restrict__ bitmap) {
+    int Hkv, int Scap, int Sp, int d, int r, int k, int W, int32_t* __restrict__ idx,
+    uint32_t* __restrict__ bitmap, const int32_t* __restrict__ lens) {
   constexpr int NWV = kFusedThreads / 64;
   constexpr int UK = 8 / KS;
   constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
@@ -226,6 +229,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
   const int gh = slot % G, gi = (slot / G) * 8 + xcd;
   if (gi >= B * Hkv) return;  // padding block (uniform)
   const int b = gi / Hkv, kv = gi - b * Hkv;
+  const int S = seq_len(lens, b, Scap);  // this sequence's tokens
   const size_t row = (size_t)b * Hq + (size_t)kv * G + gh;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, q = lane >> 4;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
   uint32_t* brow = bitmap + row * W;
 
   if (k >= S) {
-    keep_all<kFusedThreads>(S, W, orow, brow);
+    keep_all<kFusedThreads>(S, k, W, orow, brow);
     return;
   }
 
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 
   // tiles of 16 tokens, wave w takes tiles w + NWV i in double-buffered
   // batches of U; unconditional loads as in score_mfma_kernel
-  const bf16_t* base = src + (size_t)gi * S * ld;
+  const bf16_t* base = src + (size_t)gi * Scap * ld;  // rows of the cache (capacity Scap)
   const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
   auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
 #pragma unroll
@@ -295,8 +299,9 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 template <int KS, int U>
 __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P,
-    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int S, int Sp, int d,
-    int r, int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap) {
+    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int Scap, int Sp, int d,
+    int r, int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap,
+    const int32_t* __restrict__ lens) {
   constexpr int NWV = kPairThreads / 64;
   constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
   extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
   if (gi >= B * Hkv) return;  // padding block (uniform)
   const int b = gi / Hkv, kv = gi - b * Hkv;
+  const int S = seq_len(lens, b, Scap);  // this sequence's tokens
   const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = lane & 15, q4 = lane >> 4;
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   // Loads are unconditional (token clamped to S - 1, dims to the row) so
   // that each tile waits only for its own data; dims >= r are zeroed at the
   // MFMA, tiles past S are dropped at the store.
-  const bf16_t* base = src + (size_t)gi * S * ld;
+  const bf16_t* base = src + (size_t)gi * Scap * ld;  // rows of the cache (capacity Scap)
   const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
   auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
 #pragma unroll
@@ -384,8 +390,8 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   }
 
   if (k >= S) {
-    keep_all<kPairThreads>(S, W, idx + row0 * k, bitmap + row0 * W);
-    keep_all<kPairThreads>(S, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
+    keep_all<kPairThreads>(S, k, W, idx + row0 * k, bitmap + row0 * W);
+    keep_all<kPairThreads>(S, k, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
     return;
   }
 
@@ -729,7 +735,7 @@ static hipError_t score_mfma_g(const DecodePlan& p, const void* src, int ld, con
 #define LOKI_SM(K)                                                                                 \
   case K:                                                                                          \
     hipLaunchKernelGGL((score_mfma_kernel<GT, K, KEYS>), grid, block, 0, st, s, qsplit, out,       \
-                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC);                      \
+                       out_stride, mm, p.Hq, p.Hkv, p.S, p.d, ld, p.r, p.SC, p.lens);              \
     break;
   switch (ks) {
     LOKI_SM(1)
@@ -776,7 +782,7 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                     \
     if (e != hipSuccess) return e;                                                                     \
     hipLaunchKernelGGL((score_select_kernel<K>), grid, block, lds, st, s, ld, qsplit, p.B, p.Hq, p.Hkv, \
-                       p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap);                                    \
+                       p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap, p.lens);                            \
     break;
   switch (ks) {
     LOKI_SS(1)
@@ -811,7 +817,7 @@ hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld
     if (e != hipSuccess) return e;                                                                      \
     hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K>), grid, block, lds, st, s, ld,                \
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B,  \
-                       p.Hq, p.Hkv, p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap);                       \
+                       p.Hq, p.Hkv, p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap, p.lens);               \
     break;
   switch (ks) {
     LOKI_SP(1)

@@ -134,10 +134,11 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, SelScratc
   kmax = b;
 }
 
-// Writes idx (ascending) and the kept-token bitmap when every token is kept.
+// Writes idx (ascending) and the kept-token bitmap when every one of the S
+// tokens is kept (k >= S); idx entries S .. k - 1 are -1.
 template <int NTHR>
-__device__ __forceinline__ void keep_all(int S, int W, int32_t* orow, uint32_t* brow) {
-  for (int j = threadIdx.x; j < S; j += NTHR) orow[j] = j;
+__device__ __forceinline__ void keep_all(int S, int k, int W, int32_t* orow, uint32_t* brow) {
+  for (int j = threadIdx.x; j < k; j += NTHR) orow[j] = j < S ? j : -1;
   for (int w = threadIdx.x; w < W; w += NTHR) {
     const int lo = 32 * w;
     brow[w] = (lo + 32 <= S) ? 0xffffffffu : (lo >= S ? 0u : ((1u << (S - lo)) - 1u));

@@ -96,6 +96,17 @@ def test_append_rejects(lib):
     assert f(A, A, A, A, A, A, NULLP, 0, 2, 2, 64, 128, 7, NULLP) == DTYPE
 
 
+def test_decode_varlen_rejects(lib):
+    f = lib.loki_decode_varlen
+    # (q, P, K_rot, K_lead, R, V, lens, out, idx, B, Hq, Hkv, S, d, r, k, dt, ws, wsb, stream)
+    assert f(A, A, A, NULLP, 0, A, NULLP, A, A, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 1 << 30, NULLP) == NULL
+    assert f(NULLP, A, A, NULLP, 0, A, A, A, A, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 1 << 30, NULLP) == NULL
+    assert f(A, A, A, NULLP, 0, A, A, A, A, 1, 4, 2, 100, 128, 8, 101, BF16, A2, 1 << 30, NULLP) == RANGE
+    assert f(A, A, A, A, 4, A, A, A, A, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 1 << 30, NULLP) == RANGE
+    assert f(A, A, A, NULLP, 0, A, A, A, A, 1, 5, 2, 100, 128, 8, 10, BF16, A2, 1 << 30, NULLP) == SHAPE
+    assert f(A, A, A, NULLP, 0, A, A, A, A, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 16, NULLP) == WORKSPACE
+
+
 def test_stage_entry_points_reject(lib):
     assert lib.loki_scores(A, A, A, NULLP, 1, 1, 1, 8, 64, 4, F32, A2, 1 << 20, NULLP) == NULL
     assert lib.loki_scores(A, A, A, A, 1, 1, 1, 8, 64, 65, F32, A2, 1 << 20, NULLP) == RANGE

@@ -333,6 +333,80 @@ def test_decode_graph_replay(gpu_lib, shape):
         assert torch.equal(out.view(torch.int16), o.view(torch.int16)), (rep, tag)
 
 
+def run_decode_varlen(rks, x, lens, r, k, R=None):
+    """GPU decode over a ragged batch against the oracle's (each sequence a
+    decode over its own prefix), with the tie-band rule on each prefix."""
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    K_lead = Kr[..., :R].contiguous() if R else None
+    out_g, idx_g = rks.loki_decode(q, P, Kr, V, r=r, k=k, K_lead=K_lead,
+                                   lens=dev(torch.tensor(lens, dtype=torch.int32)))
+    torch.cuda.synchronize()
+    out_o, idx_o, s_o = oracle.decode_varlen(x["q"], x["P"], x["K_rot"], x["V"], lens, r, k, return_scores=True)
+    ig = idx_g.cpu().numpy().astype(np.int64)
+    S = Kr.shape[2]
+    B, Hq, _ = ig.shape
+    differ = []
+    for b in range(B):
+        L = min(max(int(lens[b]), 1), S)
+        kb = min(k, L)
+        assert np.all(ig[b, :, kb:] == -1), f"sequence {b}: entries past {kb} must be -1"
+        rows = check_index_sets(ig[b:b + 1, :, :kb], idx_o[b:b + 1, :, :kb], s_o[b:b + 1, :, :L], kb)
+        differ += [(b, h) for _, h in rows]
+    tol = OUT_TOL[x["q"].dtype]
+    og = as_np(out_g)
+    same = np.ones(og.shape[:2], dtype=bool)
+    for b, h in differ:
+        same[b, h] = False
+    err = float(np.max(np.abs(og - out_o)[same])) if same.any() else 0.0
+    assert err <= tol, f"output max-abs {err} > {tol}"
+    if differ:
+        again = rks.loki_attend(q, P, Kr, V, idx_g)
+        on_o = rks.loki_attend(q, P, Kr, V, torch.from_numpy(idx_o.astype(np.int32)).to("cuda"))
+        for b, h in differ:
+            assert torch.equal(again[b, h], out_g[b, h])
+            assert max_abs(on_o[b, h], out_o[b, h]) <= tol
+    return out_g, idx_g
+
+
+VARLEN = [
+    # (label, B, Hq, Hkv, S, d, dtype, r, k, R) -- the dispatch path each one takes
+    ("pair_fused", 16, 32, 8, 2048, 128, "bf16", 32, 100, 32),
+    ("mha_fused", 16, 16, 16, 1500, 128, "bf16", 24, 77, None),
+    ("regs16_two_kernel", 9, 8, 2, 4000, 128, "bf16", 32, 300, 32),
+    ("regs32_two_kernel", 9, 4, 2, 20000, 64, "bf16", 16, 700, None),
+    ("chunked", 9, 4, 2, 40000, 128, "bf16", 16, 1500, 16),
+    ("global", 9, 2, 1, 40000, 64, "bf16", 16, 20000, None),
+    ("f32", 9, 6, 2, 1200, 64, "f32", 8, 50, None),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_decode_varlen(gpu_lib, case):
+    label, B, Hq, Hkv, S, d, dt, r, k, R = case
+    print(f"\n[varlen {label}] B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} {dt} r={r} k={k} R={R}", flush=True)
+    cfg = CONFIGS["C3"].replace(name=label, cfg_no=51, B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, dtype=dt, r=r, k=k)
+    x = make_inputs(cfg)
+    base = [S, 1, k - 1, k, k + 1, S - 1, S // 2 + 3, 2 * S, 0]
+    lens = [base[b % len(base)] for b in range(B)]
+    g = np.random.default_rng(7)
+    for b in range(len(base), B):
+        lens[b] = int(g.integers(1, S + 1))
+    run_decode_varlen(gpu_lib, x, lens, r, k, R=R)
+
+
+def test_decode_varlen_full_lengths_match_decode(gpu_lib):
+    # every sequence full: bit-identical to the plain decode on the same path
+    cfg = cfg_case("C3", S=2048, B=16)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    Kl = Kr[..., :cfg.r].contiguous()
+    o1, i1 = gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k, K_lead=Kl)
+    o2, i2 = gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k, K_lead=Kl,
+                                 lens=dev(torch.full((cfg.B,), cfg.S, dtype=torch.int32)))
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
 def test_project_then_decode_c5_shape(gpu_lib):
     # the prefill-plus-decode workload: the GPU projection agrees with the
     # oracle's projection element-wise, and decode over the oracle's
