@@ -130,19 +130,27 @@ def load_traffic(workload: str, kernel_name: str):
 
 
 def union_rows(idx, G: int) -> int:
-    """Number of distinct kept tokens per (b, kv) group, summed."""
+    """Number of distinct kept tokens per (b, kv) group, summed (the -1
+    padding of sequences shorter than k not counted)."""
     import torch
     B, Hq, k = idx.shape
     Hkv = Hq // G
     grp = idx.view(B, Hkv, G * k).to(torch.int64)
     srt, _ = torch.sort(grp, dim=-1)
-    distinct = 1 + (srt[..., 1:] != srt[..., :-1]).sum(dim=-1)
+    distinct = 1 + (srt[..., 1:] != srt[..., :-1]).sum(dim=-1) - (srt[..., 0] < 0).to(torch.int64)
     return int(distinct.sum().item())
 
 
-def cpu_baseline(x, cfg, out_gpu, idx_gpu, seconds: float):
+def ragged_lengths(B: int, S: int):
+    """Per-sequence cache lengths of the ragged mode: spread evenly from S down
+    to a little over S/2."""
+    return [S - (b * S) // (2 * B) for b in range(B)]
+
+
+def cpu_baseline(x, cfg, out_gpu, idx_gpu, seconds: float, lens=None):
     """The float64 oracle, one thread, on whole batch elements until `seconds`
-    of CPU work; also checks the GPU result on that sample."""
+    of CPU work; also checks the GPU result on that sample.  With `lens` each
+    element is a decode over its own cache prefix."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -156,8 +164,12 @@ def cpu_baseline(x, cfg, out_gpu, idx_gpu, seconds: float):
             b = done % cfg.B
             sl = {n: x[n][b:b + 1] for n in ("q", "K_rot", "V")}
             t = time.perf_counter()
-            idx_o, s_o = oracle.select(sl["q"], x["P"], sl["K_rot"], cfg.r, cfg.k, return_scores=True)
-            out_o = oracle.attend(sl["q"], x["P"], sl["K_rot"], sl["V"], idx_o)
+            if lens is None:
+                idx_o, s_o = oracle.select(sl["q"], x["P"], sl["K_rot"], cfg.r, cfg.k, return_scores=True)
+                out_o = oracle.attend(sl["q"], x["P"], sl["K_rot"], sl["V"], idx_o)
+            else:
+                out_o, idx_o, s_o = oracle.decode_varlen(sl["q"], x["P"], sl["K_rot"], sl["V"], lens[b:b + 1],
+                                                         cfg.r, cfg.k, return_scores=True)
             t_used += time.perf_counter() - t
             if done < cfg.B:  # first pass over the batch: confirm the GPU result
                 try:
@@ -221,10 +233,13 @@ def run(args) -> dict:
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     idx = torch.empty((cfg.B, cfg.Hq, cfg.k), dtype=torch.int32, device=dev)
+    lens_h = ragged_lengths(cfg.B, cfg.S) if args.ragged else None
+    lens = None if lens_h is None else torch.tensor(lens_h, dtype=torch.int32, device=dev)
 
     def step(i, events=None):
         Kr, V, Kl = bufs[i % len(bufs)]
-        rks.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, K_lead=Kl, events=events)
+        rks.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, K_lead=Kl, events=events,
+                        lens=lens)
 
     for i in range(args.warmup):
         step(i)
@@ -274,7 +289,8 @@ def run(args) -> dict:
     # algorithmic bytes (what the method must move; intermediates excluded)
     e = cfg.elem_bytes
     U = union_rows(idx, cfg.G)
-    by_prefix = cfg.B * cfg.Hkv * cfg.S * cfg.r * e
+    tokens = cfg.B * cfg.S if lens_h is None else sum(lens_h)
+    by_prefix = tokens * cfg.Hkv * cfg.r * e
     by_gather = U * cfg.d * 2 * e
     by_step = by_prefix + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
         + cfg.B * cfg.Hq * cfg.k * 4
@@ -307,7 +323,9 @@ def run(args) -> dict:
                    "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv, "head_dim": cfg.d,
                    "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k, "score_source":
                    f"K_lead (R={R})" if R else "K_rot rows", "cache_copies_rotated": args.buffers,
-                   "launch": "HIP graph per step" if args.graph else "one call per step"},
+                   "launch": "HIP graph per step" if args.graph else "one call per step",
+                   "lengths": "full" if lens_h is None else
+                   f"ragged {lens_h[0]}..{lens_h[-1]} (mean {sum(lens_h) / len(lens_h):.0f})"},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "alg_bytes_per_step": by_step,
@@ -318,7 +336,8 @@ def run(args) -> dict:
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(x, cfg, out.float().cpu().numpy().astype(np.float64),
-                                           idx.cpu().numpy(), args.cpu_seconds)
+                                           idx.cpu().numpy(), args.cpu_seconds,
+                                           None if lens_h is None else np.array(lens_h))
     else:
         res["cpu_baseline"] = None
     return res
@@ -514,6 +533,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--ragged", action="store_true",
+                    help="decode a ragged batch: per-sequence cache lengths from S down to about S/2")
     ap.add_argument("--graph", action="store_true",
                     help="decode: time steps replayed from HIP graphs (one launch per step)")
     ap.add_argument("--op", default="decode", choices=["decode", "project", "append"],

@@ -195,8 +195,9 @@ loki_status loki_decode_varlen(const void* q, const void* P, const void* K_rot, 
 
 /*
  * Instrumented decode for measurement: exactly the work of loki_decode
- * (K_lead == NULL) or loki_decode_lead, plus hipEventRecord(events[i],
- * stream) at the stage boundaries:
+ * (K_lead == NULL) or loki_decode_lead (lens == NULL) or loki_decode_varlen
+ * (lens given), plus hipEventRecord(events[i], stream) at the stage
+ * boundaries:
  *   [0] before the query rotation    [1] after it
  *   [2] after the approximate scores [3] after the top-k selection
  *   [4] after exact attention        [5] after the partial merge (the end)
@@ -204,7 +205,7 @@ loki_status loki_decode_varlen(const void* q, const void* P, const void* K_rot, 
  * any is NULL).  Other arguments and errors as for loki_decode_lead.
  */
 loki_status loki_decode_profiled(const void* q, const void* P, const void* K_rot, const void* K_lead,
-                                 int32_t R, const void* V, void* out, int32_t* idx,
+                                 int32_t R, const void* V, const int32_t* lens, void* out, int32_t* idx,
                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d,
                                  int32_t r, int32_t k, loki_dtype dt,
                                  void* workspace, size_t workspace_bytes,

@@ -58,7 +58,7 @@ _SIGS = {
                           _P, _Z, _P], ctypes.c_int),
     "loki_decode_varlen": ([_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
                             _P, _Z, _P], ctypes.c_int),
-    "loki_decode_profiled": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+    "loki_decode_profiled": ([_P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                               ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
     "loki_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_select_workspace_bytes": ([_I, _I, _I], _Z),
@@ -235,19 +235,18 @@ def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=No
         _need(lens, "lens", dtype=torch.int32, ndim=1, device=q.device)
         if lens.shape[0] != B:
             raise ValueError("lens must be [B] int32")
-        if events is not None:
-            raise ValueError("lens and events cannot be combined")
-        _check(lib.loki_decode_varlen(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead),
-                                      0 if K_lead is None else K_lead.shape[3], _ptr(V), _ptr(lens), _ptr(out),
-                                      _ptr(idx), B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(), _stream(q)))
-    elif events is not None:
+    if events is not None:
         if len(events) != 6:
             raise ValueError("events must hold 6 torch.cuda.Event objects")
         arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])
         _check(lib.loki_decode_profiled(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead),
-                                        0 if K_lead is None else K_lead.shape[3], _ptr(V), _ptr(out),
-                                        _ptr(idx), B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(),
+                                        0 if K_lead is None else K_lead.shape[3], _ptr(V), _ptr(lens),
+                                        _ptr(out), _ptr(idx), B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(),
                                         arr, _stream(q)))
+    elif lens is not None:
+        _check(lib.loki_decode_varlen(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead),
+                                      0 if K_lead is None else K_lead.shape[3], _ptr(V), _ptr(lens), _ptr(out),
+                                      _ptr(idx), B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(), _stream(q)))
     elif K_lead is None:
         _check(lib.loki_decode(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(V), _ptr(out), _ptr(idx),
                                B, Hq, Hkv, S, d, r, k, dt, _ptr(ws), ws.numel(), _stream(q)))

@@ -238,16 +238,16 @@ loki_status loki_decode_varlen(const void* q, const void* P, const void* K_rot, 
 }
 
 loki_status loki_decode_profiled(const void* q, const void* P, const void* K_rot, const void* K_lead,
-                                 int32_t R, const void* V, void* out, int32_t* idx, int32_t B,
-                                 int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
-                                 loki_dtype dt, void* workspace, size_t workspace_bytes,
+                                 int32_t R, const void* V, const int32_t* lens, void* out, int32_t* idx,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r,
+                                 int32_t k, loki_dtype dt, void* workspace, size_t workspace_bytes,
                                  hipEvent_t* events, hipStream_t stream) {
   try {
     if (!events) return LOKI_ERR_NULL;
     for (int i = 0; i < 6; ++i)
       if (!events[i]) return LOKI_ERR_NULL;
     return decode_impl(q, P, K_rot, K_lead, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
-                       workspace_bytes, stream, events);
+                       workspace_bytes, stream, events, lens);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

@@ -461,7 +461,11 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
 
 // ============================================================================
 // Exact attention over the kept tokens, bf16 caches, G <= 8.
-// Wave = NT consecutive tokens of one (b, kv) group; four waves per block.
+// Wave = a span of up to NT consecutive tokens of one (b, kv) group; four
+// waves per block.  A full-length sequence gives every wave NT tokens; a
+// shorter one (per-sequence lengths) is cut into the same number of narrower
+// spans, whole bitmap words each, so that a block of a short sequence, whose
+// kept tokens lie closer together, still sees about as many of them.
 // The G heads' bitmap words of the span go through LDS (one load per lane)
 // and give the union list (token, head mask).  Then two passes over it:
 //   pass 1: 16-row K tiles in MFMA A layout (a load instruction reads 64
@@ -483,7 +487,8 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
                                                           const uint16_t* __restrict__ qsplit,
                                                           const uint32_t* __restrict__ bitmap,
                                                           float* __restrict__ part, int Hq, int Hkv,
-                                                          int S, int W, int NC, float scale_log2) {
+                                                          int S, int W, int NC, float scale_log2,
+                                                          const int32_t* __restrict__ lens) {
   constexpr int NGRP = (GT + 3) / 4;
   constexpr int KS = D / 32;         // 32-dim k-steps of the exact dot
   constexpr int EPL = 8;             // bf16 per 16-byte granule
@@ -507,7 +512,14 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
   const int bk = blockIdx.y, b = bk / Hkv, kv = bk % Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int t0 = (blockIdx.x * 4 + wave) * NT;
+  int span = NT, tend = S;
+  if (lens) {
+    const int L = seq_len(lens, b, S), nwv = 4 * NC;
+    span = min(NT, max(32, ((L + nwv - 1) / nwv + 31) & ~31));
+    tend = L;
+  }
+  const int t0 = (blockIdx.x * 4 + wave) * span;
+  tend = min(tend, t0 + span);
   const size_t head0 = (size_t)b * Hq + (size_t)kv * G;
   int* tok = s_tok[wave];
   uint16_t* hmk = s_hm[wave];
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(256, GT <= 4 ? 4 : 2) void attend_mfma_kernel(const
   if (lane < G * NW) {
     const int g = lane / NW, w = lane - g * NW;
     const int t = t0 + 32 * w;
-    bits[lane] = (t < S) ? bitmap[(head0 + g) * W + (t >> 5)] : 0u;
+    bits[lane] = (t < tend) ? bitmap[(head0 + g) * W + (t >> 5)] : 0u;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -841,7 +853,7 @@ hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void
   auto go = [&](auto dd, auto gt) {
     constexpr int D = decltype(dd)::value, GT = decltype(gt)::value;
     hipLaunchKernelGGL((attend_mfma_kernel<D, GT>), grid, block, 0, st, k, v, qsplit, bitmap, part,
-                       p.Hq, p.Hkv, p.S, p.W, p.NAC, scale_log2);
+                       p.Hq, p.Hkv, p.S, p.W, p.NAC, scale_log2, p.lens);
     return hipGetLastError();
   };
   auto by_g = [&](auto dd) {
