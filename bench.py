@@ -426,6 +426,93 @@ def run_project(args) -> dict:
     }
 
 
+def run_calibrate(args) -> dict:
+    """Offline calibration of the basis (loki_calibrate_pca) on the workload's
+    whole key cache: Gram matrix of each key head's rows (MFMA), fixed-order
+    sum of the partials, Jacobi eigensolver.  The Gram kernel streams the
+    cache (HBM roofline); the eigensolver is one block per key head."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(cfg, need_K=True)
+    K = x["K"].to(dev)
+    P = torch.empty((cfg.Hkv, cfg.d, cfg.d), dtype=K.dtype, device=dev)
+    lam = torch.empty((cfg.Hkv, cfg.d), dtype=torch.float64, device=dev)
+    ws = torch.empty(rks.loki_calibrate_workspace_bytes(cfg.B, cfg.Hkv, cfg.S, cfg.d), dtype=torch.uint8,
+                     device=dev)
+
+    def step(events=None):
+        rks.loki_calibrate_pca(K, P, lam, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    names = ("gram", "reduce", "eigensolver")
+    stage_us = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:
+        for ev in row:
+            ev.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    for row in evs:
+        for j, n in enumerate(names):
+            stage_us[n] += 1e3 * row[j].elapsed_time(row[j + 1]) / args.steps
+    e = cfg.elem_bytes
+    rows = cfg.B * cfg.Hkv * cfg.S
+    by = rows * cfg.d * e  # the keys, read once
+    flop = 2.0 * rows * cfg.d * cfg.d
+    gbs = by / (stage_us["gram"] * 1e-6) / 1e9
+    tflops = flop / (stage_us["gram"] * 1e-6) / 1e12
+    # oracle (float64 SVD) on one key head, single-threaded, scaled to all heads;
+    # its result also checks the GPU's leading directions and eigenvalues there
+    import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        P_o, lam_o = oracle.calibrate(x["K"][:, :1])
+        per_head = time.perf_counter() - t
+    Pg = P.double().cpu().numpy()[0]
+    cos = np.abs(np.sum(Pg[:, :cfg.r] * P_o[0][:, :cfg.r], axis=0))
+    ok = bool(np.min(cos) > 0.999 and np.max(np.abs(lam.cpu().numpy()[0] - lam_o[0])) <= 1e-4 * lam_o[0, 0])
+    return {
+        "metric": "basis calibration (principal directions of the key cache, per key head): calls/s",
+        "value": round(1e3 / ms, 3), "unit": "calls/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} key-cache calibration", "batch": cfg.B, "kv_heads": cfg.Hkv,
+                   "head_dim": cfg.d, "cached_tokens": cfg.S},
+        "stage_us": {n: round(v, 2) for n, v in stage_us.items()},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gram_bf16_kernel",
+                     "alg_bytes_per_launch": by, "avg_launch_us": round(stage_us["gram"], 2),
+                     "note": "the eigensolver (one block per key head, latency-bound) takes most of the call"},
+        "mfma": {"tflops": round(tflops, 2), "peak_tflops": 2500.0, "util": round(tflops / 2500.0, 4),
+                 "flop_per_launch": flop},
+        "cpu_baseline": {"value": round(1.0 / (per_head * cfg.Hkv), 5), "unit": "calls/s", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"one key head ({cfg.B * cfg.S}x{cfg.d} float64 SVD, {per_head:.1f} s), "
+                                   f"scaled to {cfg.Hkv} heads",
+                         "gpu_matches_oracle_on_sample": ok},
+    }
+
+
 def run_append(args) -> dict:
     """One decode step's cache append (loki_append_kv): the new key of every
     (b, kv) rotated into the basis and written with its value and lead dims
@@ -537,7 +624,7 @@ def main() -> int:
                     help="decode a ragged batch: per-sequence cache lengths from S down to about S/2")
     ap.add_argument("--graph", action="store_true",
                     help="decode: time steps replayed from HIP graphs (one launch per step)")
-    ap.add_argument("--op", default="decode", choices=["decode", "project", "append"],
+    ap.add_argument("--op", default="decode", choices=["decode", "project", "append", "calibrate"],
                     help="project: time the key projection instead (use --workload C5); "
                          "append: time one decode step's cache append")
     ap.add_argument("--summarize-trace", metavar="DB")
@@ -561,7 +648,7 @@ def main() -> int:
         for _ in range(3):
             torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-    res = {"project": run_project, "append": run_append}.get(args.op, run)(args)
+    res = {"project": run_project, "append": run_append, "calibrate": run_calibrate}.get(args.op, run)(args)
     print(json.dumps(res))
     return 0
 

@@ -245,6 +245,46 @@ loki_status loki_attend(const void* q, const void* P, const void* K_rot, const v
                         loki_dtype dt, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
+/*
+ * Offline calibration of the basis P, the step that produces the P every
+ * other entry point takes (AQUA page, appendix on the SVD: the principal
+ * directions of a key matrix A are the right singular vectors of A, i.e. the
+ * eigenvectors of A^T A; the Loki page keeps the leading ones; AQUA's related
+ * work: the matrix is computed offline).  For each key/value head kv, A is
+ * the [B*S, d] matrix of the key rows of all batch elements of that head
+ * (uncentred), and
+ *   P[kv][:, c]     = the eigenvector of A^T A with the c-th largest
+ *                     eigenvalue, scaled by +-1 so that its entry of largest
+ *                     magnitude (the first such, on exact ties) is positive;
+ *                     equal eigenvalues keep the eigensolver's order;
+ *   eigvals[kv][c]  = that eigenvalue (fp64), if eigvals is not NULL.
+ *   K       [B, Hkv, S, d] keys in the original basis (the cache layout of
+ *           loki_project_keys), dt = LOKI_F32 or LOKI_BF16;
+ *   P       [Hkv, d, d] output in dt (fp64 result rounded once, to nearest);
+ *   eigvals [Hkv, d] fp64 output or NULL (8-byte aligned).
+ * The Gram matrix is accumulated in fp64 (bf16 keys: exact products summed
+ * in fp32 over 256 rows, then in fp64; fp32 keys: exact products, fp64
+ * sums) and diagonalised by cyclic Jacobi in fp64.  When A has rank below
+ * d, the null-space columns are some orthonormal completion.
+ * Sizes: B, Hkv, S >= 1 with B*S < 2^31 (else LOKI_ERR_SHAPE); d in {64, 128}
+ * (else LOKI_ERR_UNSUPPORTED).  K and P 16-byte aligned.  Workspace of
+ * loki_calibrate_workspace_bytes(B, Hkv, S, d) bytes, 16-byte aligned.
+ */
+size_t loki_calibrate_workspace_bytes(int32_t B, int32_t Hkv, int32_t S, int32_t d);
+loki_status loki_calibrate_pca(const void* K, void* P, double* eigvals, int32_t B, int32_t Hkv,
+                               int32_t S, int32_t d, loki_dtype dt, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * loki_calibrate_pca plus hipEventRecord(events[i], stream) at the stage
+ * boundaries: [0] before the Gram kernel, [1] after it, [2] after the sum of
+ * the partials, [3] after the eigensolver and output (the end).  events must
+ * hold 4 created events (LOKI_ERR_NULL otherwise).
+ */
+loki_status loki_calibrate_pca_profiled(const void* K, void* P, double* eigvals, int32_t B, int32_t Hkv,
+                                        int32_t S, int32_t d, loki_dtype dt, void* workspace,
+                                        size_t workspace_bytes, hipEvent_t* events, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

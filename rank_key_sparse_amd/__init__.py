@@ -4,6 +4,7 @@ Argument marshalling only: every step runs in the library's HIP kernels.
 torch supplies device memory and the current HIP stream.  The entry points
 mirror the C ABI (``include/loki.h``) name for name:
 
+* :func:`loki_calibrate_pca` -- the basis ``P`` itself: principal directions of sampled keys;
 * :func:`loki_project_keys` -- ``K_rot = K P`` per key/value head;
 * :func:`loki_append_kv` -- one decode step's new key (rotated) and value written into the caches;
 * :func:`loki_decode` -- one Loki decode step -> ``(out, idx)``;
@@ -65,6 +66,9 @@ _SIGS = {
     "loki_select_topk": ([_P, _P, _I, _I, _I, _P, _Z, _P], ctypes.c_int),
     "loki_attend": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
                     ctypes.c_int),
+    "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
+    "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -150,6 +154,47 @@ def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | No
     _check(lib.loki_project_keys_lead(_ptr(K), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, B, Hkv, S, d,
                                       _dtype_code(K), _stream(K)))
     return K_rot, K_lead
+
+
+def loki_calibrate_workspace_bytes(B: int, Hkv: int, S: int, d: int) -> int:
+    return int(load_library().loki_calibrate_workspace_bytes(B, Hkv, S, d))
+
+
+def loki_calibrate_pca(K: torch.Tensor, P: torch.Tensor | None = None, eigvals: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, events=None):
+    """Principal basis of sampled keys K [B,Hkv,S,d] (cache layout), per key head:
+    returns ``(P [Hkv,d,d] in K's dtype, eigvals [Hkv,d] float64)``, columns of P in
+    decreasing eigenvalue order of ``A^T A`` (A = the head's key rows), each
+    column's largest-magnitude entry positive.  ``events``: 4 torch.cuda.Event
+    recorded at the stage boundaries (measurement)."""
+    _need(K, "K", ndim=4)
+    B, Hkv, S, d = K.shape
+    dev = K.device
+    if P is None:
+        P = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev)
+    _need(P, "P", dtype=K.dtype, ndim=3, device=dev)
+    if tuple(P.shape) != (Hkv, d, d):
+        raise ValueError("P must be [Hkv, d, d]")
+    if eigvals is None:
+        eigvals = torch.empty((Hkv, d), dtype=torch.float64, device=dev)
+    _need(eigvals, "eigvals", dtype=torch.float64, ndim=2, device=dev)
+    if tuple(eigvals.shape) != (Hkv, d):
+        raise ValueError("eigvals must be [Hkv, d]")
+    lib = load_library()
+    nbytes = int(lib.loki_calibrate_workspace_bytes(B, Hkv, S, d))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", dtype=torch.uint8, device=dev)
+    if events is None:
+        _check(lib.loki_calibrate_pca(_ptr(K), _ptr(P), _ptr(eigvals), B, Hkv, S, d, _dtype_code(K),
+                                      _ptr(workspace), workspace.numel(), _stream(K)))
+    else:
+        if len(events) != 4:
+            raise ValueError("events must hold 4 torch.cuda.Event objects")
+        arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check(lib.loki_calibrate_pca_profiled(_ptr(K), _ptr(P), _ptr(eigvals), B, Hkv, S, d, _dtype_code(K),
+                                               _ptr(workspace), workspace.numel(), arr, _stream(K)))
+    return P, eigvals
 
 
 def loki_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, P: torch.Tensor, pos: torch.Tensor,

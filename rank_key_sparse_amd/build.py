@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libloki.so")
 
-SOURCES = ["api.hip", "decode_kernels.hip", "mfma_kernels.hip", "project_kernels.hip"]
+SOURCES = ["api.hip", "calib_kernels.hip", "decode_kernels.hip", "mfma_kernels.hip", "project_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -334,4 +334,53 @@ loki_status loki_attend(const void* q, const void* P, const void* K_rot, const v
   }
 }
 
+static loki_status calibrate_impl(const void* K, void* P, double* eigvals, int32_t B, int32_t Hkv, int32_t S,
+                                  int32_t d, loki_dtype dt, void* ws, size_t wsb, hipEvent_t* ev,
+                                  hipStream_t stream) {
+  LOKI_TRY(check_dtype(dt));
+  if (!K || !P) return LOKI_ERR_NULL;
+  if (B < 1 || Hkv < 1 || S < 1 || d < 1) return LOKI_ERR_SHAPE;
+  if ((int64_t)B * S > 0x7fffffffLL || (int64_t)Hkv > kMaxRows) return LOKI_ERR_SHAPE;
+  if (d != 64 && d != 128) return LOKI_ERR_UNSUPPORTED;
+  if (!aligned16(K) || !aligned16(P)) return LOKI_ERR_ALIGN;
+  if (eigvals && (reinterpret_cast<uintptr_t>(eigvals) & 7u)) return LOKI_ERR_ALIGN;
+  CalibPlan p;
+  if (!make_calib_plan(p, B, Hkv, S, d, (int)dt)) return LOKI_ERR_INTERNAL;
+  LOKI_TRY(check_workspace(ws, wsb, p.bytes));
+  return from_hip(launch_calibrate(p, K, P, eigvals, ws, stream, ev));
+}
+
+size_t loki_calibrate_workspace_bytes(int32_t B, int32_t Hkv, int32_t S, int32_t d) {
+  try {
+    CalibPlan p;
+    if ((int64_t)B * S > 0x7fffffffLL || !make_calib_plan(p, B, Hkv, S, d, 1)) return 0;
+    return p.bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
+loki_status loki_calibrate_pca(const void* K, void* P, double* eigvals, int32_t B, int32_t Hkv, int32_t S,
+                               int32_t d, loki_dtype dt, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  try {
+    return calibrate_impl(K, P, eigvals, B, Hkv, S, d, dt, workspace, workspace_bytes, nullptr, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_calibrate_pca_profiled(const void* K, void* P, double* eigvals, int32_t B, int32_t Hkv,
+                                        int32_t S, int32_t d, loki_dtype dt, void* workspace,
+                                        size_t workspace_bytes, hipEvent_t* events, hipStream_t stream) {
+  try {
+    if (!events) return LOKI_ERR_NULL;
+    for (int i = 0; i < 4; ++i)
+      if (!events[i]) return LOKI_ERR_NULL;
+    return calibrate_impl(K, P, eigvals, B, Hkv, S, d, dt, workspace, workspace_bytes, events, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

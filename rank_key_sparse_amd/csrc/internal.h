@@ -102,4 +102,20 @@ hipError_t launch_append_kv(const void* k_new, const void* v_new, const void* P,
 hipError_t launch_project(const void* K, const void* P, void* K_rot, void* K_lead, int R, int B,
                           int Hkv, int S, int d, int dt, hipStream_t st);
 
+// Basis calibration (principal directions of the keys of each key head).
+struct CalibPlan {
+  int B, Hkv, S, d, dt;
+  int N;           // key rows per head: B * S
+  int rows, nblk;  // Gram kernel: rows per block, blocks per head
+  // workspace: Gram partials [Hkv][nblk][d][d], Gram [Hkv][d][d], eigenvectors
+  // (transposed) [Hkv][d][d], all fp64
+  size_t off_part, off_C, off_V, bytes;
+};
+bool make_calib_plan(CalibPlan& p, int B, int Hkv, int S, int d, int dt);
+// Gram partials, their sum, Jacobi eigensolver and output; when ev is non-null
+// ev[0..3] are recorded before the Gram kernel, after it, after the sum and
+// at the end.
+hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* eigvals, void* ws,
+                            hipStream_t st, hipEvent_t* ev);
+
 }  // namespace loki

@@ -156,3 +156,28 @@ def test_lead_entry_points_reject(lib):
     assert g(A, A, A, NULLP, 32, 1, 1, 8, 128, BF16, NULLP) == NULL
     assert g(A, A, A, A, 200, 1, 1, 8, 128, BF16, NULLP) == RANGE
     assert g(A, A, A, A, 6, 1, 1, 8, 128, F32, NULLP) == UNSUPPORTED
+
+
+def test_calibrate_rejects(lib):
+    f = lib.loki_calibrate_pca
+    # (K, P, eigvals, B, Hkv, S, d, dt, ws, wsb, stream)
+    big = 1 << 40
+    assert f(NULLP, A, A, 1, 2, 512, 128, BF16, A2, big, NULLP) == NULL
+    assert f(A, NULLP, A, 1, 2, 512, 128, BF16, A2, big, NULLP) == NULL
+    assert f(A, A, A, 0, 2, 512, 128, BF16, A2, big, NULLP) == SHAPE
+    assert f(A, A, A, 1, 0, 512, 128, BF16, A2, big, NULLP) == SHAPE
+    assert f(A, A, A, 1, 2, 0, 128, BF16, A2, big, NULLP) == SHAPE
+    assert f(A, A, A, 1 << 16, 2, 1 << 16, 128, BF16, A2, big, NULLP) == SHAPE  # B*S >= 2^31
+    assert f(A, A, A, 1, 2, 512, 96, BF16, A2, big, NULLP) == UNSUPPORTED
+    assert f(A, A, A, 1, 2, 512, 128, 5, A2, big, NULLP) == DTYPE
+    assert f(MIS, A, A, 1, 2, 512, 128, BF16, A2, big, NULLP) == ALIGN
+    assert f(A, MIS, A, 1, 2, 512, 128, BF16, A2, big, NULLP) == ALIGN
+    assert f(A, A, ctypes.c_void_p(0x10004), 1, 2, 512, 128, BF16, A2, big, NULLP) == ALIGN
+    need = lib.loki_calibrate_workspace_bytes(1, 2, 512, 128)
+    assert need >= 3 * 2 * 128 * 128 * 8
+    assert f(A, A, A, 1, 2, 512, 128, BF16, A2, need - 1, NULLP) == WORKSPACE
+    assert f(A, A, A, 1, 2, 512, 128, BF16, NULLP, need, NULLP) == NULL
+    assert lib.loki_calibrate_workspace_bytes(1, 2, 512, 100) == 0
+    assert lib.loki_calibrate_workspace_bytes(1 << 16, 2, 1 << 16, 128) == 0
+    g = lib.loki_calibrate_pca_profiled
+    assert g(A, A, A, 1, 2, 512, 128, BF16, A2, big, NULLP, NULLP) == NULL
