@@ -14,11 +14,12 @@
 //       bf16 keys on MFMA (products exact, fp32 sums over 256 rows, then
 //       fp64), fp32 keys with fp64 FMAs (products exact);
 //   gram_reduce_kernel - the partials of a head summed in a fixed order;
-//   jacobi_eig_kernel  - one block per head: cyclic two-sided Jacobi in fp64
-//       on the Gram matrix held in LDS, all d/2 disjoint rotations of a round
-//       applied at once (round-robin pairing), the eigenvector matrix kept in
-//       the workspace; then eigenvalues ranked in decreasing order, each
-//       eigenvector's largest-magnitude entry made positive, P written.
+//   jacobi_c_kernel, jacobi_v_kernel, eig_out_kernel - cyclic two-sided
+//       Jacobi in fp64 on the Gram matrix held in LDS (all d/2 disjoint
+//       rotations of a round at once, round-robin pairing, rotations logged),
+//       the eigenvector matrix rebuilt from the log, then eigenvalues ranked
+//       in decreasing order, each eigenvector's largest-magnitude entry made
+//       positive, P written.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -33,7 +34,10 @@ constexpr int kGramTile = 32;       // key rows per tile (one 32-deep MFMA k-ste
 constexpr int kGramFlush = 8;       // tiles summed in fp32 before adding into fp64
 constexpr int kGramBlocks = 512;    // Gram blocks per call (all heads), before rounding
 constexpr int kJacobiThreads = 1024;
-constexpr int kJacobiMaxSweeps = 64;
+constexpr int kJacobiMaxSweeps = 48;
+
+// Rounds of the rotation log per head (d - 1 rounds per sweep).
+__host__ __device__ constexpr int jacobi_max_rounds(int D) { return kJacobiMaxSweeps * (D - 1); }
 
 bool make_calib_plan(CalibPlan& p, int B, int Hkv, int S, int d, int dt) {
   if (B < 1 || Hkv < 1 || S < 1 || (d != 64 && d != 128)) return false;
@@ -51,6 +55,9 @@ bool make_calib_plan(CalibPlan& p, int B, int Hkv, int S, int d, int dt) {
   p.off_part = off; off = align_up(off + (size_t)Hkv * p.nblk * dd, 256);
   p.off_C = off;    off = align_up(off + (size_t)Hkv * dd, 256);
   p.off_V = off;    off = align_up(off + (size_t)Hkv * dd, 256);
+  p.off_log = off;  off = align_up(off + (size_t)Hkv * jacobi_max_rounds(d) * (d / 2) * 2 * sizeof(double), 256);
+  p.off_nr = off;   off = align_up(off + (size_t)Hkv * sizeof(int), 256);
+  p.off_lam = off;  off = align_up(off + (size_t)Hkv * d * sizeof(double), 256);
   p.bytes = off;
   return true;
 }
@@ -280,62 +287,63 @@ template <> __device__ __forceinline__ bf16_t from_f64<bf16_t>(double x) {
 }
 
 // ---------------------------------------------------------------------------
-// Cyclic two-sided Jacobi, one block of 1024 threads per head.  C (d x d,
-// fp64) lives in LDS; V is kept transposed in the workspace (Vt[col][row]).
-// A round rotates the d/2 disjoint pairs (p, q) of the round-robin pairing:
-// for a pair with C_pq off the diagonal by more than a relative threshold,
+// Cyclic two-sided Jacobi on the Gram matrix C of one head, in three launches.
+//
+// jacobi_c_kernel (one block of 1024 threads per head): C (fp64) in LDS, only
+// its upper triangle (row stride d + 1, so that a wave's accesses along a row
+// or a column fall into different banks).  A round rotates the d/2 disjoint
+// pairs (p, q) of the round-robin pairing; for a pair whose C_pq is off the
+// diagonal by more than a relative threshold,
 //   tau = (C_qq - C_pp) / (2 C_pq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
 //   c = 1 / sqrt(1 + t^2), s = t c, J = [[c, s], [-s, c]] on (p, q)
-// (the symmetric Schur rotation that zeroes C_pq), and C <- J^T C J, V <- V J
-// for all pairs at once: each 2 x 2 block of C between pairs j <= j' is
-// updated by one thread (and mirrored), each pair's two columns of V by 16
-// threads.  Sweeps repeat until one rotates nothing (at most 64).
+// (the symmetric Schur rotation that zeroes C_pq), and C <- J^T C J for all
+// pairs at once: one thread per 2 x 2 block between pairs j <= j'.  The
+// rotations (c, s) of every round go to a log in the workspace.  Sweeps
+// repeat until one rotates nothing (at most kJacobiMaxSweeps).
+//
+// jacobi_v_kernel (one block per 16 rows of V and head): V = I J_1 J_2 ...
+// from the log, the rows in LDS, one rotation of one row per thread and round.
+//
+// eig_out_kernel (one block per head): eigenvalues ranked in decreasing order
+// (equal values by index), each eigenvector's first entry of largest
+// magnitude made positive, P and the eigenvalues written.
 // ---------------------------------------------------------------------------
-template <int D, typename T>
-__global__ __launch_bounds__(kJacobiThreads) void jacobi_eig_kernel(const double* __restrict__ Cg,
-                                                                     double* __restrict__ Vt_all,
-                                                                     T* __restrict__ P,
-                                                                     double* __restrict__ eigvals) {
+constexpr int kJacobiVRows = 16;   // rows of V per block of the rotation-apply kernel
+constexpr int kJacobiLogChunk = 16;  // logged rounds staged in LDS at a time
+
+template <int D>
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* __restrict__ Cg,
+                                                                   double2* __restrict__ rlog,
+                                                                   int* __restrict__ nrounds,
+                                                                   double* __restrict__ lam_raw) {
   constexpr int NP = D / 2;
-  constexpr int VPT = D * D / (2 * kJacobiThreads);  // V entries of each column per thread
-  constexpr int VT = D / VPT;                        // threads per pair in the V update
+  constexpr int DS = D + 1;
   constexpr double kTol = 1e-14;
   constexpr double kTiny = 1e-300;
   extern __shared__ __align__(16) double sC[];
   __shared__ double s_c[NP], s_s[NP], s_t[NP];
-  __shared__ int s_rank[D];
   __shared__ int s_rot;
 
   const int kv = blockIdx.x, tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  double* Vt = Vt_all + (size_t)kv * D * D;
   const double* Ch = Cg + (size_t)kv * D * D;
+  double2* lg = rlog + (size_t)kv * jacobi_max_rounds(D) * NP;
+  auto U = [&](int x, int y) -> double& { return sC[min(x, y) * DS + max(x, y)]; };
 
-  // C from its upper triangle (exactly symmetric), V = I
   for (int e = tid; e < D * D; e += kJacobiThreads) {
     const int i = e / D, j = e - i * D;
-    sC[e] = Ch[min(i, j) * D + max(i, j)];
-    Vt[e] = (i == j) ? 1.0 : 0.0;
+    if (i <= j) sC[i * DS + j] = Ch[e];
   }
   if (tid == 0) s_rot = 0;
   __syncthreads();
 
-  const int jv = tid / VT, i0 = (tid % VT) * VPT;
-  for (int sweep = 0; sweep < kJacobiMaxSweeps; ++sweep) {
-    for (int r = 0; r < D - 1; ++r) {
-      // this thread's V entries of the round (issued before the rotation is known)
-      int pv, qv;
-      jacobi_pair(r, jv, D, pv, qv);
-      double vp[VPT], vq[VPT];
-#pragma unroll
-      for (int e = 0; e < VPT; ++e) {
-        vp[e] = Vt[pv * D + i0 + e];
-        vq[e] = Vt[qv * D + i0 + e];
-      }
+  int round = 0;
+  bool still = true;
+  for (int sweep = 0; sweep < kJacobiMaxSweeps && still; ++sweep) {
+    for (int r = 0; r < D - 1; ++r, ++round) {
       if (tid < NP) {
         int p, q;
         jacobi_pair(r, tid, D, p, q);
-        const double a = sC[p * D + p], b = sC[q * D + q], g = sC[p * D + q];
+        const double a = U(p, p), b = U(q, q), g = U(p, q);
         double c = 1.0, s = 0.0, t = 0.0;
         if (fabs(g) > kTiny && fabs(g) > kTol * sqrt(fabs(a)) * sqrt(fabs(b))) {
           const double tau = (b - a) / (2.0 * g);
@@ -348,6 +356,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_eig_kernel(const double
         s_c[tid] = c;
         s_s[tid] = s;
         s_t[tid] = t;
+        lg[(size_t)round * NP + tid] = make_double2(c, s);
       }
       __syncthreads();
       for (int id = tid; id < NP * NP; id += kJacobiThreads) {
@@ -355,76 +364,118 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_eig_kernel(const double
         if (j > j2) continue;
         int p, q, p2, q2;
         jacobi_pair(r, j, D, p, q);
-        jacobi_pair(r, j2, D, p2, q2);
         const double c = s_c[j], s = s_s[j];
         if (j == j2) {
           if (s != 0.0) {
-            const double t = s_t[j], g = sC[p * D + q];
-            sC[p * D + p] -= t * g;
-            sC[q * D + q] += t * g;
-            sC[p * D + q] = 0.0;
-            sC[q * D + p] = 0.0;
+            const double t = s_t[j], g = U(p, q);
+            U(p, p) -= t * g;
+            U(q, q) += t * g;
+            U(p, q) = 0.0;
           }
           continue;
         }
+        jacobi_pair(r, j2, D, p2, q2);
         const double c2 = s_c[j2], s2 = s_s[j2];
-        const double m00 = sC[p * D + p2], m01 = sC[p * D + q2];
-        const double m10 = sC[q * D + p2], m11 = sC[q * D + q2];
-        // rows: J^T M
+        const double m00 = U(p, p2), m01 = U(p, q2), m10 = U(q, p2), m11 = U(q, q2);
+        // rows: J^T M; columns: (J^T M) J'
         const double l00 = c * m00 - s * m10, l01 = c * m01 - s * m11;
         const double l10 = s * m00 + c * m10, l11 = s * m01 + c * m11;
-        // columns: (J^T M) J'
-        const double n00 = c2 * l00 - s2 * l01, n01 = s2 * l00 + c2 * l01;
-        const double n10 = c2 * l10 - s2 * l11, n11 = s2 * l10 + c2 * l11;
-        sC[p * D + p2] = n00;
-        sC[p * D + q2] = n01;
-        sC[q * D + p2] = n10;
-        sC[q * D + q2] = n11;
-        sC[p2 * D + p] = n00;
-        sC[q2 * D + p] = n01;
-        sC[p2 * D + q] = n10;
-        sC[q2 * D + q] = n11;
-      }
-      {
-        const double c = s_c[jv], s = s_s[jv];
-        if (s != 0.0) {
-#pragma unroll
-          for (int e = 0; e < VPT; ++e) {
-            Vt[pv * D + i0 + e] = c * vp[e] - s * vq[e];
-            Vt[qv * D + i0 + e] = s * vp[e] + c * vq[e];
-          }
-        }
+        U(p, p2) = c2 * l00 - s2 * l01;
+        U(p, q2) = s2 * l00 + c2 * l01;
+        U(q, p2) = c2 * l10 - s2 * l11;
+        U(q, q2) = s2 * l10 + c2 * l11;
       }
       __syncthreads();
     }
-    const int rotated = s_rot;
+    still = s_rot != 0;  // the same value in every thread
     __syncthreads();
-    if (!rotated) break;  // the same value in every thread
     if (tid == 0) s_rot = 0;
     __syncthreads();
   }
+  if (tid == 0) nrounds[kv] = still ? round : round - (D - 1);  // a last sweep without rotations is not replayed
+  if (tid < D) lam_raw[(size_t)kv * D + tid] = sC[tid * DS + tid];
+}
 
-  // ranks: decreasing eigenvalue, equal values by index
+template <int D>
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_v_kernel(const double2* __restrict__ rlog,
+                                                                   const int* __restrict__ nrounds,
+                                                                   double* __restrict__ V) {
+  constexpr int NP = D / 2;
+  constexpr int DS = D + 1;
+  constexpr int RB = kJacobiVRows;
+  constexpr int CH = kJacobiLogChunk;
+  constexpr int NT = NP * RB;  // threads: one (pair, row) each
+  static_assert(CH * NP == NT, "one logged rotation per thread per chunk");
+  __shared__ __align__(16) double sV[RB * DS];
+  __shared__ __align__(16) double2 sL[2][CH * NP];
+
+  const int kv = blockIdx.y, rb = blockIdx.x, tid = threadIdx.x;
+  const int j = tid / RB, row = tid - j * RB;
+  const int nr = nrounds[kv];
+  const double2* lg = rlog + (size_t)kv * jacobi_max_rounds(D) * NP;
+  auto fetch = [&](int c0) {
+    const int rd = c0 + tid / NP;
+    const double2 v = lg[(size_t)min(rd, max(nr - 1, 0)) * NP + tid % NP];
+    return rd < nr ? v : make_double2(1.0, 0.0);
+  };
+
+  for (int e = tid; e < RB * D; e += NT) {
+    const int rr = e / D, c = e - rr * D;
+    sV[rr * DS + c] = (rb * RB + rr == c) ? 1.0 : 0.0;
+  }
+  if (nr > 0) sL[0][tid] = fetch(0);
+  __syncthreads();
+  const int nch = (nr + CH - 1) / CH;
+  for (int ch = 0; ch < nch; ++ch) {
+    const double2 nxt = fetch((ch + 1) * CH);  // the next chunk travels while this one is applied
+    const double2* L = sL[ch & 1];
+    const int kend = min(CH, nr - ch * CH);
+    for (int k = 0; k < kend; ++k) {
+      int p, q;
+      jacobi_pair((ch * CH + k) % (D - 1), j, D, p, q);
+      const double2 cs = L[k * NP + j];
+      if (cs.y != 0.0) {
+        const double vp = sV[row * DS + p], vq = sV[row * DS + q];
+        sV[row * DS + p] = cs.x * vp - cs.y * vq;
+        sV[row * DS + q] = cs.y * vp + cs.x * vq;
+      }
+      __syncthreads();
+    }
+    sL[(ch + 1) & 1][tid] = nxt;
+    __syncthreads();
+  }
+  for (int e = tid; e < RB * D; e += NT) {
+    const int rr = e / D, c = e - rr * D;
+    V[((size_t)kv * D + rb * RB + rr) * D + c] = sV[rr * DS + c];
+  }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(kJacobiThreads) void eig_out_kernel(const double* __restrict__ V,
+                                                                  const double* __restrict__ lam_raw,
+                                                                  T* __restrict__ P, double* __restrict__ eigvals) {
+  __shared__ int s_rank[D];
+  const int kv = blockIdx.x, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const double* lam = lam_raw + (size_t)kv * D;
+  const double* Vh = V + (size_t)kv * D * D;
   if (tid < D) {
-    const double li = sC[tid * D + tid];
+    const double li = lam[tid];
     int rank = 0;
     for (int j = 0; j < D; ++j) {
-      const double lj = sC[j * D + j];
+      const double lj = lam[j];
       rank += (lj > li) || (lj == li && j < tid);
     }
     s_rank[tid] = rank;
     if (eigvals) eigvals[(size_t)kv * D + rank] = li;
   }
   __syncthreads();
-
-  // eigenvector of column `col` -> column rank[col] of P, its first entry of
-  // largest magnitude made positive
   T* Ph = P + (size_t)kv * D * D;
   for (int col = wave; col < D; col += kJacobiThreads / 64) {
     double best = -1.0;
     int bi = 0;
     for (int i = lane; i < D; i += 64) {
-      const double v = fabs(Vt[col * D + i]);
+      const double v = fabs(Vh[(size_t)i * D + col]);
       if (v > best) {
         best = v;
         bi = i;
@@ -439,9 +490,9 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_eig_kernel(const double
         bi = oi;
       }
     }
-    const double sg = (Vt[col * D + bi] < 0.0) ? -1.0 : 1.0;
+    const double sg = (Vh[(size_t)bi * D + col] < 0.0) ? -1.0 : 1.0;
     const int rk = s_rank[col];
-    for (int i = lane; i < D; i += 64) Ph[(size_t)i * D + rk] = from_f64<T>(sg * Vt[col * D + i]);
+    for (int i = lane; i < D; i += 64) Ph[(size_t)i * D + rk] = from_f64<T>(sg * Vh[(size_t)i * D + col]);
   }
 }
 
@@ -481,21 +532,31 @@ hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* 
                      DD);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  const size_t lds = (size_t)DD * sizeof(double);
+  double2* rlog = reinterpret_cast<double2*>(w + p.off_log);
+  int* nr = reinterpret_cast<int*>(w + p.off_nr);
+  double* lam_raw = reinterpret_cast<double*>(w + p.off_lam);
+  const size_t lds = (size_t)D * (D + 1) * sizeof(double);
+  {
+    auto kc = (D == 128) ? &jacobi_c_kernel<128> : &jacobi_c_kernel<64>;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kc), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(kc, dim3(p.Hkv), dim3(kJacobiThreads), lds, st, C, rlog, nr, lam_raw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (D == 128)
+    hipLaunchKernelGGL(jacobi_v_kernel<128>, dim3(128 / kJacobiVRows, p.Hkv), dim3(64 * kJacobiVRows), 0, st, rlog,
+                       nr, Vt);
+  else
+    hipLaunchKernelGGL(jacobi_v_kernel<64>, dim3(64 / kJacobiVRows, p.Hkv), dim3(32 * kJacobiVRows), 0, st, rlog,
+                       nr, Vt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dt == 1) {
-    bf16_t* out = static_cast<bf16_t*>(P);
-    auto kern = (D == 128) ? &jacobi_eig_kernel<128, bf16_t> : &jacobi_eig_kernel<64, bf16_t>;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(kern, dim3(p.Hkv), dim3(kJacobiThreads), lds, st, C, Vt, out, eigvals);
+    auto ko = (D == 128) ? &eig_out_kernel<128, bf16_t> : &eig_out_kernel<64, bf16_t>;
+    hipLaunchKernelGGL(ko, dim3(p.Hkv), dim3(kJacobiThreads), 0, st, Vt, lam_raw, static_cast<bf16_t*>(P), eigvals);
   } else {
-    float* out = static_cast<float*>(P);
-    auto kern = (D == 128) ? &jacobi_eig_kernel<128, float> : &jacobi_eig_kernel<64, float>;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(kern, dim3(p.Hkv), dim3(kJacobiThreads), lds, st, C, Vt, out, eigvals);
+    auto ko = (D == 128) ? &eig_out_kernel<128, float> : &eig_out_kernel<64, float>;
+    hipLaunchKernelGGL(ko, dim3(p.Hkv), dim3(kJacobiThreads), 0, st, Vt, lam_raw, static_cast<float*>(P), eigvals);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;

@@ -108,8 +108,9 @@ struct CalibPlan {
   int N;           // key rows per head: B * S
   int rows, nblk;  // Gram kernel: rows per block, blocks per head
   // workspace: Gram partials [Hkv][nblk][d][d], Gram [Hkv][d][d], eigenvectors
-  // (transposed) [Hkv][d][d], all fp64
-  size_t off_part, off_C, off_V, bytes;
+  // [Hkv][d][d] (fp64); the eigensolver's rotation log [Hkv][rounds][d/2]
+  // (c, s), rounds used per head (int), unsorted eigenvalues [Hkv][d]
+  size_t off_part, off_C, off_V, off_log, off_nr, off_lam, bytes;
 };
 bool make_calib_plan(CalibPlan& p, int B, int Hkv, int S, int d, int dt);
 // Gram partials, their sum, Jacobi eigensolver and output; when ev is non-null
