@@ -426,6 +426,124 @@ def run_project(args) -> dict:
     }
 
 
+def run_aqua(args) -> dict:
+    """Decode steps whose approximate scores use each query head's r rotated
+    dims of largest |q_rot| (loki_decode_aqua) on the decode workload."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(cfg)
+    q, P = x["q"].to(dev), x["P"].to(dev)
+    bufs = [(x["K_rot"].to(dev), x["V"].to(dev)) for _ in range(args.buffers)]
+    ws = torch.empty(rks.loki_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.d, cfg.r, cfg.k, q.dtype),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    idx = torch.empty((cfg.B, cfg.Hq, cfg.k), dtype=torch.int32, device=dev)
+    dims = torch.empty((cfg.B, cfg.Hq, cfg.r), dtype=torch.int32, device=dev)
+    info = torch.empty((cfg.B, cfg.Hq), dtype=torch.float32, device=dev)
+
+    def step(i, events=None):
+        Kr, V = bufs[i % len(bufs)]
+        rks.loki_decode_aqua(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, dims=dims, info_loss=info,
+                             events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in evs:
+        for ev in row:
+            ev.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    stage_us = {s: 0.0 for s in STAGES}
+    for row in evs:
+        for j, s_ in enumerate(STAGES):
+            stage_us[s_] += 1e3 * row[j].elapsed_time(row[j + 1]) / args.steps
+    e = cfg.elem_bytes
+    # the dims the method reads: per (b, kv) group the union of its heads' dims
+    dg = dims.view(cfg.B, cfg.Hkv, cfg.G * cfg.r).cpu().numpy()
+    union_dims = int(sum(len(np.unique(dg[b, kv])) for b in range(cfg.B) for kv in range(cfg.Hkv)))
+    by_scores = union_dims * cfg.S * e
+    by_rows = cfg.B * cfg.Hkv * cfg.S * cfg.d * e  # what the kernel streams: whole rotated rows
+    U = union_rows(idx, cfg.G)
+    by_gather = U * cfg.d * 2 * e
+    by_step = by_scores + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
+        + cfg.B * cfg.Hq * cfg.k * 4
+    per = {"scores": by_scores, "attend": by_gather}
+    dom = max(("scores", "attend"), key=lambda s_: stage_us[s_])
+    kern = {"scores": "score_mfma_kernel" if cfg.dtype == "bf16" else "score_kernel",
+            "attend": "attend_mfma_kernel"}[dom]
+    ach = per[dom] / (stage_us[dom] * 1e-6) / 1e9
+    res = {
+        "metric": "decode steps/s with query-magnitude score dims (all heads)",
+        "value": round(1e3 / ms, 1), "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} decode, query-magnitude dims", "batch": cfg.B, "q_heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "head_dim": cfg.d, "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k},
+        "stage_us": {s_: round(v, 2) for s_, v in stage_us.items()},
+        "union_dims_per_group": round(union_dims / (cfg.B * cfg.Hkv), 2),
+        "score_rows_streamed_bytes": by_rows,
+        "info_loss_mean": round(float(info.mean()), 5),
+        "hbm_gbs_step": round(by_step / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kern,
+                     "alg_bytes_per_launch": per[dom], "avg_launch_us": round(stage_us[dom], 2)},
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+        return res
+    # oracle on whole batch elements (bounded), single-threaded; also the
+    # leading-dims information loss of the same queries for comparison
+    import oracle
+    from oracle import aqua
+    from threadpoolctl import threadpool_limits
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity_helpers import check_index_sets
+    ig = idx.cpu().numpy().astype(np.int64)
+    done, used, ok = 0, 0.0, True
+    with threadpool_limits(limits=1):
+        while used < args.cpu_seconds or done == 0:
+            b = done % cfg.B
+            sl = {n: x[n][b:b + 1] for n in ("q", "K_rot", "V")}
+            t = time.perf_counter()
+            idx_o, s_o = aqua.select(sl["q"], x["P"], sl["K_rot"], cfg.r, cfg.k, return_scores=True)
+            oracle.attend(sl["q"], x["P"], sl["K_rot"], sl["V"], idx_o)
+            used += time.perf_counter() - t
+            if done < cfg.B:
+                dims_o = aqua.query_dims(sl["q"], x["P"], cfg.r)
+                same = np.all(dims_o == dg.reshape(cfg.B, cfg.Hq, cfg.r)[b:b + 1], axis=-1)[0]
+                for h in np.nonzero(same)[0]:
+                    try:
+                        check_index_sets(ig[b:b + 1, h:h + 1], idx_o[:, h:h + 1], s_o[:, h:h + 1], cfg.k)
+                    except AssertionError:
+                        ok = False
+            done += 1
+    lead = np.broadcast_to(np.arange(cfg.r), (cfg.B, cfg.Hq, cfg.r))
+    res["info_loss_leading_dims_mean"] = round(float(aqua.info_loss(x["q"], x["P"], lead).mean()), 5)
+    res["cpu_baseline"] = {"value": round(1.0 / (used / done * cfg.B), 4), "unit": "steps/s", "cores": 1,
+                           "kind": "oracle", "sample": f"{done} batch-element decodes, {used:.1f} s single-threaded",
+                           "gpu_matches_oracle_on_sample": ok}
+    return res
+
+
 def run_calibrate(args) -> dict:
     """Offline calibration of the basis (loki_calibrate_pca) on the workload's
     whole key cache: Gram matrix of each key head's rows (MFMA), fixed-order
@@ -624,7 +742,7 @@ def main() -> int:
                     help="decode a ragged batch: per-sequence cache lengths from S down to about S/2")
     ap.add_argument("--graph", action="store_true",
                     help="decode: time steps replayed from HIP graphs (one launch per step)")
-    ap.add_argument("--op", default="decode", choices=["decode", "project", "append", "calibrate"],
+    ap.add_argument("--op", default="decode", choices=["decode", "project", "append", "calibrate", "aqua"],
                     help="project: time the key projection instead (use --workload C5); "
                          "append: time one decode step's cache append")
     ap.add_argument("--summarize-trace", metavar="DB")
@@ -648,7 +766,7 @@ def main() -> int:
         for _ in range(3):
             torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-    res = {"project": run_project, "append": run_append, "calibrate": run_calibrate}.get(args.op, run)(args)
+    res = {"project": run_project, "append": run_append, "calibrate": run_calibrate, "aqua": run_aqua}.get(args.op, run)(args)
     print(json.dumps(res))
     return 0
 

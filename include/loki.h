@@ -246,6 +246,42 @@ loki_status loki_attend(const void* q, const void* P, const void* K_rot, const v
                         hipStream_t stream);
 
 /*
+ * Decode step with query-magnitude dimensions for the approximate scores
+ * (AQUA page, online phase: the dims kept for the approximate scores are
+ * those where the rotated query is largest in magnitude; AQUA page,
+ * information-retention paragraph for L_info).  As loki_decode, except that
+ * for each query head the approximate score of token j is
+ *   s_j = sum_{c in I_h} q_rot[b,h,c] * K_rot[b,kv,j,c],
+ *   I_h = the r dims c of largest |q_rot[b,h,c]| (ties -> lower c),
+ * computed in fp32 from the fp32 q_rot (decisions on |q_rot| in fp32); the
+ * kept tokens and the exact attention over them are as in loki_decode.
+ *   lens       DEVICE [B] int32 per-sequence lengths as in loki_decode_varlen,
+ *              or NULL (every sequence holds S tokens).
+ *   dims       [B, Hq, r] int32 output: I_h ascending, or NULL.
+ *   info_loss  [B, Hq] fp32 output: | ||q|| - ||q_rot[I_h]|| | / ||q|| (0 for a
+ *              zero query), or NULL.  dims and info_loss 4-byte aligned.
+ * The score stage reads every rotated key row in full (the dims differ per
+ * head and step), so no lead-dims copy applies.  Sizes, ranges, workspace
+ * (loki_decode_workspace_bytes) and errors as for loki_decode.
+ */
+loki_status loki_decode_aqua(const void* q, const void* P, const void* K_rot, const void* V,
+                             const int32_t* lens, void* out, int32_t* idx, int32_t* dims, float* info_loss,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                             loki_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * loki_decode_aqua plus hipEventRecord(events[i], stream) at the stage
+ * boundaries, as loki_decode_profiled: [0] start, [1] after the rotation and
+ * the dims, [2] after the scores, [3] after the selection, [4] after the exact
+ * attention, [5] end.  events must hold 6 created events (else LOKI_ERR_NULL).
+ */
+loki_status loki_decode_aqua_profiled(const void* q, const void* P, const void* K_rot, const void* V,
+                                      const int32_t* lens, void* out, int32_t* idx, int32_t* dims,
+                                      float* info_loss, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
+                                      int32_t d, int32_t r, int32_t k, loki_dtype dt, void* workspace,
+                                      size_t workspace_bytes, hipEvent_t* events, hipStream_t stream);
+
+/*
  * Offline calibration of the basis P, the step that produces the P every
  * other entry point takes (AQUA page, appendix on the SVD: the principal
  * directions of a key matrix A are the right singular vectors of A, i.e. the

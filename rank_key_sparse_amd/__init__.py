@@ -66,6 +66,10 @@ _SIGS = {
     "loki_select_topk": ([_P, _P, _I, _I, _I, _P, _Z, _P], ctypes.c_int),
     "loki_attend": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
                     ctypes.c_int),
+    "loki_decode_aqua": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
+                         ctypes.c_int),
+    "loki_decode_aqua_profiled": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
+                                   _P, _Z, _P, _P], ctypes.c_int),
     "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
@@ -154,6 +158,50 @@ def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | No
     _check(lib.loki_project_keys_lead(_ptr(K), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, B, Hkv, S, d,
                                       _dtype_code(K), _stream(K)))
     return K_rot, K_lead
+
+
+def loki_decode_aqua(q, P, K_rot, V, r: int, k: int, lens=None, out=None, idx=None, workspace=None,
+                     dims=None, info_loss=None, events=None):
+    """Decode step whose approximate scores use, per query head, the ``r``
+    rotated dims where the query is largest in magnitude (the token selection
+    and exact attention are as in :func:`loki_decode`).  Returns ``(out, idx,
+    dims [B,Hq,r] int32, info_loss [B,Hq] float32)``."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    B, Hq, d = q.shape
+    _need(P, "P", dtype=q.dtype, ndim=3, device=dev)
+    _need(K_rot, "K_rot", dtype=q.dtype, ndim=4, device=dev)
+    _need(V, "V", dtype=q.dtype, ndim=4, device=dev)
+    Hkv, S = K_rot.shape[1], K_rot.shape[2]
+    if tuple(K_rot.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d) or tuple(P.shape) != (Hkv, d, d):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else out
+    idx = torch.empty((B, Hq, k), dtype=torch.int32, device=dev) if idx is None else idx
+    dims = torch.empty((B, Hq, r), dtype=torch.int32, device=dev) if dims is None else dims
+    info_loss = torch.empty((B, Hq), dtype=torch.float32, device=dev) if info_loss is None else info_loss
+    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
+    _need(idx, "idx", dtype=torch.int32, ndim=3, device=dev)
+    _need(dims, "dims", dtype=torch.int32, ndim=3, device=dev)
+    _need(info_loss, "info_loss", dtype=torch.float32, ndim=2, device=dev)
+    if lens is not None:
+        _need(lens, "lens", dtype=torch.int32, ndim=1, device=dev)
+        if lens.shape[0] != B:
+            raise ValueError("lens must be [B] int32")
+    dt = _dtype_code(q)
+    lib = load_library()
+    if workspace is None:
+        workspace = torch.empty(max(1, loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, q.dtype)),
+                                dtype=torch.uint8, device=dev)
+    args = (_ptr(q), _ptr(P), _ptr(K_rot), _ptr(V), _ptr(lens), _ptr(out), _ptr(idx), _ptr(dims), _ptr(info_loss),
+            B, Hq, Hkv, S, d, r, k, dt, _ptr(workspace), workspace.numel())
+    if events is None:
+        _check(lib.loki_decode_aqua(*args, _stream(q)))
+    else:
+        if len(events) != 6:
+            raise ValueError("events must hold 6 torch.cuda.Event objects")
+        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check(lib.loki_decode_aqua_profiled(*args, arr, _stream(q)))
+    return out, idx, dims, info_loss
 
 
 def loki_calibrate_workspace_bytes(B: int, Hkv: int, S: int, d: int) -> int:

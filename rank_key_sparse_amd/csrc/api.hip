@@ -149,7 +149,8 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
                                int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
                                loki_dtype dt, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* ev = nullptr,
-                               const int32_t* lens = nullptr) {
+                               const int32_t* lens = nullptr, int aqua_r = 0, int32_t* dims = nullptr,
+                               float* info = nullptr) {
   LOKI_TRY(check_dtype(dt));
   if (!q || !P || !K_rot || !V || !out || !idx) return LOKI_ERR_NULL;
   LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
@@ -168,16 +169,30 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   uint32_t* bitmap = at<uint32_t>(workspace, p.off_bitmap);
   float* part = at<float>(workspace, p.off_part);
   const void* src = K_lead ? K_lead : K_rot;
-  const int ld = K_lead ? R : d;
+  int ld = K_lead ? R : d;
   // bf16, a head's keys small enough for LDS and enough blocks to fill the
   // chip: scores and selection in one kernel, one block per query head when
   // each query head has its own key head, one block per pair of query heads
   // of a group otherwise (that kernel also rotates its queries, so the
   // rotation stage is empty); else two kernels with the keys in the workspace
-  const bool fused = dt == LOKI_BF16 && Hq == Hkv && S <= kFusedMaxS && (int64_t)B * Hq >= 256;
-  const bool pair = !fused && score_select_pair_fits(p) && (int64_t)B * Hq >= 2 * 256;
+  // query-magnitude dims (aqua_r > 0): each head scores with its own dims of
+  // the full rotated rows, so the two-kernel path with a masked query
+  const bool aqua = aqua_r > 0;
+  const bool fused = !aqua && dt == LOKI_BF16 && Hq == Hkv && S <= kFusedMaxS && (int64_t)B * Hq >= 256;
+  const bool pair = !aqua && !fused && score_select_pair_fits(p) && (int64_t)B * Hq >= 2 * 256;
+  float* qrot_s = qrot;
+  uint16_t* qsplit_s = qsplit;
+  DecodePlan ps = p;  // the score stage's plan
+  if (aqua) {
+    qrot_s = at<float>(workspace, p.off_qrot_m);
+    qsplit_s = at<uint16_t>(workspace, p.off_qsplit_m);
+    ps.r = d;
+    src = K_rot;
+    ld = d;
+  }
   if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
   if (!pair) LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
+  if (aqua) LOKI_HIP(launch_qdims(p, q, qrot, qrot_s, qsplit_s, dims, info, aqua_r, stream));
   if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
   if (fused || pair) {
     if (fused) LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
@@ -185,7 +200,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
   } else {
     uint2* mm = select_needs_minmax(S) ? at<uint2>(workspace, p.off_mm) : nullptr;
-    LOKI_HIP(launch_scores(p, src, ld, qrot, qsplit, keys, true, p.Sp, mm, stream));
+    LOKI_HIP(launch_scores(ps, src, ld, qrot_s, qsplit_s, keys, true, p.Sp, mm, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
     LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, mm, p.NSC, at<uint32_t>(workspace, p.off_masks),
                            idx, bitmap, stream, at<int32_t>(workspace, p.off_cidx),
@@ -329,6 +344,38 @@ loki_status loki_attend(const void* q, const void* P, const void* K_rot, const v
     LOKI_HIP(launch_idx_to_bitmap(p, idx, bitmap, stream));
     LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream));
     return LOKI_OK;
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_aqua(const void* q, const void* P, const void* K_rot, const void* V, const int32_t* lens,
+                             void* out, int32_t* idx, int32_t* dims, float* info_loss, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k, loki_dtype dt,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if ((reinterpret_cast<uintptr_t>(dims) & 3u) || (reinterpret_cast<uintptr_t>(info_loss) & 3u))
+      return LOKI_ERR_ALIGN;
+    return decode_impl(q, P, K_rot, nullptr, 0, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream, nullptr, lens, r, dims, info_loss);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_aqua_profiled(const void* q, const void* P, const void* K_rot, const void* V,
+                                      const int32_t* lens, void* out, int32_t* idx, int32_t* dims, float* info_loss,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r,
+                                      int32_t k, loki_dtype dt, void* workspace, size_t workspace_bytes,
+                                      hipEvent_t* events, hipStream_t stream) {
+  try {
+    if (!events) return LOKI_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return LOKI_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(dims) & 3u) || (reinterpret_cast<uintptr_t>(info_loss) & 3u))
+      return LOKI_ERR_ALIGN;
+    return decode_impl(q, P, K_rot, nullptr, 0, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                       workspace_bytes, stream, events, lens, r, dims, info_loss);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

@@ -93,6 +93,107 @@ __global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, cons
 }
 
 // ============================================================================
+// Query-magnitude dimensions (AQUA page, online phase): for each query head,
+// the r dims of q_rot with the largest magnitude, ties to the lower index.
+// One wave per head (d / 64 elements per lane).  The r-th largest magnitude
+// thr is found bit by bit on the magnitudes' bit patterns (non-negative
+// floats order as their bits): the largest thr with at least r magnitudes
+// >= thr.  The kept dims are those above thr and, of those equal to it, the
+// lowest-index ones up to r.
+// Writes the masked q_rot (zero outside the chosen dims) and its three-way
+// bf16 split for the score stage (a full-width dot product with the masked
+// query adds exact zeros for the other dims), and optionally the chosen dims
+// in ascending order and the information retention loss
+// | ||q|| - ||q_rot[I]|| | / ||q|| (AQUA page, information-retention paragraph).
+// ============================================================================
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void qdims_kernel(const T* __restrict__ q, const float* __restrict__ qrot,
+                                                    float* __restrict__ qrot_m, bf16_t* __restrict__ qsplit_m,
+                                                    int32_t* __restrict__ dims, float* __restrict__ info,
+                                                    int rows, int r) {
+  constexpr int D = 64 * EPL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // the whole wave
+  float v[EPL];
+  uint32_t a[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    v[e] = qrot[(size_t)row * D + lane + 64 * e];
+    a[e] = __float_as_uint(v[e]) & 0x7fffffffu;
+  }
+  uint32_t thr = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) cnt += __popcll(__ballot(a[e] >= cand));
+    if (cnt >= r) thr = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) above += __popcll(__ballot(a[e] > thr));
+  const int need = r - above;  // dims equal to thr still to take, lowest index first
+  const uint64_t lt = (1ull << lane) - 1ull;
+  float kept = 0.f, tot = 0.f;
+  int before = 0;  // chosen dims below this wave's current 64-block
+  int eq_before = 0;  // dims equal to thr below it
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int c = lane + 64 * e;
+    const uint64_t eqm = __ballot(a[e] == thr);
+    const bool sel = a[e] > thr || (a[e] == thr && eq_before + __popcll(eqm & lt) < need);
+    eq_before += __popcll(eqm);
+    const float m = sel ? v[e] : 0.f;
+    qrot_m[(size_t)row * D + c] = m;
+    bf16_t* o4 = qsplit_m + (size_t)row * D * 4 + c;
+    const bf16_t h = f32_to_bf16(m);
+    const float r1 = m - to_f32(h);
+    const bf16_t mid = f32_to_bf16(r1);
+    const bf16_t lo = f32_to_bf16(r1 - to_f32(mid));
+    o4[0] = h;
+    o4[D] = mid;
+    o4[2 * D] = lo;
+    o4[3 * D] = 0;
+    const uint64_t mask = __ballot(sel);
+    if (dims && sel) dims[(size_t)row * r + before + __popcll(mask & lt)] = c;
+    before += __popcll(mask);
+    kept = fmaf(m, m, kept);
+    const float x = to_f32(q[(size_t)row * D + c]);
+    tot = fmaf(x, x, tot);
+  }
+  if (info) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kept += __shfl_xor(kept, o);
+      tot += __shfl_xor(tot, o);
+    }
+    if (lane == 0) {
+      const float n = sqrtf(tot);
+      info[row] = n > 0.f ? fabsf(n - sqrtf(kept)) / n : 0.f;
+    }
+  }
+}
+
+hipError_t launch_qdims(const DecodePlan& p, const void* q, const float* qrot, float* qrot_m, uint16_t* qsplit_m,
+                        int32_t* dims, float* info, int r, hipStream_t st) {
+  const int rows = p.B * p.Hq;
+  const dim3 grid((rows + 3) / 4), block(256);
+  bf16_t* qs = reinterpret_cast<bf16_t*>(qsplit_m);
+  auto go = [&](auto ee) {
+    constexpr int E = decltype(ee)::value;
+    if (p.dt == 1)
+      hipLaunchKernelGGL((qdims_kernel<bf16_t, E>), grid, block, 0, st, static_cast<const bf16_t*>(q), qrot, qrot_m,
+                         qs, dims, info, rows, r);
+    else
+      hipLaunchKernelGGL((qdims_kernel<float, E>), grid, block, 0, st, static_cast<const float*>(q), qrot, qrot_m,
+                         qs, dims, info, rows, r);
+    return hipGetLastError();
+  };
+  return p.d == 128 ? go(std::integral_constant<int, 2>{}) : go(std::integral_constant<int, 1>{});
+}
+
+// ============================================================================
 // Approximate scores over the leading r rotated dimensions.
 // The source is either K_rot itself (row stride d) or a lead-dims copy
 // K_lead holding only the leading R >= r rotated dims of each token (row
@@ -626,6 +727,8 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
   size_t off = 0;
   p.off_qrot = off;   off = align_up(off + rows * d * sizeof(float), 256);
   p.off_qsplit = off; off = align_up(off + rows * 4 * d * sizeof(uint16_t), 256);
+  p.off_qrot_m = off; off = align_up(off + rows * d * sizeof(float), 256);
+  p.off_qsplit_m = off; off = align_up(off + rows * 4 * d * sizeof(uint16_t), 256);
   p.off_keys = off;   off = align_up(off + rows * (size_t)p.Sp * sizeof(uint32_t), 256);
   p.off_mm = off;     off = align_up(off + rows * (size_t)p.NSC * sizeof(uint2), 256);
   p.off_masks = off;  off = align_up(off + rows * (size_t)(p.Sp / 16) * sizeof(uint32_t), 256);

@@ -29,6 +29,8 @@ struct DecodePlan {
   // extremes [row][NSC] (uint2 min, max), selection masks [row][Sp/16] (used
   // when a row's keys do not fit in LDS), bitmap [row][W], attention partials
   size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_cidx, off_ckey, off_bitmap, off_part, bytes;
+  // query-magnitude scoring: q_rot masked to each head's chosen dims, and its split
+  size_t off_qrot_m, off_qsplit_m;
   // per-sequence lengths [B] on the device (each clamped into [1, S]), or
   // null: every sequence holds S tokens
   const int32_t* lens = nullptr;
@@ -70,6 +72,11 @@ hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* 
                          int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
                          int32_t* cidx = nullptr, uint32_t* ckey = nullptr, const int32_t* lens = nullptr,
                          int Hq = 1);
+// Query-magnitude dims: the r dims of largest |q_rot| per head; writes the
+// masked q_rot and its split, and (when non-null) the dims ascending and the
+// information retention loss per head.
+hipError_t launch_qdims(const DecodePlan& p, const void* q, const float* qrot, float* qrot_m, uint16_t* qsplit_m,
+                        int32_t* dims, float* info, int r, hipStream_t st);
 hipError_t launch_scores_to_keys(const float* scores, uint32_t* keys, uint2* mm, int nmm, int rows,
                                  int S, int Sp, hipStream_t st);
 hipError_t launch_idx_to_bitmap(const DecodePlan& p, const int32_t* idx, uint32_t* bitmap,

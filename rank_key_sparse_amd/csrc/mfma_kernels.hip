@@ -135,6 +135,21 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qa[grp][s] = q_rows(qsplit, head0 + 4 * grp, d, G - 4 * grp, r, m, 32 * s + 8 * q);
+  // k-steps up to the last one where some head's query is non-zero (a query
+  // masked to a few dims, as for query-magnitude scoring, may end early):
+  // later k-steps re-read the first k-step's columns (cached, no new HBM
+  // traffic) and multiply them by zeros, so every load stays unconditional
+  int kuse = 0;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    bool nz = false;
+#pragma unroll
+    for (int grp = 0; grp < NGRP; ++grp) {
+      const uint4 v = __builtin_bit_cast(uint4, qa[grp][s]);
+      nz = nz || ((v.x | v.y | v.z | v.w) & 0x7fff7fffu) != 0u;
+    }
+    if (__ballot(nz)) kuse = s + 1;  // the same in every wave: they hold the same operands
+  }
 
   const bf16_t* base = src + (size_t)bk * S * ld;
   __shared__ uint32_t smn[GT], smx[GT];
@@ -148,7 +163,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const bf16_t* __restric
     for (int u = 0; u < U; ++u) {
       const int t = min(t0 + 16 * (wave + 4 * (bi * U + u)) + m, t1 - 1);  // t1 >= 1
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
+      for (int s = 0; s < KS; ++s)
+        a[u][s] = ldg16(base + (size_t)t * ld + min((s < kuse ? 32 * s : 0) + 8 * q, ld - 8));
     }
   };
   auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {

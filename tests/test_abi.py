@@ -181,3 +181,30 @@ def test_calibrate_rejects(lib):
     assert lib.loki_calibrate_workspace_bytes(1 << 16, 2, 1 << 16, 128) == 0
     g = lib.loki_calibrate_pca_profiled
     assert g(A, A, A, 1, 2, 512, 128, BF16, A2, big, NULLP, NULLP) == NULL
+
+
+def test_decode_aqua_rejects(lib):
+    f = lib.loki_decode_aqua
+    # (q, P, K_rot, V, lens, out, idx, dims, info, B, Hq, Hkv, S, d, r, k, dt, ws, wsb, stream)
+    base = [A, A, A, A, NULLP, A, A, NULLP, NULLP, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 1 << 30, NULLP]
+
+    def call(**kw):
+        a = list(base)
+        names = ["q", "P", "K", "V", "lens", "out", "idx", "dims", "info", "B", "Hq", "Hkv", "S", "d", "r", "k",
+                 "dt", "ws", "wsb"]
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    for n in ("q", "P", "K", "V", "out", "idx"):
+        assert call(**{n: NULLP}) == NULL, n
+    assert call(r=0) == RANGE
+    assert call(r=129) == RANGE
+    assert call(k=101) == RANGE
+    assert call(Hq=5) == SHAPE
+    assert call(d=96) == UNSUPPORTED
+    assert call(dt=9) == DTYPE
+    assert call(dims=ctypes.c_void_p(0x10002)) == ALIGN
+    assert call(info=ctypes.c_void_p(0x10001)) == ALIGN
+    assert call(out=MIS) == ALIGN
+    assert call(wsb=16) == WORKSPACE
