@@ -11,7 +11,7 @@ attention, brute-force top-k on tiny inputs, closed forms); see the test file
 of oracle pins.
 """
 
-from . import aqua  # noqa: F401
+from . import aqua, asym  # noqa: F401
 from .calibrate import calibrate, energy_fraction, fix_signs  # noqa: F401
 from .loki import (approx_scores, attend, decode, decode_varlen, dense, project,  # noqa: F401
                    rotate_queries, select, topk_indices)
