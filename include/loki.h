@@ -97,6 +97,8 @@ loki_status loki_project_keys(const void* K, const void* P, void* K_rot,
  * As loki_project_keys, and in the same pass also writes the leading R
  * rotated dims of every cached key into a separate dense array:
  *   K_lead [B, Hkv, S, R]   K_lead[b,kv,j,c] = K_rot[b,kv,j,c] for c < R
+ * K_rot may be NULL: then only K_lead is written (a key index K B for
+ * loki_decode_asym, with P = B).
  * K_lead is a second copy of data K_rot already holds (R/d of the key cache
  * in extra memory).  It lets the approximate-score stage of
  * loki_decode_lead stream R*elem bytes per token contiguously instead of a
@@ -280,6 +282,37 @@ loki_status loki_decode_aqua_profiled(const void* q, const void* P, const void* 
                                       float* info_loss, int32_t B, int32_t Hq, int32_t Hkv, int32_t S,
                                       int32_t d, int32_t r, int32_t k, loki_dtype dt, void* workspace,
                                       size_t workspace_bytes, hipEvent_t* events, hipStream_t stream);
+
+/*
+ * Decode step with an asymmetric low-rank scoring index (page "SAKI:
+ * Score-Aware Low-Rank Key Indexing with Random-Matrix Noise Correction for
+ * KV Retrieval", abstract: approximate scores (q A_r) . (k B_r) with a
+ * query-side and a key-side projection).  For each query head h of key head kv:
+ *   s_j = sum_{c<r} (q[b,h] A[kv])[c] * K_idx[b,kv,j,c]
+ * (fp32 accumulation, the query-side product as for q_rot), the k largest
+ * s_j kept (ties -> lower index, idx ascending), and exact attention over
+ * them with the query and keys themselves:
+ *   out[b,h] = sum_{j in idx} softmax_j(q[b,h] . K[b,kv,j] / sqrt(d)) V[b,kv,j].
+ *   A      [Hkv, d, d] in dt: the query-side projection in its first r
+ *          columns (the other columns are not used);
+ *   K_idx  [B, Hkv, S, R] in dt, r <= R <= d, R*elem a multiple of 16: the key
+ *          index K B (loki_project_keys_lead with K_rot = NULL writes it);
+ *   K, V   [B, Hkv, S, d] the keys (not rotated) and values;
+ *   lens   DEVICE [B] int32 per-sequence lengths or NULL, as in loki_decode_varlen.
+ * Other arguments, workspace (loki_decode_workspace_bytes) and errors as for
+ * loki_decode_lead (K_idx NULL -> LOKI_ERR_NULL).
+ */
+loki_status loki_decode_asym(const void* q, const void* A, const void* K_idx, int32_t R, const void* K,
+                             const void* V, const int32_t* lens, void* out, int32_t* idx, int32_t B,
+                             int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                             loki_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* loki_decode_asym plus the six stage events of loki_decode_profiled. */
+loki_status loki_decode_asym_profiled(const void* q, const void* A, const void* K_idx, int32_t R, const void* K,
+                                      const void* V, const int32_t* lens, void* out, int32_t* idx, int32_t B,
+                                      int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                                      loki_dtype dt, void* workspace, size_t workspace_bytes,
+                                      hipEvent_t* events, hipStream_t stream);
 
 /*
  * Offline calibration of the basis P, the step that produces the P every

@@ -10,4 +10,4 @@ storage dtype (fp32 or bf16, round-to-nearest-even by torch's cast).
 
 from .configs import CONFIGS, Config, config  # noqa: F401
 from .gen import (make_basis, make_inputs, make_integer_inputs,  # noqa: F401
-                  ordered_scores_fixture, spectrum)
+                  make_query_samples, ordered_scores_fixture, spectrum)

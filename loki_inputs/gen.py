@@ -39,7 +39,7 @@ import torch
 from .configs import Config
 
 _MAGIC = 0x4C4F4B49
-ROLE_P, ROLE_K, ROLE_Q, ROLE_V, ROLE_HEAVY, ROLE_NOISE, ROLE_INT = range(7)
+ROLE_P, ROLE_K, ROLE_Q, ROLE_V, ROLE_HEAVY, ROLE_NOISE, ROLE_INT, ROLE_QSAMPLE = range(8)
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -105,6 +105,21 @@ def make_inputs(cfg: Config, need_K: bool = False, seed: int = 0) -> dict:
             V[b, kv] = _to(rng(cfg.cfg_no, ROLE_V, b, kv, seed).standard_normal((S, d)), cfg.dtype)
     return {"q": q, "P": _to(P64, cfg.dtype), "K_rot": K_rot, "V": V, "K": K,
             "heavy_idx": heavy_idx, "cfg": cfg, "P64": P64}
+
+
+def make_query_samples(cfg: Config, n: int, seed: int = 0) -> torch.Tensor:
+    """``n`` further queries per query head drawn like the workload's queries
+    (spectrum in the basis of the key head they read), as calibration data:
+    ``[n, Hq, d]`` in ``cfg.dtype``."""
+    s = spectrum(cfg)
+    out = np.empty((n, cfg.Hq, cfg.d))
+    for kv in range(cfg.Hkv):
+        P = make_basis(cfg.d, cfg.cfg_no, kv, seed)
+        for g in range(cfg.G):
+            h = kv * cfg.G + g
+            z = rng(cfg.cfg_no, ROLE_QSAMPLE, 0, h, seed).standard_normal((n, cfg.d)) * s
+            out[:, h] = z @ P.T
+    return _to(out, cfg.dtype)
 
 
 def make_integer_inputs(B: int, Hq: int, Hkv: int, d: int, S: int, dtype: str,

@@ -70,6 +70,10 @@ _SIGS = {
                          ctypes.c_int),
     "loki_decode_aqua_profiled": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
                                    _P, _Z, _P, _P], ctypes.c_int),
+    "loki_decode_asym": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P],
+                         ctypes.c_int),
+    "loki_decode_asym_profiled": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
+                                   _P, _Z, _P, _P], ctypes.c_int),
     "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
@@ -132,12 +136,29 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | None = None,
-                      R: int | None = None, K_lead: torch.Tensor | None = None):
+                      R: int | None = None, K_lead: torch.Tensor | None = None, lead_only: bool = False):
     """``K_rot[b, kv] = K[b, kv] @ P[kv]``; K [B,Hkv,S,d], P [Hkv,d,d].
 
     With ``R``, also writes the lead-dims copy ``K_lead = K_rot[..., :R]``
-    (contiguous) in the same pass and returns ``(K_rot, K_lead)``.
+    (contiguous) in the same pass and returns ``(K_rot, K_lead)``; with
+    ``lead_only`` only ``K_lead`` is written and returned (a key index).
     """
+    if lead_only:
+        if R is None:
+            raise ValueError("lead_only needs R")
+        _need(K, "K", ndim=4)
+        _need(P, "P", dtype=K.dtype, ndim=3, device=K.device)
+        B, Hkv, S, d = K.shape
+        if tuple(P.shape) != (Hkv, d, d):
+            raise ValueError("P must be [Hkv, d, d]")
+        if K_lead is None:
+            K_lead = torch.empty((B, Hkv, S, R), dtype=K.dtype, device=K.device)
+        _need(K_lead, "K_lead", dtype=K.dtype, ndim=4, device=K.device)
+        if tuple(K_lead.shape) != (B, Hkv, S, R):
+            raise ValueError("K_lead must be [B, Hkv, S, R]")
+        _check(load_library().loki_project_keys_lead(_ptr(K), _ptr(P), None, _ptr(K_lead), R, B, Hkv, S, d,
+                                                     _dtype_code(K), _stream(K)))
+        return K_lead
     _need(K, "K", ndim=4)
     _need(P, "P", dtype=K.dtype, ndim=3, device=K.device)
     B, Hkv, S, d = K.shape
@@ -202,6 +223,46 @@ def loki_decode_aqua(q, P, K_rot, V, r: int, k: int, lens=None, out=None, idx=No
         arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])
         _check(lib.loki_decode_aqua_profiled(*args, arr, _stream(q)))
     return out, idx, dims, info_loss
+
+
+def loki_decode_asym(q, A, K_idx, K, V, r: int, k: int, lens=None, out=None, idx=None, workspace=None,
+                     events=None):
+    """Decode step with an asymmetric scoring index: scores ``(q A[kv])[:r] .
+    K_idx[..., :r]``, the k best tokens, exact attention with ``q`` over the
+    unrotated keys ``K``.  A [Hkv,d,d] (first r columns used), K_idx
+    [B,Hkv,S,R].  Returns ``(out, idx)``."""
+    _need(q, "q", ndim=3)
+    dev = q.device
+    B, Hq, d = q.shape
+    for t, n in ((A, "A"), (K_idx, "K_idx"), (K, "K"), (V, "V")):
+        _need(t, n, dtype=q.dtype, device=dev)
+    Hkv, S = K.shape[1], K.shape[2]
+    R = K_idx.shape[3]
+    if (tuple(A.shape) != (Hkv, d, d) or tuple(K.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d)
+            or tuple(K_idx.shape[:3]) != (B, Hkv, S)):
+        raise ValueError("inconsistent shapes")
+    out = torch.empty_like(q) if out is None else out
+    idx = torch.empty((B, Hq, k), dtype=torch.int32, device=dev) if idx is None else idx
+    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
+    _need(idx, "idx", dtype=torch.int32, ndim=3, device=dev)
+    if lens is not None:
+        _need(lens, "lens", dtype=torch.int32, ndim=1, device=dev)
+        if lens.shape[0] != B:
+            raise ValueError("lens must be [B] int32")
+    lib = load_library()
+    if workspace is None:
+        workspace = torch.empty(max(1, loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, q.dtype)),
+                                dtype=torch.uint8, device=dev)
+    args = (_ptr(q), _ptr(A), _ptr(K_idx), R, _ptr(K), _ptr(V), _ptr(lens), _ptr(out), _ptr(idx), B, Hq, Hkv, S,
+            d, r, k, _dtype_code(q), _ptr(workspace), workspace.numel())
+    if events is None:
+        _check(lib.loki_decode_asym(*args, _stream(q)))
+    else:
+        if len(events) != 6:
+            raise ValueError("events must hold 6 torch.cuda.Event objects")
+        arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check(lib.loki_decode_asym_profiled(*args, arr, _stream(q)))
+    return out, idx
 
 
 def loki_calibrate_workspace_bytes(B: int, Hkv: int, S: int, d: int) -> int:

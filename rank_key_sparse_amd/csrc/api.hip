@@ -112,7 +112,8 @@ loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, vo
                                    int32_t R, int32_t B, int32_t Hkv, int32_t S, int32_t d,
                                    loki_dtype dt, hipStream_t stream) {
   try {
-    LOKI_TRY(check_project(K, P, K_rot, B, Hkv, S, d, dt));
+    // K_rot may be NULL (only the lead dims wanted); K_lead stands in for its checks
+    LOKI_TRY(check_project(K, P, K_rot ? K_rot : K_lead, B, Hkv, S, d, dt));
     LOKI_TRY(check_lead(K_lead, R, d, 0, dt));
     return from_hip(launch_project(K, P, K_rot, K_lead, R, B, Hkv, S, d, (int)dt, stream));
   } catch (...) {
@@ -150,7 +151,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
                                loki_dtype dt, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* ev = nullptr,
                                const int32_t* lens = nullptr, int aqua_r = 0, int32_t* dims = nullptr,
-                               float* info = nullptr) {
+                               float* info = nullptr, bool plain_attn = false) {
   LOKI_TRY(check_dtype(dt));
   if (!q || !P || !K_rot || !V || !out || !idx) return LOKI_ERR_NULL;
   LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
@@ -207,6 +208,9 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
                            at<uint32_t>(workspace, p.off_ckey), lens, Hq));
   }
   if (ev) LOKI_HIP(hipEventRecord(ev[3], stream));
+  // asymmetric index: the score stage used q P (P the query-side matrix);
+  // the exact stage takes the query itself against the unrotated keys
+  if (plain_attn) LOKI_HIP(launch_qplain(p, q, qrot, qsplit, stream));
   LOKI_HIP(launch_attend(p, K_rot, V, qrot, qsplit, bitmap, part, out, stream, ev ? ev[4] : nullptr));
   if (ev) LOKI_HIP(hipEventRecord(ev[5], stream));
   return LOKI_OK;
@@ -376,6 +380,45 @@ loki_status loki_decode_aqua_profiled(const void* q, const void* P, const void* 
       return LOKI_ERR_ALIGN;
     return decode_impl(q, P, K_rot, nullptr, 0, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
                        workspace_bytes, stream, events, lens, r, dims, info_loss);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+static loki_status decode_asym_impl(const void* q, const void* A, const void* K_idx, int32_t R, const void* K,
+                                    const void* V, const int32_t* lens, void* out, int32_t* idx, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                                    loki_dtype dt, void* ws, size_t wsb, hipEvent_t* ev, hipStream_t stream) {
+  if (!K_idx) return LOKI_ERR_NULL;
+  // the decode with A in place of the basis, the key index as the lead-dims
+  // source, the keys themselves for the exact stage
+  return decode_impl(q, A, K, K_idx, R, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, ws, wsb, stream, ev, lens, 0,
+                     nullptr, nullptr, true);
+}
+
+loki_status loki_decode_asym(const void* q, const void* A, const void* K_idx, int32_t R, const void* K,
+                             const void* V, const int32_t* lens, void* out, int32_t* idx, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k, loki_dtype dt,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    return decode_asym_impl(q, A, K_idx, R, K, V, lens, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                            workspace_bytes, nullptr, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_decode_asym_profiled(const void* q, const void* A, const void* K_idx, int32_t R, const void* K,
+                                      const void* V, const int32_t* lens, void* out, int32_t* idx, int32_t B,
+                                      int32_t Hq, int32_t Hkv, int32_t S, int32_t d, int32_t r, int32_t k,
+                                      loki_dtype dt, void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                                      hipStream_t stream) {
+  try {
+    if (!events) return LOKI_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+      if (!events[i]) return LOKI_ERR_NULL;
+    return decode_asym_impl(q, A, K_idx, R, K, V, lens, out, idx, B, Hq, Hkv, S, d, r, k, dt, workspace,
+                            workspace_bytes, events, stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

@@ -93,6 +93,41 @@ __global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, cons
 }
 
 // ============================================================================
+// The query itself in the layouts the attention stage reads (fp32 and the
+// three-way bf16 split), for an exact stage over keys that are not rotated
+// (the asymmetric scoring index keeps the keys as they are).
+// ============================================================================
+template <typename T>
+__global__ __launch_bounds__(256) void qplain_kernel(const T* __restrict__ q, float* __restrict__ qf,
+                                                     bf16_t* __restrict__ qsplit, int n, int d) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int row = i / d, c = i - row * d;
+  const float v = to_f32(q[i]);
+  qf[i] = v;
+  bf16_t* o4 = qsplit + (size_t)row * d * 4 + c;
+  const bf16_t h = f32_to_bf16(v);
+  const float r1 = v - to_f32(h);
+  const bf16_t mid = f32_to_bf16(r1);
+  o4[0] = h;
+  o4[d] = mid;
+  o4[2 * d] = f32_to_bf16(r1 - to_f32(mid));
+  o4[3 * d] = 0;
+}
+
+hipError_t launch_qplain(const DecodePlan& p, const void* q, float* qf, uint16_t* qsplit, hipStream_t st) {
+  const int n = p.B * p.Hq * p.d;
+  bf16_t* qs = reinterpret_cast<bf16_t*>(qsplit);
+  if (p.dt == 1)
+    hipLaunchKernelGGL(qplain_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, st, static_cast<const bf16_t*>(q),
+                       qf, qs, n, p.d);
+  else
+    hipLaunchKernelGGL(qplain_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, st, static_cast<const float*>(q),
+                       qf, qs, n, p.d);
+  return hipGetLastError();
+}
+
+// ============================================================================
 // Query-magnitude dimensions (AQUA page, online phase): for each query head,
 // the r dims of q_rot with the largest magnitude, ties to the lower index.
 // One wave per head (d / 64 elements per lane).  The r-th largest magnitude

@@ -72,6 +72,8 @@ hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* 
                          int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
                          int32_t* cidx = nullptr, uint32_t* ckey = nullptr, const int32_t* lens = nullptr,
                          int Hq = 1);
+// The query itself as fp32 and split (attention over unrotated keys).
+hipError_t launch_qplain(const DecodePlan& p, const void* q, float* qf, uint16_t* qsplit, hipStream_t st);
 // Query-magnitude dims: the r dims of largest |q_rot| per head; writes the
 // masked q_rot and its split, and (when non-null) the dims ascending and the
 // information retention loss per head.

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(const bf16_t* __restr
   __syncthreads();
 
   const bf16_t* Kb = K + (size_t)bk * S * D;
-  bf16_t* Ob = out + (size_t)bk * S * D;
+  bf16_t* Ob = out ? out + (size_t)bk * S * D : nullptr;  // null: only the lead dims are written
   bf16_t* Lb = lead ? lead + (size_t)bk * S * R : nullptr;
   const int m = lane & 31, half = lane >> 5;
   bf16_t* so = sO[wave];
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void project_bf16_kernel(const bf16_t* __restr
       const int grow = row0 + rr;
       const uint4 v = *reinterpret_cast<const uint4*>(&so[rr * PS + c8]);
       if (grow < S) {
-        *reinterpret_cast<uint4*>(Ob + (size_t)grow * D + c8) = v;
+        if (out) *reinterpret_cast<uint4*>(Ob + (size_t)grow * D + c8) = v;
         if (Lb && c8 < R) *reinterpret_cast<uint4*>(Lb + (size_t)grow * R + c8) = v;
       }
     }
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void project_f32_kernel(const float* __restric
   const float* Pk = P + (size_t)kv * D * D;
   for (int i = threadIdx.x; i < D * D; i += 256) sP[i] = Pk[i];
   const float* Kb = K + (size_t)bk * S * D;
-  float* Ob = out + (size_t)bk * S * D;
+  float* Ob = out ? out + (size_t)bk * S * D : nullptr;
   float* Lb = lead ? lead + (size_t)bk * S * R : nullptr;
   constexpr int CPT = D / 4;   // threads per row (4 columns each)
   constexpr int RPP = 256 / CPT;
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void project_f32_kernel(const float* __restric
       }
       if (row0 + rr < S) {
         const float4 o = make_float4(a0, a1, a2, a3);
-        *reinterpret_cast<float4*>(Ob + (size_t)(row0 + rr) * D + c4) = o;
+        if (out) *reinterpret_cast<float4*>(Ob + (size_t)(row0 + rr) * D + c4) = o;
         if (Lb && c4 < R) *reinterpret_cast<float4*>(Lb + (size_t)(row0 + rr) * R + c4) = o;
       }
     }

@@ -208,3 +208,35 @@ def test_decode_aqua_rejects(lib):
     assert call(info=ctypes.c_void_p(0x10001)) == ALIGN
     assert call(out=MIS) == ALIGN
     assert call(wsb=16) == WORKSPACE
+
+
+def test_decode_asym_rejects(lib):
+    f = lib.loki_decode_asym
+    # (q, A, K_idx, R, K, V, lens, out, idx, B, Hq, Hkv, S, d, r, k, dt, ws, wsb, stream)
+    names = ["q", "A", "K_idx", "R", "K", "V", "lens", "out", "idx", "B", "Hq", "Hkv", "S", "d", "r", "k", "dt",
+             "ws", "wsb"]
+    base = [A, A, A, 32, A, A, NULLP, A, A, 1, 4, 2, 100, 128, 8, 10, BF16, A2, 1 << 30]
+
+    def call(**kw):
+        a = list(base)
+        for n, v in kw.items():
+            a[names.index(n)] = v
+        return f(*a, NULLP)
+
+    for n in ("q", "A", "K_idx", "K", "V", "out", "idx"):
+        assert call(**{n: NULLP}) == NULL, n
+    assert call(r=33) == RANGE          # r > R
+    assert call(R=0) == RANGE
+    assert call(R=12) == UNSUPPORTED    # R * 2 bytes not a multiple of 16
+    assert call(K_idx=MIS) == ALIGN
+    assert call(k=0) == RANGE
+    assert call(wsb=8) == WORKSPACE
+    assert lib.loki_decode_asym_profiled(*base, NULLP, NULLP) == NULL
+
+
+def test_project_lead_only_rejects(lib):
+    f = lib.loki_project_keys_lead
+    # K_rot may be NULL; K_lead then carries the output checks
+    assert f(A, A, NULLP, NULLP, 32, 1, 1, 8, 128, BF16, NULLP) == NULL
+    assert f(A, A, NULLP, MIS, 32, 1, 1, 8, 128, BF16, NULLP) == ALIGN
+    assert f(A, A, NULLP, A, 0, 1, 1, 8, 128, BF16, NULLP) == RANGE
