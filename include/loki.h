@@ -354,6 +354,35 @@ loki_status loki_calibrate_pca_profiled(const void* K, void* P, double* eigvals,
                                         int32_t S, int32_t d, loki_dtype dt, void* workspace,
                                         size_t workspace_bytes, hipEvent_t* events, hipStream_t stream);
 
+/*
+ * Calibration of the asymmetric scoring index taken by loki_decode_asym
+ * (page "SAKI: Score-Aware Low-Rank Key Indexing with Random-Matrix Noise
+ * Correction for KV Retrieval", abstract: the optimal rank-r factors of the
+ * covariance-weighted score distortion come from the SVD of the
+ * covariance-weighted query-key operator).  Per key/value head kv, with
+ *   Cq = mean of q^T q over the query samples of the heads of kv's group,
+ *   Ck = mean of k^T k over the key rows of all batch elements of kv,
+ *   W  = Cq^{1/2} Ck^{1/2} = U S V^T,
+ * the factors minimising || Cq^{1/2} (I - A_r B_r^T) Ck^{1/2} ||_F are
+ *   A_r = Cq^{-1/2} U_r S_r^{1/2},  B_r = Ck^{-1/2} V_r S_r^{1/2}
+ * (pseudo-inverse roots: eigenvalues below 1e-12 of the largest count as
+ * zero).  Written as A [Hkv, d, d] and Bm [Hkv, d, d] in dt with the factors
+ * in the first r columns and zeros after (the layout loki_decode_asym and
+ * loki_project_keys_lead take).  The columns are unique up to a common sign
+ * per column pair (and rotations within equal singular values); A_r B_r^T is
+ * unique when S_r > S_{r+1}.  All arithmetic in fp64 (Gram matrices as in
+ * loki_calibrate_pca, Jacobi eigendecompositions).
+ *   q_samples [N, Hq, d] query samples in dt;  K [B, Hkv, S, d] keys in dt.
+ * Sizes: N, Hq, B, Hkv, S >= 1, Hq % Hkv == 0, B*S < 2^31 (LOKI_ERR_SHAPE);
+ * d in {64, 128} (LOKI_ERR_UNSUPPORTED); 1 <= r <= d (LOKI_ERR_RANGE).
+ * Workspace of loki_calibrate_asym_workspace_bytes bytes.
+ */
+size_t loki_calibrate_asym_workspace_bytes(int32_t N, int32_t Hq, int32_t B, int32_t Hkv, int32_t S,
+                                          int32_t d, int32_t r);
+loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, void* Bm, int32_t N,
+                                int32_t Hq, int32_t B, int32_t Hkv, int32_t S, int32_t d, int32_t r,
+                                loki_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

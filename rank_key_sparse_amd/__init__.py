@@ -74,6 +74,8 @@ _SIGS = {
                          ctypes.c_int),
     "loki_decode_asym_profiled": ([_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int,
                                    _P, _Z, _P, _P], ctypes.c_int),
+    "loki_calibrate_asym_workspace_bytes": ([_I, _I, _I, _I, _I, _I, _I], _Z),
+    "loki_calibrate_asym": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
@@ -263,6 +265,30 @@ def loki_decode_asym(q, A, K_idx, K, V, r: int, k: int, lens=None, out=None, idx
         arr = (ctypes.c_void_p * 6)(*[ctypes.c_void_p(e.cuda_event) for e in events])
         _check(lib.loki_decode_asym_profiled(*args, arr, _stream(q)))
     return out, idx
+
+
+def loki_calibrate_asym(q_samples, K, r: int, A=None, Bm=None, workspace=None):
+    """Asymmetric scoring index factors from query samples [N,Hq,d] and keys
+    [B,Hkv,S,d]: ``(A, Bm)``, each [Hkv,d,d] in the keys' dtype with the
+    rank-r factors in the first r columns (zeros after)."""
+    _need(q_samples, "q_samples", ndim=3)
+    dev = q_samples.device
+    _need(K, "K", dtype=q_samples.dtype, ndim=4, device=dev)
+    N, Hq, d = q_samples.shape
+    B, Hkv, S, dk = K.shape
+    if dk != d:
+        raise ValueError("inconsistent head dims")
+    A = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev) if A is None else A
+    Bm = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev) if Bm is None else Bm
+    _need(A, "A", dtype=K.dtype, ndim=3, device=dev)
+    _need(Bm, "Bm", dtype=K.dtype, ndim=3, device=dev)
+    lib = load_library()
+    if workspace is None:
+        nb = int(lib.loki_calibrate_asym_workspace_bytes(N, Hq, B, Hkv, S, d, r))
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(lib.loki_calibrate_asym(_ptr(q_samples), _ptr(K), _ptr(A), _ptr(Bm), N, Hq, B, Hkv, S, d, r,
+                                   _dtype_code(K), _ptr(workspace), workspace.numel(), _stream(K)))
+    return A, Bm
 
 
 def loki_calibrate_workspace_bytes(B: int, Hkv: int, S: int, d: int) -> int:

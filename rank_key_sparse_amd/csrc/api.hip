@@ -473,4 +473,35 @@ loki_status loki_calibrate_pca_profiled(const void* K, void* P, double* eigvals,
   }
 }
 
+size_t loki_calibrate_asym_workspace_bytes(int32_t N, int32_t Hq, int32_t B, int32_t Hkv, int32_t S, int32_t d,
+                                          int32_t r) {
+  try {
+    AsymPlan p;
+    if ((int64_t)B * S > 0x7fffffffLL || !make_asym_plan(p, N, Hq, B, Hkv, S, d, r, 1)) return 0;
+    return p.bytes;
+  } catch (...) {
+    return 0;
+  }
+}
+
+loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, void* Bm, int32_t N, int32_t Hq,
+                                int32_t B, int32_t Hkv, int32_t S, int32_t d, int32_t r, loki_dtype dt,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    LOKI_TRY(check_dtype(dt));
+    if (!q_samples || !K || !A || !Bm) return LOKI_ERR_NULL;
+    if (N < 1 || Hq < 1 || B < 1 || Hkv < 1 || S < 1 || d < 1 || Hq % Hkv) return LOKI_ERR_SHAPE;
+    if ((int64_t)B * S > 0x7fffffffLL || (int64_t)Hq > kMaxRows) return LOKI_ERR_SHAPE;
+    if (d != 64 && d != 128) return LOKI_ERR_UNSUPPORTED;
+    if (r < 1 || r > d) return LOKI_ERR_RANGE;
+    if (!aligned16(q_samples) || !aligned16(K) || !aligned16(A) || !aligned16(Bm)) return LOKI_ERR_ALIGN;
+    AsymPlan p;
+    if (!make_asym_plan(p, N, Hq, B, Hkv, S, d, r, (int)dt)) return LOKI_ERR_INTERNAL;
+    LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
+    return from_hip(launch_calibrate_asym(p, q_samples, K, A, Bm, workspace, stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

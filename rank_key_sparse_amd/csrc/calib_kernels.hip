@@ -22,6 +22,8 @@
 //       positive, P written.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -499,15 +501,11 @@ __global__ __launch_bounds__(kJacobiThreads) void eig_out_kernel(const double* _
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* eigvals, void* ws,
-                            hipStream_t st, hipEvent_t* ev) {
-  char* w = static_cast<char*>(ws);
-  double* part = reinterpret_cast<double*>(w + p.off_part);
-  double* C = reinterpret_cast<double*>(w + p.off_C);
-  double* Vt = reinterpret_cast<double*>(w + p.off_V);
+// Gram partials of the plan's rows and their sum into C [Hkv][d][d]; the
+// event (may be null) is recorded between the two launches.
+static hipError_t launch_gram(const CalibPlan& p, const void* K, double* part, double* C, hipStream_t st,
+                              hipEvent_t mid) {
   const int D = p.d, DD = D * D;
-  hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   const dim3 ggrid(p.nblk, p.Hkv);
   if (p.dt == 1) {
     const bf16_t* k = static_cast<const bf16_t*>(K);
@@ -526,31 +524,47 @@ hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* 
       hipLaunchKernelGGL((gram_f32_kernel<64>), ggrid, dim3(256), 0, st, k, part, p.Hkv, p.S, p.N, p.rows,
                          p.nblk);
   }
+  hipError_t e;
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gram_reduce_kernel, dim3((DD + 255) / 256, p.Hkv), dim3(256), 0, st, part, C, p.nblk,
-                     DD);
+  if (mid && (e = hipEventRecord(mid, st)) != hipSuccess) return e;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3((DD + 255) / 256, p.Hkv), dim3(256), 0, st, part, C, p.nblk, DD);
+  return hipGetLastError();
+}
+
+// Jacobi on the H symmetric matrices C [H][d][d]: unsorted eigenvalues to
+// lam_raw [H][d], eigenvectors as the columns of V [H][d][d].
+static hipError_t launch_sym_eig(int D, int H, const double* C, double2* rlog, int* nr, double* lam_raw, double* V,
+                                 hipStream_t st) {
+  const size_t lds = (size_t)D * (D + 1) * sizeof(double);
+  hipError_t e;
+  auto kc = (D == 128) ? &jacobi_c_kernel<128> : &jacobi_c_kernel<64>;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kc), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL(kc, dim3(H), dim3(kJacobiThreads), lds, st, C, rlog, nr, lam_raw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if (D == 128)
+    hipLaunchKernelGGL(jacobi_v_kernel<128>, dim3(128 / kJacobiVRows, H), dim3(64 * kJacobiVRows), 0, st, rlog, nr, V);
+  else
+    hipLaunchKernelGGL(jacobi_v_kernel<64>, dim3(64 / kJacobiVRows, H), dim3(32 * kJacobiVRows), 0, st, rlog, nr, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* eigvals, void* ws,
+                            hipStream_t st, hipEvent_t* ev) {
+  char* w = static_cast<char*>(ws);
+  double* part = reinterpret_cast<double*>(w + p.off_part);
+  double* C = reinterpret_cast<double*>(w + p.off_C);
+  double* Vt = reinterpret_cast<double*>(w + p.off_V);
   double2* rlog = reinterpret_cast<double2*>(w + p.off_log);
   int* nr = reinterpret_cast<int*>(w + p.off_nr);
   double* lam_raw = reinterpret_cast<double*>(w + p.off_lam);
-  const size_t lds = (size_t)D * (D + 1) * sizeof(double);
-  {
-    auto kc = (D == 128) ? &jacobi_c_kernel<128> : &jacobi_c_kernel<64>;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(kc), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(kc, dim3(p.Hkv), dim3(kJacobiThreads), lds, st, C, rlog, nr, lam_raw);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (D == 128)
-    hipLaunchKernelGGL(jacobi_v_kernel<128>, dim3(128 / kJacobiVRows, p.Hkv), dim3(64 * kJacobiVRows), 0, st, rlog,
-                       nr, Vt);
-  else
-    hipLaunchKernelGGL(jacobi_v_kernel<64>, dim3(64 / kJacobiVRows, p.Hkv), dim3(32 * kJacobiVRows), 0, st, rlog,
-                       nr, Vt);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int D = p.d;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if ((e = launch_gram(p, K, part, C, st, ev ? ev[1] : nullptr)) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if ((e = launch_sym_eig(D, p.Hkv, C, rlog, nr, lam_raw, Vt, st)) != hipSuccess) return e;
   if (p.dt == 1) {
     auto ko = (D == 128) ? &eig_out_kernel<128, bf16_t> : &eig_out_kernel<64, bf16_t>;
     hipLaunchKernelGGL(ko, dim3(p.Hkv), dim3(kJacobiThreads), 0, st, Vt, lam_raw, static_cast<bf16_t*>(P), eigvals);
@@ -561,6 +575,181 @@ hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* 
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
+}
+
+// ===========================================================================
+// Asymmetric scoring index (page "SAKI: Score-Aware Low-Rank Key Indexing
+// with Random-Matrix Noise Correction for KV Retrieval", abstract): the rank-r
+// factors minimising the expected squared score error
+// || Cq^{1/2} (I - A B^T) Ck^{1/2} ||_F^2, Cq and Ck the query and key second
+// moments, are read off the SVD of W = Cq^{1/2} Ck^{1/2} = U S V^T:
+// A = Cq^{-1/2} W V_r S_r^{-1/2} (= Cq^{-1/2} U_r S_r^{1/2}), B = Ck^{-1/2} V_r S_r^{1/2}.
+// Matrix square roots and inverse square roots come from Jacobi
+// eigendecompositions (eigenvalues below 1e-12 of the largest count as zero);
+// V and S^2 from the eigendecomposition of W^T W.  All in fp64.
+// ===========================================================================
+constexpr double kAsymFloor = 1e-12;
+
+// out[h][e] = scale * sum_{g < G} in[h G + g][e]
+__global__ __launch_bounds__(256) void pool_kernel(const double* __restrict__ in, double* __restrict__ out, int G,
+                                                   int DD, double scale) {
+  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= DD) return;
+  double s = 0.0;
+  for (int g = 0; g < G; ++g) s += in[((size_t)h * G + g) * DD + e];
+  out[(size_t)h * DD + e] = s * scale;
+}
+
+// out[h] = V[h] diag(f(lam[h])) V[h]^T, f = sqrt (mode 0) or the inverse
+// square root above the floor, else 0 (mode 1); negative rounding -> 0.
+template <int D>
+__global__ __launch_bounds__(D) void psd_fn_kernel(const double* __restrict__ V, const double* __restrict__ lam,
+                                                   double* __restrict__ out, int mode) {
+  __shared__ double f[D], vi[D], red[D];
+  const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
+  const double* Vh = V + (size_t)h * D * D;
+  const double l = fmax(lam[(size_t)h * D + j], 0.0);
+  red[j] = l;
+  vi[j] = Vh[(size_t)i * D + j];
+  __syncthreads();
+  for (int o = D / 2; o > 0; o >>= 1) {
+    if (j < o) red[j] = fmax(red[j], red[j + o]);
+    __syncthreads();
+  }
+  const double lmax = red[0];
+  f[j] = mode == 0 ? sqrt(l) : (l > kAsymFloor * lmax ? 1.0 / sqrt(l) : 0.0);
+  __syncthreads();
+  double s = 0.0;
+  for (int c = 0; c < D; ++c) s = fma(vi[c] * f[c], Vh[(size_t)j * D + c], s);
+  out[((size_t)h * D + i) * D + j] = s;
+}
+
+// out[h] = X'[h] Y[h], X' = X or X^T
+template <int D>
+__global__ __launch_bounds__(D) void matmul_kernel(const double* __restrict__ X, const double* __restrict__ Y,
+                                                   double* __restrict__ out, int tx) {
+  __shared__ double xr[D];
+  const int h = blockIdx.y, i = blockIdx.x, j = threadIdx.x;
+  const double* Xh = X + (size_t)h * D * D;
+  const double* Yh = Y + (size_t)h * D * D;
+  xr[j] = tx ? Xh[(size_t)j * D + i] : Xh[(size_t)i * D + j];
+  __syncthreads();
+  double s = 0.0;
+  for (int c = 0; c < D; ++c) s = fma(xr[c], Yh[(size_t)c * D + j], s);
+  out[((size_t)h * D + i) * D + j] = s;
+}
+
+// From the eigenpairs (unsorted) of W^T W: the r largest s^2 = lam in
+// decreasing order (equal values by index); column k < r of VA / VB is the
+// k-th such eigenvector times s^{-1/2} / s^{1/2} (both 0 below the floor),
+// columns k >= r are zero.
+template <int D>
+__global__ __launch_bounds__(D) void asym_cols_kernel(const double* __restrict__ Vw, const double* __restrict__ lam,
+                                                      double* __restrict__ VA, double* __restrict__ VB, int r) {
+  __shared__ double ls[D];
+  const int h = blockIdx.x, c = threadIdx.x;
+  const double lc = fmax(lam[(size_t)h * D + c], 0.0);
+  ls[c] = lc;
+  __syncthreads();
+  int rank = 0;
+  double lmax = 0.0;
+  for (int j = 0; j < D; ++j) {
+    rank += (ls[j] > lc) || (ls[j] == lc && j < c);
+    lmax = fmax(lmax, ls[j]);
+  }
+  const double s = sqrt(lc);
+  const bool keep = rank < r && lc > kAsymFloor * lmax;
+  const double fa = keep ? 1.0 / sqrt(s) : 0.0, fb = keep ? sqrt(s) : 0.0;
+  const double* Vh = Vw + (size_t)h * D * D;
+  double* A = VA + (size_t)h * D * D;
+  double* B = VB + (size_t)h * D * D;
+  for (int i = 0; i < D; ++i) {
+    const double v = Vh[(size_t)i * D + c];
+    A[(size_t)i * D + rank] = v * fa;
+    B[(size_t)i * D + rank] = v * fb;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void cast_kernel(const double* __restrict__ in, T* __restrict__ out, int n) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < n) out[e] = from_f64<T>(in[e]);
+}
+
+bool make_asym_plan(AsymPlan& p, int N, int Hq, int B, int Hkv, int S, int d, int r, int dt) {
+  if (N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || r < 1 || r > d) return false;
+  if (!make_calib_plan(p.qp, N, Hq, 1, d, dt) || !make_calib_plan(p.kp, B, Hkv, S, d, dt)) return false;
+  p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv; p.d = d; p.r = r; p.dt = dt; p.N = N; p.BS = (long long)B * S;
+  const size_t dd = (size_t)d * d * sizeof(double);
+  const size_t part = std::max((size_t)Hq * p.qp.nblk, (size_t)Hkv * p.kp.nblk) * dd;
+  size_t off = 0;
+  auto take = [&](size_t n) { const size_t o = off; off = align_up(off + n, 256); return o; };
+  p.off_part = take(part);
+  p.off_Cqh = take((size_t)Hq * dd);
+  p.off_log = take((size_t)Hkv * jacobi_max_rounds(d) * (d / 2) * 2 * sizeof(double));
+  p.off_nr = take((size_t)Hkv * sizeof(int));
+  p.off_lam = take((size_t)Hkv * d * sizeof(double));
+  for (int m = 0; m < kAsymMats; ++m) p.off_mat[m] = take((size_t)Hkv * dd);
+  p.bytes = off;
+  return true;
+}
+
+hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const void* K, void* A, void* Bm, void* ws,
+                                 hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  double* part = reinterpret_cast<double*>(w + p.off_part);
+  double* Cqh = reinterpret_cast<double*>(w + p.off_Cqh);
+  double2* rlog = reinterpret_cast<double2*>(w + p.off_log);
+  int* nr = reinterpret_cast<int*>(w + p.off_nr);
+  double* lam = reinterpret_cast<double*>(w + p.off_lam);
+  double* M[kAsymMats];
+  for (int m = 0; m < kAsymMats; ++m) M[m] = reinterpret_cast<double*>(w + p.off_mat[m]);
+  double *Cq = M[0], *Ck = M[1], *Vq = M[2], *Sq = M[3], *Sqi = M[4], *Sk = M[5], *Ski = M[6], *W = M[7],
+         *WtW = M[8], *VA = M[9], *VB = M[10], *T = M[11];
+  const int D = p.d, DD = D * D, H = p.Hkv;
+  hipError_t e;
+  // second moments: queries pooled over each group's heads, keys
+  if ((e = launch_gram(p.qp, q_samples, part, Cqh, st, nullptr)) != hipSuccess) return e;
+  hipLaunchKernelGGL(pool_kernel, dim3((DD + 255) / 256, H), dim3(256), 0, st, Cqh, Cq, p.G, DD,
+                     1.0 / ((double)p.N * p.G));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_gram(p.kp, K, part, Cqh, st, nullptr)) != hipSuccess) return e;
+  hipLaunchKernelGGL(pool_kernel, dim3((DD + 255) / 256, H), dim3(256), 0, st, Cqh, Ck, 1, DD, 1.0 / (double)p.BS);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 mg(D, H), mb(D);
+  auto psd = [&](const double* Vv, double* out, int mode) {
+    if (D == 128) hipLaunchKernelGGL(psd_fn_kernel<128>, mg, mb, 0, st, Vv, lam, out, mode);
+    else hipLaunchKernelGGL(psd_fn_kernel<64>, mg, mb, 0, st, Vv, lam, out, mode);
+    return hipGetLastError();
+  };
+  auto mm = [&](const double* X, const double* Y, double* out, int tx) {
+    if (D == 128) hipLaunchKernelGGL(matmul_kernel<128>, mg, mb, 0, st, X, Y, out, tx);
+    else hipLaunchKernelGGL(matmul_kernel<64>, mg, mb, 0, st, X, Y, out, tx);
+    return hipGetLastError();
+  };
+  // Cq^{1/2}, Cq^{-1/2}, Ck^{1/2}, Ck^{-1/2}
+  if ((e = launch_sym_eig(D, H, Cq, rlog, nr, lam, Vq, st)) != hipSuccess) return e;
+  if ((e = psd(Vq, Sq, 0)) != hipSuccess || (e = psd(Vq, Sqi, 1)) != hipSuccess) return e;
+  if ((e = launch_sym_eig(D, H, Ck, rlog, nr, lam, Vq, st)) != hipSuccess) return e;
+  if ((e = psd(Vq, Sk, 0)) != hipSuccess || (e = psd(Vq, Ski, 1)) != hipSuccess) return e;
+  // W = Cq^{1/2} Ck^{1/2}; V, S^2 from W^T W
+  if ((e = mm(Sq, Sk, W, 0)) != hipSuccess || (e = mm(W, W, WtW, 1)) != hipSuccess) return e;
+  if ((e = launch_sym_eig(D, H, WtW, rlog, nr, lam, Vq, st)) != hipSuccess) return e;
+  if (D == 128) hipLaunchKernelGGL(asym_cols_kernel<128>, dim3(H), dim3(128), 0, st, Vq, lam, VA, VB, p.r);
+  else hipLaunchKernelGGL(asym_cols_kernel<64>, dim3(H), dim3(64), 0, st, Vq, lam, VA, VB, p.r);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // A = Cq^{-1/2} (W VA), B = Ck^{-1/2} VB
+  if ((e = mm(W, VA, T, 0)) != hipSuccess || (e = mm(Sqi, T, VA, 0)) != hipSuccess) return e;
+  if ((e = mm(Ski, VB, T, 0)) != hipSuccess) return e;
+  const int n = H * DD;
+  if (p.dt == 1) {
+    hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, st, VA, static_cast<bf16_t*>(A), n);
+    hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3((n + 255) / 256), dim3(256), 0, st, T, static_cast<bf16_t*>(Bm), n);
+  } else {
+    hipLaunchKernelGGL(cast_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, st, VA, static_cast<float*>(A), n);
+    hipLaunchKernelGGL(cast_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, st, T, static_cast<float*>(Bm), n);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace loki

@@ -128,4 +128,17 @@ bool make_calib_plan(CalibPlan& p, int B, int Hkv, int S, int d, int dt);
 hipError_t launch_calibrate(const CalibPlan& p, const void* K, void* P, double* eigvals, void* ws,
                             hipStream_t st, hipEvent_t* ev);
 
+// Asymmetric scoring index calibration: Gram plans of the query samples
+// ([N, Hq, 1, d]) and of the keys, and fp64 scratch matrices.
+constexpr int kAsymMats = 12;
+struct AsymPlan {
+  CalibPlan qp, kp;
+  int Hq, Hkv, G, d, r, dt, N;
+  long long BS;  // key rows per head
+  size_t off_part, off_Cqh, off_log, off_nr, off_lam, off_mat[kAsymMats], bytes;
+};
+bool make_asym_plan(AsymPlan& p, int N, int Hq, int B, int Hkv, int S, int d, int r, int dt);
+hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const void* K, void* A, void* Bm, void* ws,
+                                 hipStream_t st);
+
 }  // namespace loki

@@ -240,3 +240,21 @@ def test_project_lead_only_rejects(lib):
     assert f(A, A, NULLP, NULLP, 32, 1, 1, 8, 128, BF16, NULLP) == NULL
     assert f(A, A, NULLP, MIS, 32, 1, 1, 8, 128, BF16, NULLP) == ALIGN
     assert f(A, A, NULLP, A, 0, 1, 1, 8, 128, BF16, NULLP) == RANGE
+
+
+def test_calibrate_asym_rejects(lib):
+    f = lib.loki_calibrate_asym
+    # (q_samples, K, A, Bm, N, Hq, B, Hkv, S, d, r, dt, ws, wsb, stream)
+    big = 1 << 40
+    assert f(NULLP, A, A, A, 100, 4, 1, 2, 50, 128, 8, BF16, A2, big, NULLP) == NULL
+    assert f(A, A, A, NULLP, 100, 4, 1, 2, 50, 128, 8, BF16, A2, big, NULLP) == NULL
+    assert f(A, A, A, A, 100, 5, 1, 2, 50, 128, 8, BF16, A2, big, NULLP) == SHAPE
+    assert f(A, A, A, A, 0, 4, 1, 2, 50, 128, 8, BF16, A2, big, NULLP) == SHAPE
+    assert f(A, A, A, A, 100, 4, 1, 2, 50, 96, 8, BF16, A2, big, NULLP) == UNSUPPORTED
+    assert f(A, A, A, A, 100, 4, 1, 2, 50, 128, 0, BF16, A2, big, NULLP) == RANGE
+    assert f(A, A, A, A, 100, 4, 1, 2, 50, 128, 129, BF16, A2, big, NULLP) == RANGE
+    assert f(A, A, MIS, A, 100, 4, 1, 2, 50, 128, 8, BF16, A2, big, NULLP) == ALIGN
+    assert f(A, A, A, A, 100, 4, 1, 2, 50, 128, 8, 3, A2, big, NULLP) == DTYPE
+    need = lib.loki_calibrate_asym_workspace_bytes(100, 4, 1, 2, 50, 128, 8)
+    assert need > 0
+    assert f(A, A, A, A, 100, 4, 1, 2, 50, 128, 8, BF16, A2, need - 1, NULLP) == WORKSPACE

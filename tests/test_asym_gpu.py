@@ -123,3 +123,57 @@ def test_index_projection_lead_only(gpu_lib, dt):
     acc = 2.0 * (cfg.d + 2) * U * oracle.project(x["K"].abs(), B_t.abs())[..., :R]
     tol = (2.0 ** -8 * (np.abs(exact) + acc) + acc) if dt == "bf16" else acc + 1e-30
     assert np.all(np.abs(idx_only.double().cpu().numpy() - exact) <= tol)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_calibrate_asym_matches_oracle(gpu_lib, dt, d):
+    # the GPU's factors give the oracle's rank-r product M = A_r B_r^T (unique:
+    # the columns themselves carry a sign per pair) and reach the optimal
+    # distortion; the columns past r are zero
+    cfg = CONFIGS["C1"].replace(B=2, Hq=4, Hkv=2, d=d, S=1000, r=16, dtype=dt, tau=6.0)
+    x = make_inputs(cfg, need_K=True)
+    qs = make_query_samples(cfg, 300)
+    A_g, B_g = gpu_lib.loki_calibrate_asym(dev(qs), dev(x["K"]), cfg.r)
+    torch.cuda.synchronize()
+    A_o, B_o = asym.calibrate(qs, x["K"], cfg.r)
+    Ag, Bg = A_g.double().cpu().numpy(), B_g.double().cpu().numpy()
+    assert np.all(Ag[:, :, cfg.r:] == 0) and np.all(Bg[:, :, cfg.r:] == 0)
+    for kv in range(cfg.Hkv):
+        Qk = qs[:, 2 * kv:2 * kv + 2].double().numpy().reshape(-1, d)
+        Kk = np.concatenate([x["K"][b, kv].double().numpy() for b in range(cfg.B)])
+        Cq, Ck = Qk.T @ Qk / len(Qk), Kk.T @ Kk / len(Kk)
+        Mg = Ag[kv, :, :cfg.r] @ Bg[kv, :, :cfg.r].T
+        Mo = A_o[kv] @ B_o[kv].T
+        rel = 1e-4 if dt == "f32" else 2e-2
+        assert np.max(np.abs(Mg - Mo)) <= rel * np.max(np.abs(Mo)), (kv, np.max(np.abs(Mg - Mo)))
+        dg, do = asym.distortion(Cq, Ck, Mg), asym.distortion(Cq, Ck, Mo)
+        assert dg <= do * (1.0 + (1e-6 if dt == "f32" else 5e-2)) + 1e-12 * np.trace(Cq) * np.trace(Ck)
+
+
+def test_calibrated_index_end_to_end(gpu_lib):
+    # calibrate, write the index and decode, all on the GPU, against the
+    # oracle's own pipeline from the same query samples and keys
+    cfg = CONFIGS["C3"].scaled(S=2048, B=2)
+    x = make_inputs(cfg, need_K=True)
+    qs = make_query_samples(cfg, 256)
+    K = dev(x["K"])
+    A_g, B_g = gpu_lib.loki_calibrate_asym(dev(qs), K, cfg.r)
+    K_idx = gpu_lib.loki_project_keys(K, B_g, R=cfg.r, lead_only=True)
+    out_g, idx_g = gpu_lib.loki_decode_asym(dev(x["q"]), A_g, K_idx, K, dev(x["V"]), cfg.r, cfg.k)
+    torch.cuda.synchronize()
+    # the oracle's own pipeline from the same q samples and keys
+    A_o, B_o = asym.calibrate(qs, x["K"], cfg.r)
+    idx_o = asym.select(x["q"], A_o, np.einsum("bhsd,hdr->bhsr", x["K"].double().numpy(), B_o), cfg.r, cfg.k)
+    # both pipelines keep nearly the same tokens (bf16 storage of A, B and the
+    # index moves scores near the threshold; the recall of the oracle's set)
+    ig = idx_g.cpu().numpy()
+    recall = np.mean([len(set(ig[b, h]) & set(idx_o[b, h])) / cfg.k
+                      for b in range(cfg.B) for h in range(cfg.Hq)])
+    assert recall > 0.95, recall
+    # and the output is the exact attention over the GPU's own kept set (the
+    # attention stage alone with an identity basis reads the query as it is)
+    eye = torch.eye(cfg.d, dtype=torch.bfloat16, device="cuda").expand(cfg.Hkv, cfg.d, cfg.d).contiguous()
+    again = gpu_lib.loki_attend(dev(x["q"]), eye, K, dev(x["V"]), idx_g)
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), out_g.view(torch.int16))
