@@ -544,6 +544,122 @@ def run_aqua(args) -> dict:
     return res
 
 
+def run_asym(args) -> dict:
+    """Decode steps with an asymmetric scoring index (loki_decode_asym) on the
+    decode workload: the factors calibrated on the GPU from seeded query
+    samples and the keys, the key index written by the projection kernel
+    (both timed once, outside the steps), then the timed decode steps."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    from loki_inputs import CONFIGS, make_inputs, make_query_samples
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    rks.load_library()
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(cfg, need_K=True)
+    qs = make_query_samples(cfg, 512).to(dev)
+    q = x["q"].to(dev)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    bufs = []
+    for i in range(args.buffers):
+        K, V = x["K"].to(dev), x["V"].to(dev)
+        if i == 0:
+            e0.record()
+            A, Bm = rks.loki_calibrate_asym(qs, K, cfg.r)
+            e1.record()
+        Ki = rks.loki_project_keys(K, Bm, R=cfg.r, lead_only=True)
+        if i == 0:
+            e2.record()
+        bufs.append((K, V, Ki))
+    torch.cuda.synchronize()
+    calib_ms, index_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+    ws = torch.empty(rks.loki_decode_workspace_bytes(cfg.B, cfg.Hq, cfg.Hkv, cfg.S, cfg.d, cfg.r, cfg.k, q.dtype),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    idx = torch.empty((cfg.B, cfg.Hq, cfg.k), dtype=torch.int32, device=dev)
+
+    def step(i, events=None):
+        K, V, Ki = bufs[i % len(bufs)]
+        rks.loki_decode_asym(q, A, Ki, K, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for row in evs:
+        for ev in row:
+            ev.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    stage_us = {s_: 0.0 for s_ in STAGES}
+    for row in evs:
+        for j, s_ in enumerate(STAGES):
+            stage_us[s_] += 1e3 * row[j].elapsed_time(row[j + 1]) / args.steps
+    e = cfg.elem_bytes
+    U = union_rows(idx, cfg.G)
+    by_scores = cfg.B * cfg.Hkv * cfg.S * cfg.r * e
+    by_gather = U * cfg.d * 2 * e
+    by_step = by_scores + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
+        + cfg.B * cfg.Hq * cfg.k * 4
+    per = {"scores": by_scores, "attend": by_gather}
+    dom = max(("scores", "attend"), key=lambda s_: stage_us[s_])
+    kern = {"scores": score_stage_kernel(cfg), "attend": "attend_mfma_kernel"}[dom]
+    ach = per[dom] / (stage_us[dom] * 1e-6) / 1e9
+    res = {
+        "metric": "decode steps/s with an asymmetric scoring index (all heads)",
+        "value": round(1e3 / ms, 1), "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} decode, asymmetric index", "batch": cfg.B, "q_heads": cfg.Hq,
+                   "kv_heads": cfg.Hkv, "head_dim": cfg.d, "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k,
+                   "calibration_queries_per_head": 512},
+        "stage_us": {s_: round(v, 2) for s_, v in stage_us.items()},
+        "calibration_ms": round(calib_ms, 3), "index_projection_ms": round(index_ms, 3),
+        "hbm_gbs_step": round(by_step / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kern,
+                     "alg_bytes_per_launch": per[dom], "avg_launch_us": round(stage_us[dom], 2)},
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+        return res
+    # the oracle's own pipeline (its factors from the same query samples and
+    # keys, then per batch element the index, selection and attention),
+    # single-threaded on whole batch elements for a bounded time; the factors
+    # are set up outside the timed part, as on the GPU
+    import oracle
+    from oracle import asym
+    from threadpoolctl import threadpool_limits
+    A_o, B_o = asym.calibrate(qs.cpu(), x["K"], cfg.r)
+    eye = np.broadcast_to(np.eye(cfg.d), (cfg.Hkv, cfg.d, cfg.d))
+    done, used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while used < args.cpu_seconds or done == 0:
+            b = done % cfg.B
+            t = time.perf_counter()
+            Ki = np.einsum("hsd,hdr->hsr", x["K"][b].double().numpy(), B_o)[None]
+            ii = asym.select(x["q"][b:b + 1], A_o, Ki, cfg.r, cfg.k)
+            oracle.attend(x["q"][b:b + 1], eye, x["K"][b:b + 1], x["V"][b:b + 1], ii)
+            used += time.perf_counter() - t
+            done += 1
+    res["cpu_baseline"] = {"value": round(1.0 / (used / done * cfg.B), 4), "unit": "steps/s", "cores": 1,
+                           "kind": "oracle", "sample": f"{done} batch-element decodes (index, selection, attention), "
+                                                       f"{used:.1f} s single-threaded"}
+    return res
+
+
 def run_calibrate(args) -> dict:
     """Offline calibration of the basis (loki_calibrate_pca) on the workload's
     whole key cache: Gram matrix of each key head's rows (MFMA), fixed-order
@@ -742,7 +858,7 @@ def main() -> int:
                     help="decode a ragged batch: per-sequence cache lengths from S down to about S/2")
     ap.add_argument("--graph", action="store_true",
                     help="decode: time steps replayed from HIP graphs (one launch per step)")
-    ap.add_argument("--op", default="decode", choices=["decode", "project", "append", "calibrate", "aqua"],
+    ap.add_argument("--op", default="decode", choices=["decode", "project", "append", "calibrate", "aqua", "asym"],
                     help="project: time the key projection instead (use --workload C5); "
                          "append: time one decode step's cache append")
     ap.add_argument("--summarize-trace", metavar="DB")
@@ -766,7 +882,7 @@ def main() -> int:
         for _ in range(3):
             torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
-    res = {"project": run_project, "append": run_append, "calibrate": run_calibrate, "aqua": run_aqua}.get(args.op, run)(args)
+    res = {"project": run_project, "append": run_append, "calibrate": run_calibrate, "aqua": run_aqua, "asym": run_asym}.get(args.op, run)(args)
     print(json.dumps(res))
     return 0
 
