@@ -643,3 +643,17 @@ def test_project_lead_copy(gpu_lib, dt, d, R):
     Kr2 = gpu_lib.loki_project_keys(dev(K), dev(P))
     assert torch.equal(Kr.view(torch.int16) if dt == "bf16" else Kr, Kr2.view(torch.int16) if dt == "bf16" else Kr2)
     assert torch.equal(Kl, Kr[..., :R].contiguous())
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("k", [16, 64])
+def test_decode_maximum_cache_length(gpu_lib, k):
+    # the largest cache the library accepts (2^24 tokens; one more is
+    # rejected): k = 16 takes the chunked two-stage selection (1024 chunks of
+    # 16384 tokens), k = 64 overflows its candidate list and takes the
+    # global-memory selection
+    cfg = CONFIGS["C1"].replace(B=1, Hq=2, Hkv=1, d=64, S=1 << 24, r=16, k=k, dtype="bf16", tau=8.0)
+    print(f"\n[max S] S={cfg.S} k={k}", flush=True)
+    x = make_inputs(cfg)
+    _, _, differ = run_decode(gpu_lib, x, cfg.r, cfg.k)
+    print(f"[max S] rows with band-equivalent sets: {len(differ)}", flush=True)
