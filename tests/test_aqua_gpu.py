@@ -95,6 +95,7 @@ CASES = {
     "C5_r64": (CONFIGS["C5"].scaled(S=4096, B=1), {}),
     "gqa_f32_d128": (CONFIGS["C3"].replace(dtype="f32").scaled(S=3000, B=2), {}),
     "C4_long": (CONFIGS["C4"].scaled(S=40000), {}),
+    "C3_b16": (CONFIGS["C3"].scaled(S=2048, B=16), {}),     # 512 query heads
 }
 
 
@@ -150,3 +151,20 @@ def test_aqua_exact_integer_ties(gpu_lib, dt):
     assert np.array_equal(idx_g.cpu().numpy(), aqua.select(x["q"], x["P"], x["K_rot"], r, k))
     out_o, _ = aqua.decode(x["q"], x["P"], x["K_rot"], x["V"], r, k)
     assert np.max(np.abs(out_g.double().cpu().numpy() - out_o)) <= OUT_TOL[x["q"].dtype]
+
+
+def test_aqua_large_batch_ragged_and_full_rank(gpu_lib):
+    # 512 query heads: ragged lengths, then r = d bit for bit equal to the
+    # leading-dims decode at r = d (which takes the pair-fused kernel here;
+    # its scores equal the score kernel's bit for bit)
+    cfg = CONFIGS["C3"].scaled(S=2048, B=16)
+    x = make_inputs(cfg)
+    lens = [2048 - 97 * b for b in range(cfg.B)]
+    lens[3], lens[7] = 1, cfg.k - 1
+    run_aqua(gpu_lib, x, cfg.r, cfg.k, lens=lens)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    out_a, idx_a, _, _ = gpu_lib.loki_decode_aqua(q, P, Kr, V, cfg.d, cfg.k)
+    out_l, idx_l = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.d, k=cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_l)
+    assert torch.equal(out_a.view(torch.int16), out_l.view(torch.int16))
