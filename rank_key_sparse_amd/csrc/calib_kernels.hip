@@ -299,7 +299,8 @@ template <> __device__ __forceinline__ bf16_t from_f64<bf16_t>(double x) {
 //   tau = (C_qq - C_pp) / (2 C_pq), t = sign(tau) / (|tau| + sqrt(1 + tau^2)),
 //   c = 1 / sqrt(1 + t^2), s = t c, J = [[c, s], [-s, c]] on (p, q)
 // (the symmetric Schur rotation that zeroes C_pq), and C <- J^T C J for all
-// pairs at once: one thread per 2 x 2 block between pairs j <= j'.  The
+// pairs at once: one thread per 2 x 2 block between pairs j <= j' (the
+// upper triangle of blocks packed densely over the threads).  The
 // rotations (c, s) of every round go to a log in the workspace.  Sweeps
 // repeat until one rotates nothing (at most kJacobiMaxSweeps).
 //
@@ -361,9 +362,13 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
         lg[(size_t)round * NP + tid] = make_double2(c, s);
       }
       __syncthreads();
-      for (int id = tid; id < NP * NP; id += kJacobiThreads) {
-        const int j = id / NP, j2 = id - j * NP;
-        if (j > j2) continue;
+      // the NP (NP + 1) / 2 blocks j <= j2, packed densely over the threads:
+      // fold i holds row i (j2 = i .. NP-1) and row NP-1-i (j2 = NP-1-i .. NP-1)
+      for (int id = tid; id < NP * (NP + 1) / 2; id += kJacobiThreads) {
+        const int fi = id / (NP + 1), fc = id - fi * (NP + 1);
+        const bool lo = fc < NP - fi;
+        const int j = lo ? fi : NP - 1 - fi;
+        const int j2 = lo ? fi + fc : fc - 1;  // row NP-1-i: j2 = (NP-1-i) + (fc - (NP-i))
         int p, q, p2, q2;
         jacobi_pair(r, j, D, p, q);
         const double c = s_c[j], s = s_s[j];
