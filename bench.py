@@ -29,7 +29,6 @@ turn rocprofv3 result databases into the summaries kept under profiles/.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -45,11 +44,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ["qrot", "scores", "select", "attend", "merge"]
 
 
+# the sources of the decode kernels whose counters profiles/traffic_*.json holds
+DECODE_SOURCES = ("common.h", "select_core.h", "mfma_kernels.hip", "decode_kernels.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "rank_key_sparse_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "rank_key_sparse_amd", "csrc", name), "rb") as fh:
+            h.update(name.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
