@@ -40,6 +40,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# plain streaming read measured on this part (a read-only micro-benchmark):
+# the practical ceiling next to the nominal peak
+READ_CEILING_GBS = 6390.0
 PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ["qrot", "scores", "select", "attend", "merge"]
 
@@ -288,6 +291,21 @@ def run(args) -> dict:
         for j, s in enumerate(STAGES):
             stage_us[s] += 1e3 * row[j].elapsed_time(row[j + 1])
     stage_us = {s: v / args.steps for s, v in stage_us.items()}
+    # whole-step durations from the same events (first to last): percentiles
+    step_us = np.sort([1e3 * row[0].elapsed_time(row[5]) for row in evs])
+    pct = {"p10": float(np.percentile(step_us, 10)), "p50": float(np.percentile(step_us, 50)),
+           "p90": float(np.percentile(step_us, 90))}
+
+    # quality context (not timed): how many of the exact top-k tokens the
+    # kept set holds, the exact top-k from the library's full-rank decode
+    Kr0, V0, _ = bufs[0]
+    step(0)
+    idx_kept = idx.clone()
+    _, idx_exact = rks.loki_decode(q, P, Kr0, V0, cfg.d, cfg.k, lens=lens)
+    torch.cuda.synchronize()
+    a_k, a_x = idx_kept.cpu().numpy(), idx_exact.cpu().numpy()
+    recall = float(np.mean([np.intersect1d(a_k[b, h][a_k[b, h] >= 0], a_x[b, h][a_x[b, h] >= 0]).size
+                            / max(1, int((a_x[b, h] >= 0).sum())) for b in range(cfg.B) for h in range(cfg.Hq)]))
 
     # algorithmic bytes (what the method must move; intermediates excluded)
     e = cfg.elem_bytes
@@ -331,6 +349,9 @@ def run(args) -> dict:
                    f"ragged {lens_h[0]}..{lens_h[-1]} (mean {sum(lens_h) / len(lens_h):.0f})"},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "frac_of_read_ceiling_step": round(step_gbs / READ_CEILING_GBS, 4),
+        "step_us_events": {k_: round(v_, 2) for k_, v_ in pct.items()},
+        "recall_at_k_vs_exact_topk": round(recall, 4),
         "alg_bytes_per_step": by_step,
         "union_rows": U,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
