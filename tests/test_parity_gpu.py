@@ -657,3 +657,61 @@ def test_decode_maximum_cache_length(gpu_lib, k):
     x = make_inputs(cfg)
     _, _, differ = run_decode(gpu_lib, x, cfg.r, cfg.k)
     print(f"[max S] rows with band-equivalent sets: {len(differ)}", flush=True)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[c[0] for c in VARLEN])
+def test_decode_ignores_stale_workspace(gpu_lib, case):
+    # every kernel writes what it later reads: a workspace full of 0xFF
+    # bytes (and one full of zeros) gives bit for bit the same step, with
+    # and without per-sequence lengths, on every dispatch path
+    label, B, Hq, Hkv, S, d, dt, r, k, R = case
+    cfg = CONFIGS["C3"].replace(name=label, cfg_no=52, B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, dtype=dt, r=r, k=k)
+    x = make_inputs(cfg)
+    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
+    Kl = Kr[..., :R].contiguous() if R else None
+    nb = gpu_lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, q.dtype)
+    lens = dev(torch.tensor([max(1, S - 37 * b) for b in range(B)], dtype=torch.int32))
+    for ln in (None, lens):
+        results = []
+        for fill in (0x00, 0xFF):
+            ws = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+            out, idx = gpu_lib.loki_decode(q, P, Kr, V, r, k, workspace=ws, K_lead=Kl, lens=ln)
+            torch.cuda.synchronize()
+            results.append((out.clone(), idx.clone()))
+        assert torch.equal(results[0][1], results[1][1])
+        assert torch.equal(_bits(results[0][0]), _bits(results[1][0]))
+
+
+def test_concurrent_streams_match_sequential(gpu_lib):
+    # the library keeps no state between calls: four decodes of different
+    # inputs issued on four streams at once, each with its own workspace,
+    # equal the same decodes run one after the other
+    cases = [cfg_case("C3", S=2048, B=16), cfg_case("C2", S=2048, B=8), cfg_case("C3", S=4096, B=2),
+             cfg_case("C5", S=4096, B=1)]
+    inputs = []
+    for cfg in cases:
+        x = make_inputs(cfg)
+        inputs.append((cfg, *(dev(x[n]) for n in ("q", "P", "K_rot", "V"))))
+    seq = []
+    for cfg, q, P, Kr, V in inputs:
+        out, idx = gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k)
+        seq.append((out.clone(), idx.clone()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in inputs]
+    wss = [torch.empty(gpu_lib.loki_decode_workspace_bytes(c.B, c.Hq, c.Hkv, c.S, c.d, c.r, c.k, q.dtype),
+                       dtype=torch.uint8, device="cuda") for c, q, *_ in inputs]
+    outs = [torch.empty_like(q) for _, q, *_ in inputs]
+    idxs = [torch.empty((c.B, c.Hq, c.k), dtype=torch.int32, device="cuda") for c, *_ in inputs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, (cfg, q, P, Kr, V) in enumerate(inputs):
+            with torch.cuda.stream(streams[i]):
+                gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=outs[i], idx=idxs[i], workspace=wss[i])
+        torch.cuda.synchronize()
+        for i in range(len(inputs)):
+            assert torch.equal(idxs[i], seq[i][1]), (rep, i)
+            assert torch.equal(_bits(outs[i]), _bits(seq[i][0])), (rep, i)
