@@ -323,13 +323,28 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   constexpr int DS = D + 1;
   constexpr double kTol = 1e-14;
   constexpr double kTiny = 1e-300;
+  constexpr int NB = NP * (NP + 1) / 2;                          // 2 x 2 blocks j <= j2
+  constexpr int NIDS = (NB + kJacobiThreads - 1) / kJacobiThreads;  // per thread
   extern __shared__ __align__(16) double sC[];
   __shared__ double s_c[NP], s_s[NP], s_t[NP];
+  __shared__ int s_p[NP], s_q[NP];  // this round's pairs
   __shared__ int s_rot;
 
   const int kv = blockIdx.x, tid = threadIdx.x;
   const double* Ch = Cg + (size_t)kv * D * D;
   double2* lg = rlog + (size_t)kv * jacobi_max_rounds(D) * NP;
+  // this thread's blocks (the same every round): the upper triangle of
+  // blocks packed densely over the threads -- fold i holds row i
+  // (j2 = i .. NP-1) and row NP-1-i (j2 = NP-1-i .. NP-1)
+  int bj[NIDS], bj2[NIDS];
+#pragma unroll
+  for (int u = 0; u < NIDS; ++u) {
+    const int id = tid + u * kJacobiThreads;
+    const int fi = id / (NP + 1), fc = id - fi * (NP + 1);
+    const bool lo = fc < NP - fi;
+    bj[u] = id < NB ? (lo ? fi : NP - 1 - fi) : -1;
+    bj2[u] = lo ? fi + fc : fc - 1;
+  }
   auto U = [&](int x, int y) -> double& { return sC[min(x, y) * DS + max(x, y)]; };
 
   for (int e = tid; e < D * D; e += kJacobiThreads) {
@@ -359,18 +374,16 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
         s_c[tid] = c;
         s_s[tid] = s;
         s_t[tid] = t;
+        s_p[tid] = p;
+        s_q[tid] = q;
         lg[(size_t)round * NP + tid] = make_double2(c, s);
       }
       __syncthreads();
-      // the NP (NP + 1) / 2 blocks j <= j2, packed densely over the threads:
-      // fold i holds row i (j2 = i .. NP-1) and row NP-1-i (j2 = NP-1-i .. NP-1)
-      for (int id = tid; id < NP * (NP + 1) / 2; id += kJacobiThreads) {
-        const int fi = id / (NP + 1), fc = id - fi * (NP + 1);
-        const bool lo = fc < NP - fi;
-        const int j = lo ? fi : NP - 1 - fi;
-        const int j2 = lo ? fi + fc : fc - 1;  // row NP-1-i: j2 = (NP-1-i) + (fc - (NP-i))
-        int p, q, p2, q2;
-        jacobi_pair(r, j, D, p, q);
+#pragma unroll
+      for (int u = 0; u < NIDS; ++u) {
+        const int j = bj[u], j2 = bj2[u];
+        if (j < 0) break;
+        const int p = s_p[j], q = s_q[j];
         const double c = s_c[j], s = s_s[j];
         if (j == j2) {
           if (s != 0.0) {
@@ -381,7 +394,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
           }
           continue;
         }
-        jacobi_pair(r, j2, D, p2, q2);
+        const int p2 = s_p[j2], q2 = s_q[j2];
         const double c2 = s_c[j2], s2 = s_s[j2];
         const double m00 = U(p, p2), m01 = U(p, q2), m10 = U(q, p2), m11 = U(q, q2);
         // rows: J^T M; columns: (J^T M) J'
