@@ -586,7 +586,13 @@ def run_asym(args) -> dict:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = make_inputs(cfg, need_K=True)
-    qs = make_query_samples(cfg, 512).to(dev)
+    if args.queries == "mismatched":
+        # queries (and the calibration samples) drawn in another basis than
+        # the keys: the query and key second moments differ
+        both = make_query_samples(cfg, 512 + cfg.B, seed=1)
+        qs, x["q"] = both[:512].to(dev), both[512:].contiguous()
+    else:
+        qs = make_query_samples(cfg, 512).to(dev)
     q = x["q"].to(dev)
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     bufs = []
@@ -631,6 +637,24 @@ def run_asym(args) -> dict:
     for row in evs:
         for j, s_ in enumerate(STAGES):
             stage_us[s_] += 1e3 * row[j].elapsed_time(row[j + 1]) / args.steps
+    # quality context (untimed): recall of the exact top-k (the library's
+    # full-rank decode with an identity basis) by this index and by Loki's
+    # leading dims of the keys' own principal basis, both at rank r
+    K0, V0, _ = bufs[0]
+    step(0)
+    idx_asym = idx.clone()
+    eye = torch.eye(cfg.d, dtype=q.dtype, device=dev).expand(cfg.Hkv, cfg.d, cfg.d).contiguous()
+    _, idx_exact = rks.loki_decode(q, eye, K0, V0, cfg.d, cfg.k)
+    P_pca, _ = rks.loki_calibrate_pca(K0)
+    K_rot_pca = rks.loki_project_keys(K0, P_pca)
+    _, idx_pca = rks.loki_decode(q, P_pca, K_rot_pca, V0, cfg.r, cfg.k)
+    torch.cuda.synchronize()
+    ex = idx_exact.cpu().numpy()
+
+    def recall(ii):
+        a = ii.cpu().numpy()
+        return float(np.mean([np.intersect1d(a[b, h], ex[b, h]).size / cfg.k
+                              for b in range(cfg.B) for h in range(cfg.Hq)]))
     e = cfg.elem_bytes
     U = union_rows(idx, cfg.G)
     by_scores = cfg.B * cfg.Hkv * cfg.S * cfg.r * e
@@ -648,7 +672,9 @@ def run_asym(args) -> dict:
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": f"{cfg.name} decode, asymmetric index", "batch": cfg.B, "q_heads": cfg.Hq,
                    "kv_heads": cfg.Hkv, "head_dim": cfg.d, "cached_tokens": cfg.S, "r": cfg.r, "k": cfg.k,
-                   "calibration_queries_per_head": 512},
+                   "calibration_queries_per_head": 512, "queries": args.queries},
+        "recall_at_k_vs_exact_topk": {"asymmetric_index": round(recall(idx_asym), 4),
+                                      "key_pca_leading_dims": round(recall(idx_pca), 4)},
         "stage_us": {s_: round(v, 2) for s_, v in stage_us.items()},
         "calibration_ms": round(calib_ms, 3), "index_projection_ms": round(index_ms, 3),
         "hbm_gbs_step": round(by_step / (ms * 1e-3) / 1e9, 1),
@@ -878,6 +904,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--queries", default="matched", choices=["matched", "mismatched"],
+                    help="--op asym: queries drawn in the keys' basis, or in another one")
     ap.add_argument("--ragged", action="store_true",
                     help="decode a ragged batch: per-sequence cache lengths from S down to about S/2")
     ap.add_argument("--graph", action="store_true",

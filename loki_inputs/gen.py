@@ -109,8 +109,9 @@ def make_inputs(cfg: Config, need_K: bool = False, seed: int = 0) -> dict:
 
 def make_query_samples(cfg: Config, n: int, seed: int = 0) -> torch.Tensor:
     """``n`` further queries per query head drawn like the workload's queries
-    (spectrum in the basis of the key head they read), as calibration data:
-    ``[n, Hq, d]`` in ``cfg.dtype``."""
+    (the spectrum in ``make_basis(d, cfg_no, kv, seed)``: the basis of the key
+    head they read for the workload's own seed, another basis for another
+    seed), as calibration data: ``[n, Hq, d]`` in ``cfg.dtype``."""
     s = spectrum(cfg)
     out = np.empty((n, cfg.Hq, cfg.d))
     for kv in range(cfg.Hkv):
