@@ -500,6 +500,20 @@ def run_aqua(args) -> dict:
     for row in evs:
         for j, s_ in enumerate(STAGES):
             stage_us[s_] += 1e3 * row[j].elapsed_time(row[j + 1]) / args.steps
+    # quality context (untimed): recall of the exact top-k (the library's
+    # full-rank decode) by these dims and by the leading r dims of the basis
+    Kr0, V0 = bufs[0]
+    step(0)
+    idx_aq = idx.clone()
+    _, idx_exact = rks.loki_decode(q, P, Kr0, V0, cfg.d, cfg.k)
+    _, idx_lead = rks.loki_decode(q, P, Kr0, V0, cfg.r, cfg.k)
+    torch.cuda.synchronize()
+    ex = idx_exact.cpu().numpy()
+
+    def recall(ii):
+        a = ii.cpu().numpy()
+        return float(np.mean([np.intersect1d(a[b, h], ex[b, h]).size / cfg.k
+                              for b in range(cfg.B) for h in range(cfg.Hq)]))
     e = cfg.elem_bytes
     # the dims the method reads: per (b, kv) group the union of its heads' dims
     dg = dims.view(cfg.B, cfg.Hkv, cfg.G * cfg.r).cpu().numpy()
@@ -526,6 +540,8 @@ def run_aqua(args) -> dict:
         "union_dims_per_group": round(union_dims / (cfg.B * cfg.Hkv), 2),
         "score_rows_streamed_bytes": by_rows,
         "info_loss_mean": round(float(info.mean()), 5),
+        "recall_at_k_vs_exact_topk": {"query_magnitude_dims": round(recall(idx_aq), 4),
+                                      "leading_dims": round(recall(idx_lead), 4)},
         "hbm_gbs_step": round(by_step / (ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": kern,
