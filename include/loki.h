@@ -12,6 +12,19 @@
  * attention itself is eqs. 1-5 of the AQUA page's preliminaries: S = q K^T,
  * A = softmax(S / sqrt(d_head)), c = A V.
  *
+ * Entry points, in the order of a deployment:
+ *   loki_calibrate_pca               the basis P from sampled keys (offline)
+ *   loki_project_keys[_lead]         the rotated cache K P (and its lead dims)
+ *   loki_append_kv                   one new token per sequence, in place
+ *   loki_decode / _lead / _varlen    one decode step (full or ragged batch)
+ *   loki_decode_aqua                 the same with per-query magnitude dims
+ *   loki_calibrate_asym, loki_decode_asym
+ *                                    an asymmetric (query side A, key side B)
+ *                                    scoring index, its calibration and decode
+ *   loki_scores, loki_select_topk, loki_attend
+ *                                    the decode stages alone
+ *   *_profiled                       the same work with stage events
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers (HIP global memory) owned by the
