@@ -304,15 +304,14 @@ template <> __device__ __forceinline__ bf16_t from_f64<bf16_t>(double x) {
 // rotations (c, s) of every round go to a log in the workspace.  Sweeps
 // repeat until one rotates nothing (at most kJacobiMaxSweeps).
 //
-// jacobi_v_kernel (one block per 16 rows of V and head): V = I J_1 J_2 ...
-// from the log, the rows in LDS, one rotation of one row per thread and round.
+// jacobi_v_kernel (one wave per row of V): V = I J_1 J_2 ... from the log,
+// partner columns exchanged by lane permutes.
 //
 // eig_out_kernel (one block per head): eigenvalues ranked in decreasing order
 // (equal values by index), each eigenvector's first entry of largest
 // magnitude made positive, P and the eigenvalues written.
 // ---------------------------------------------------------------------------
-constexpr int kJacobiVRows = 16;   // rows of V per block of the rotation-apply kernel
-constexpr int kJacobiLogChunk = 16;  // logged rounds staged in LDS at a time
+constexpr int kJacobiVChunk = 16;  // logged rounds staged in LDS at a time by the rotation-apply kernel
 
 template <int D>
 __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* __restrict__ Cg,
@@ -416,58 +415,93 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   if (tid < D) lam_raw[(size_t)kv * D + tid] = sC[tid * DS + tid];
 }
 
+// V = I J_1 J_2 ... from the log.  The rows of V evolve independently (V <- V J
+// acts on columns), so one wave owns a row: lane l holds its columns l and
+// l + 64 (d = 128) or l (d = 64).  In round r a column's partner and pair
+// index follow from the round-robin pairing (col = d-1 pairs with r; col = r
+// with d-1; otherwise the partner is 2r - col mod (d-1) and the pair index
+// whichever of (col - r), (r - col) mod (d-1) is below d/2); the partner's
+// value comes from its lane by a lane permute, the pair's (c, s) from LDS,
+// where the block stages the log a chunk at a time (the next chunk travels
+// in registers meanwhile), so the only barriers are per chunk.
 template <int D>
-__global__ __launch_bounds__(kJacobiThreads) void jacobi_v_kernel(const double2* __restrict__ rlog,
-                                                                   const int* __restrict__ nrounds,
-                                                                   double* __restrict__ V) {
+__global__ __launch_bounds__(256) void jacobi_v_kernel(const double2* __restrict__ rlog,
+                                                       const int* __restrict__ nrounds,
+                                                       double* __restrict__ V) {
   constexpr int NP = D / 2;
-  constexpr int DS = D + 1;
-  constexpr int RB = kJacobiVRows;
-  constexpr int CH = kJacobiLogChunk;
-  constexpr int NT = NP * RB;  // threads: one (pair, row) each
-  static_assert(CH * NP == NT, "one logged rotation per thread per chunk");
-  __shared__ __align__(16) double sV[RB * DS];
+  constexpr int EPL = D / 64;
+  constexpr int WPB = 4;                      // rows (waves) per block
+  constexpr int CH = kJacobiVChunk;           // logged rounds per chunk
+  constexpr int PER = CH * NP / 256;          // log entries per thread per chunk
+  static_assert(CH * NP % 256 == 0, "chunk split over the block");
   __shared__ __align__(16) double2 sL[2][CH * NP];
 
-  const int kv = blockIdx.y, rb = blockIdx.x, tid = threadIdx.x;
-  const int j = tid / RB, row = tid - j * RB;
+  const int kv = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * WPB + wave;
   const int nr = nrounds[kv];
   const double2* lg = rlog + (size_t)kv * jacobi_max_rounds(D) * NP;
-  auto fetch = [&](int c0) {
-    const int rd = c0 + tid / NP;
-    const double2 v = lg[(size_t)min(rd, max(nr - 1, 0)) * NP + tid % NP];
-    return rd < nr ? v : make_double2(1.0, 0.0);
+  auto fetch = [&](int c0, double2 (&buf)[PER]) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      const int rd = c0 + e / NP;
+      const double2 v = lg[(size_t)min(rd, max(nr - 1, 0)) * NP + e % NP];
+      buf[u] = rd < nr ? v : make_double2(1.0, 0.0);
+    }
   };
-
-  for (int e = tid; e < RB * D; e += NT) {
-    const int rr = e / D, c = e - rr * D;
-    sV[rr * DS + c] = (rb * RB + rr == c) ? 1.0 : 0.0;
+  double v[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) v[e] = (row == lane + 64 * e) ? 1.0 : 0.0;
+  double2 buf[PER];
+  if (nr > 0) {
+    fetch(0, buf);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sL[0][threadIdx.x + 256 * u] = buf[u];
   }
-  if (nr > 0) sL[0][tid] = fetch(0);
   __syncthreads();
   const int nch = (nr + CH - 1) / CH;
   for (int ch = 0; ch < nch; ++ch) {
-    const double2 nxt = fetch((ch + 1) * CH);  // the next chunk travels while this one is applied
+    fetch((ch + 1) * CH, buf);  // the next chunk travels while this one is applied
     const double2* L = sL[ch & 1];
-    const int kend = min(CH, nr - ch * CH);
-    for (int k = 0; k < kend; ++k) {
-      int p, q;
-      jacobi_pair((ch * CH + k) % (D - 1), j, D, p, q);
-      const double2 cs = L[k * NP + j];
-      if (cs.y != 0.0) {
-        const double vp = sV[row * DS + p], vq = sV[row * DS + q];
-        sV[row * DS + p] = cs.x * vp - cs.y * vq;
-        sV[row * DS + q] = cs.y * vp + cs.x * vq;
+    // rounds past the last logged one hold (1, 0), an exact identity, so
+    // every chunk runs whole and its index arithmetic is off the chain
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int r = (ch * CH + k) % (D - 1);
+      double nv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int col = lane + 64 * e;
+        int partner, j;
+        if (col == D - 1) {
+          partner = r;
+          j = 0;
+        } else if (col == r) {
+          partner = D - 1;
+          j = 0;
+        } else {
+          partner = (2 * r - col + 2 * (D - 1)) % (D - 1);
+          const int jj = (col - r + (D - 1)) % (D - 1);
+          j = jj < NP ? jj : (r - col + (D - 1)) % (D - 1);
+        }
+        double pv = __shfl(v[0], partner & 63);
+        if constexpr (EPL == 2) {
+          const double pv1 = __shfl(v[1], partner & 63);
+          pv = partner >= 64 ? pv1 : pv;
+        }
+        const double2 cs = L[k * NP + j];
+        // V'[:, p] = c V[:, p] - s V[:, q],  V'[:, q] = s V[:, p] + c V[:, q]
+        nv[e] = col < partner ? cs.x * v[e] - cs.y * pv : cs.y * pv + cs.x * v[e];
       }
-      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = nv[e];
     }
-    sL[(ch + 1) & 1][tid] = nxt;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sL[(ch + 1) & 1][threadIdx.x + 256 * u] = buf[u];
     __syncthreads();
   }
-  for (int e = tid; e < RB * D; e += NT) {
-    const int rr = e / D, c = e - rr * D;
-    V[((size_t)kv * D + rb * RB + rr) * D + c] = sV[rr * DS + c];
-  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) V[((size_t)kv * D + row) * D + lane + 64 * e] = v[e];
 }
 
 template <int D, typename T>
@@ -562,9 +596,9 @@ static hipError_t launch_sym_eig(int D, int H, const double* C, double2* rlog, i
   hipLaunchKernelGGL(kc, dim3(H), dim3(kJacobiThreads), lds, st, C, rlog, nr, lam_raw);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (D == 128)
-    hipLaunchKernelGGL(jacobi_v_kernel<128>, dim3(128 / kJacobiVRows, H), dim3(64 * kJacobiVRows), 0, st, rlog, nr, V);
+    hipLaunchKernelGGL(jacobi_v_kernel<128>, dim3(128 / 4, H), dim3(256), 0, st, rlog, nr, V);
   else
-    hipLaunchKernelGGL(jacobi_v_kernel<64>, dim3(64 / kJacobiVRows, H), dim3(32 * kJacobiVRows), 0, st, rlog, nr, V);
+    hipLaunchKernelGGL(jacobi_v_kernel<64>, dim3(64 / 4, H), dim3(256), 0, st, rlog, nr, V);
   return hipGetLastError();
 }
 
