@@ -382,8 +382,9 @@ __global__ __launch_bounds__(kSelThreads, T <= 16 ? 8 : 4) void select_regs_kern
 // tokens, head) keeps the chunk's top-k; its positions (made absolute) and
 // keys go to the candidate lists, chunk c at offset c k, ascending.  Stage 2:
 // one block per head selects the top-k of its candidate list (position order
-// is token order, so ties still go to the lower token) and maps positions
-// back to tokens; the bitmap is rebuilt from idx afterwards.
+// is token order, so ties still go to the lower token), maps positions back
+// to tokens and sets the kept tokens' bits in the head's bitmap row (cleared
+// while the selection runs).
 __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_t* __restrict__ keys, int Scap,
                                                                    int Sp, int k, int ldc,
                                                                    int32_t* __restrict__ cidx,
@@ -414,8 +415,9 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_
 template <int T>
 __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_t* __restrict__ ckey,
                                                                    const int32_t* __restrict__ cidx,
-                                                                   int S2, int ldc, int k,
+                                                                   int S2, int ldc, int k, int W,
                                                                    int32_t* __restrict__ idx,
+                                                                   uint32_t* __restrict__ bitmap,
                                                                    const int32_t* __restrict__ lens, int Hq,
                                                                    int Scap) {
   __shared__ uint32_t lds[kNB];
@@ -423,16 +425,24 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_
   __shared__ SelScratch<kSelThreads> sh;
   const int row = blockIdx.x;
   const int S = seq_len(lens, row / Hq, Scap);
-  if (k >= S) {  // a short head keeps all its tokens (the bitmap is built from idx)
-    for (int j = threadIdx.x; j < k; j += kSelThreads) idx[(size_t)row * k + j] = j < S ? j : -1;
+  int32_t* orow = idx + (size_t)row * k;
+  uint32_t* brow = bitmap + (size_t)row * W;
+  if (k >= S) {  // a short head keeps all its tokens
+    keep_all<kSelThreads>(S, k, W, orow, brow);
     return;
   }
+  for (int w = threadIdx.x; w < W; w += kSelThreads) brow[w] = 0u;  // ordered before the bits by the barriers below
   // every chunk filled its k slots (free ones with key 0, below every score's
   // key), and the head has more than k real candidates: none is chosen
   uint32_t key[T];
   load_regs<T>(ckey + (size_t)row * ldc, S2, key);
-  select_regs<kSelThreads, T>(key, lds, take, S2, k, 2 * ((S2 + 63) / 64), idx + (size_t)row * k, nullptr, sh,
+  select_regs<kSelThreads, T>(key, lds, take, S2, k, 2 * ((S2 + 63) / 64), orow, nullptr, sh,
                               cidx + (size_t)row * ldc);
+  __syncthreads();  // every thread's idx entries written
+  for (int i = threadIdx.x; i < k; i += kSelThreads) {
+    const int j = orow[i];
+    if (j >= 0 && j < S) atomicOr(&brow[j >> 5], 1u << (j & 31));
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_global_kernel(const uint32_t* __restrict__ keys,
@@ -724,6 +734,86 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   out[(size_t)row * d + c] = from_f32<T>(L > 0.f ? a / L : 0.f);
 }
 
+// Heads with 33 to 128 chunk partials (long heads): four waves per head, wave
+// w merging partials [w n, (w + 1) n), n = ceil(NC / 4), with every load of
+// its share issued up front (the loop above keeps eight in flight, a chain of
+// NC / 8 memory round trips); the four waves' (max, sum, acc) are then merged
+// by log-sum-exp through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_multi_kernel(const float* __restrict__ part,
+                                                            T* __restrict__ out, int NC) {
+  constexpr int MAXW = 32;     // partials per wave
+  constexpr int EPL = D / 64;  // dims per lane
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_a[4][D];
+  const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = (NC + 3) / 4;  // <= MAXW for NC <= 128
+  const int c0 = wave * n, cn = max(0, min(n, NC - c0));
+  const size_t st = (size_t)D + 2;
+  const float* pr = part + ((size_t)row * NC + c0) * st;
+  float acc[MAXW][EPL];
+#pragma unroll
+  for (int ch = 0; ch < MAXW; ++ch) {
+    if (ch < cn) {
+      if constexpr (EPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(pr + ch * st + 2 + 2 * lane);
+        acc[ch][0] = v.x;
+        acc[ch][1] = v.y;
+      } else {
+        acc[ch][0] = pr[ch * st + 2 + lane];
+      }
+    }
+  }
+  float m = -INFINITY, l = 0.f;
+  if (lane < cn) {
+    m = pr[lane * st];
+    l = pr[lane * st + 1];
+  }
+  const float Mw = wave_max(m);
+  const float f = (m == -INFINITY) ? 0.f : exp2f(m - Mw);
+  float L = 0.f, a[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < MAXW; ++ch) {
+    if (ch < cn) {
+      const float fc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), ch));
+      const float lc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), ch));
+      L = fmaf(lc, fc, L);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = fmaf(acc[ch][e], fc, a[e]);
+    }
+  }
+  if (lane == 0) {
+    s_m[wave] = Mw;
+    s_l[wave] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) s_a[wave][lane * EPL + e] = a[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    float Lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float fw = (s_m[w] == -INFINITY) ? 0.f : exp2f(s_m[w] - M);
+      Lt = fmaf(s_l[w], fw, Lt);
+      at = fmaf(s_a[w][c], fw, at);
+    }
+    out[(size_t)row * D + c] = from_f32<T>(Lt > 0.f ? at / Lt : 0.f);
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_combine(const float* part, T* out, int rows, int NC, hipStream_t st) {
+  if (NC > 32 && NC <= 128)
+    hipLaunchKernelGGL((combine_multi_kernel<T, D>), dim3(rows), dim3(256), 0, st, part, out, NC);
+  else
+    hipLaunchKernelGGL((combine_kernel<T>), dim3(rows), dim3(D), 0, st, part, out, NC, D);
+  return hipGetLastError();
+}
+
 // ============================================================================
 // host side
 // ============================================================================
@@ -881,14 +971,21 @@ hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* 
                        cidx, ckey, lens, Hq);
     if (S2 <= kSelThreads * 16)
       hipLaunchKernelGGL((select_merge_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, S2,
-                         (int)ldc, k, idx, lens, Hq, S);
+                         (int)ldc, k, W, idx, bitmap, lens, Hq, S);
     else
       hipLaunchKernelGGL((select_merge_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx,
-                         S2, (int)ldc, k, idx, lens, Hq, S);
-    hipLaunchKernelGGL(idx_to_bitmap_kernel, dim3(rows), dim3(256), 0, st, idx, bitmap, S, k, W);
+                         S2, (int)ldc, k, W, idx, bitmap, lens, Hq, S);
     return hipGetLastError();
   }
-  if (S <= kSelThreads * 16) {
+  // the fewest keys per lane that hold the head: each wave owns 64 T
+  // consecutive tokens, so a larger T than needed leaves whole waves idle
+  if (S <= kSelThreads * 4) {
+    hipLaunchKernelGGL((select_regs_kernel<4>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
+                       idx, bitmap, lens, Hq);
+  } else if (S <= kSelThreads * 8) {
+    hipLaunchKernelGGL((select_regs_kernel<8>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
+                       idx, bitmap, lens, Hq);
+  } else if (S <= kSelThreads * 16) {
     hipLaunchKernelGGL((select_regs_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, W,
                        idx, bitmap, lens, Hq);
   } else if (S <= kSelThreads * kSelRegMaxT) {
@@ -930,9 +1027,7 @@ static hipError_t attend_td(const DecodePlan& p, const void* K_rot, const void* 
   });
   if (e != hipSuccess) return e;
   if (mid && (e = hipEventRecord(mid, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<T>), dim3(p.B * p.Hq), dim3(D), 0, st, part, static_cast<T*>(out),
-                     p.NAC, D);
-  return hipGetLastError();
+  return launch_combine<T, D>(part, static_cast<T*>(out), p.B * p.Hq, p.NAC, st);
 }
 
 hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, const float* qrot,
@@ -942,13 +1037,9 @@ hipError_t launch_attend(const DecodePlan& p, const void* K_rot, const void* V, 
     hipError_t e = launch_attend_mfma(p, K_rot, V, qsplit, bitmap, part, st);
     if (e != hipSuccess) return e;
     if (mid && (e = hipEventRecord(mid, st)) != hipSuccess) return e;
-    if (p.d == 64)
-      hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(p.B * p.Hq), dim3(64), 0, st, part,
-                         static_cast<bf16_t*>(out), p.NAC, 64);
-    else
-      hipLaunchKernelGGL((combine_kernel<bf16_t>), dim3(p.B * p.Hq), dim3(128), 0, st, part,
-                         static_cast<bf16_t*>(out), p.NAC, 128);
-    return hipGetLastError();
+    bf16_t* o = static_cast<bf16_t*>(out);
+    return p.d == 64 ? launch_combine<bf16_t, 64>(part, o, p.B * p.Hq, p.NAC, st)
+                     : launch_combine<bf16_t, 128>(part, o, p.B * p.Hq, p.NAC, st);
   }
   if (p.dt == 0)
     return p.d == 64 ? attend_td<float, 64>(p, K_rot, V, qrot, bitmap, part, out, st, mid)
