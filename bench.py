@@ -198,14 +198,21 @@ def score_stage_kernel(cfg) -> str:
     """The kernel that runs the score stage of a bf16 decode (the library's
     dispatch rule): scores and selection fused, one block per query head, when
     every query head has its own key head; fused per pair of query heads of a
-    group when the group size is even; otherwise the score kernel alone (the
-    selection then runs as its own stage)."""
+    group when the group size is even; for heads longer than 32768 tokens
+    selected in two stages, the scores fused with the first stage, one block
+    per query head and 16384-token chunk, when that gives 256 blocks;
+    otherwise the score kernel alone (the selection then runs as its own
+    stage)."""
     G = cfg.Hq // cfg.Hkv
     if cfg.dtype == "bf16" and cfg.S <= 16384:
         if cfg.Hq == cfg.Hkv and cfg.B * cfg.Hq >= 256:
             return "score_select_kernel"
         if G % 2 == 0 and cfg.B * cfg.Hq >= 512 and cfg.r <= 128:
             return "score_select_pair_kernel"
+    C = -(-cfg.S // 16384)
+    if (cfg.dtype == "bf16" and cfg.S > 32768 and cfg.k < cfg.S and cfg.k <= 16384 and C * cfg.k <= 32768
+            and cfg.B * cfg.Hq * C >= 256 and cfg.r <= 128):
+        return "score_select_chunk_kernel"
     return "score_mfma_kernel"
 
 

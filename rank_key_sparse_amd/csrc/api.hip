@@ -181,6 +181,11 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
   const bool aqua = aqua_r > 0;
   const bool fused = !aqua && dt == LOKI_BF16 && Hq == Hkv && S <= kFusedMaxS && (int64_t)B * Hq >= 256;
   const bool pair = !aqua && !fused && score_select_pair_fits(p) && (int64_t)B * Hq >= 2 * 256;
+  // long heads selected in two stages: the first stage fused with the scores
+  // (one block per query head and 16384-token chunk) when that fills the chip
+  const int ldc = (int)select_chunked_ldc(S, k);
+  const bool chunk = !aqua && ldc > 0 && k < S && score_select_chunk_fits(p) &&
+                     (int64_t)B * Hq * ((S + kSelChunk - 1) / kSelChunk) >= 256;
   float* qrot_s = qrot;
   uint16_t* qsplit_s = qsplit;
   DecodePlan ps = p;  // the score stage's plan
@@ -199,6 +204,12 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     if (fused) LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
     else LOKI_HIP(launch_score_select_pair(p, src, ld, q, P, qrot, qsplit, idx, bitmap, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+  } else if (chunk) {
+    int32_t* cidx = at<int32_t>(workspace, p.off_cidx);
+    uint32_t* ckey = at<uint32_t>(workspace, p.off_ckey);
+    LOKI_HIP(launch_score_select_chunk(ps, src, ld, qsplit_s, cidx, ckey, ldc, stream));
+    if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+    LOKI_HIP(launch_select_merge(B * Hq, S, k, p.W, ldc, ckey, cidx, idx, bitmap, lens, Hq, stream));
   } else {
     uint2* mm = select_needs_minmax(S) ? at<uint2>(workspace, p.off_mm) : nullptr;
     LOKI_HIP(launch_scores(ps, src, ld, qrot_s, qsplit_s, keys, true, p.Sp, mm, stream));

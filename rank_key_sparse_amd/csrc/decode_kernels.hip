@@ -958,6 +958,20 @@ size_t select_chunked_ldc(int S, int k) {
   return (size_t)S2;
 }
 
+// Second stage of the long-head selection over the candidate lists (ldc =
+// select_chunked_ldc(S, k) words per row).
+hipError_t launch_select_merge(int rows, int S, int k, int W, int ldc, const uint32_t* ckey, const int32_t* cidx,
+                               int32_t* idx, uint32_t* bitmap, const int32_t* lens, int Hq, hipStream_t st) {
+  if (!lens) Hq = 1;
+  if (ldc <= kSelThreads * 16)
+    hipLaunchKernelGGL((select_merge_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, ldc, ldc, k,
+                       W, idx, bitmap, lens, Hq, S);
+  else
+    hipLaunchKernelGGL((select_merge_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, ldc,
+                       ldc, k, W, idx, bitmap, lens, Hq, S);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* keys, const uint2* mm,
                          int nmm, uint32_t* gmasks, int32_t* idx, uint32_t* bitmap, hipStream_t st,
                          int32_t* cidx, uint32_t* ckey, const int32_t* lens, int Hq) {
@@ -969,13 +983,9 @@ hipError_t launch_select(int rows, int S, int Sp, int k, int W, const uint32_t* 
     const int S2 = (int)ldc;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(C, rows), dim3(kSelThreads), 0, st, keys, S, Sp, k, (int)ldc,
                        cidx, ckey, lens, Hq);
-    if (S2 <= kSelThreads * 16)
-      hipLaunchKernelGGL((select_merge_kernel<16>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx, S2,
-                         (int)ldc, k, W, idx, bitmap, lens, Hq, S);
-    else
-      hipLaunchKernelGGL((select_merge_kernel<kSelRegMaxT>), dim3(rows), dim3(kSelThreads), 0, st, ckey, cidx,
-                         S2, (int)ldc, k, W, idx, bitmap, lens, Hq, S);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_select_merge(rows, S, k, W, S2, ckey, cidx, idx, bitmap, lens, Hq, st);
   }
   // the fewest keys per lane that hold the head: each wave owns 64 T
   // consecutive tokens, so a larger T than needed leaves whole waves idle

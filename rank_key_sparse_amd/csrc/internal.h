@@ -102,6 +102,14 @@ bool score_select_pair_fits(const DecodePlan& p);
 hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
                                     float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
                                     hipStream_t st);
+// Long heads (bf16): fused scores + the first selection stage, one block per
+// (query head, chunk of kSelChunk tokens), into the candidate lists cidx /
+// ckey (ldc words per row); then launch_select_merge finishes the selection.
+bool score_select_chunk_fits(const DecodePlan& p);
+hipError_t launch_score_select_chunk(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                                     int32_t* cidx, uint32_t* ckey, int ldc, hipStream_t st);
+hipError_t launch_select_merge(int rows, int S, int k, int W, int ldc, const uint32_t* ckey, const int32_t* cidx,
+                               int32_t* idx, uint32_t* bitmap, const int32_t* lens, int Hq, hipStream_t st);
 hipError_t launch_attend_mfma(const DecodePlan& p, const void* K_rot, const void* V,
                               const uint16_t* qsplit, const uint32_t* bitmap, float* part,
                               hipStream_t st);

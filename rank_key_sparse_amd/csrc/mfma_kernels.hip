@@ -302,6 +302,104 @@ __global__ __launch_bounds__(kFusedThreads) void score_select_kernel(
 }
 
 // ============================================================================
+// Long heads (bf16): fused approximate scores + the first selection stage, one
+// block of 1024 threads per (query head, chunk of kSelChunk tokens).  The
+// chunk's keys stay in LDS (they never go to HBM and back), and the block
+// keeps the chunk's top-k with their keys in the candidate lists, chunk c at
+// offset c k, positions made absolute, exactly as the workspace-key first
+// stage does; free slots of a chunk with at most k tokens (or past the
+// sequence's end) get index -1 and key 0, below every score's key.  The G
+// query heads of a group's chunk get block ids with the same value mod 8 (one
+// XCD) and consecutive dispatch order, so they share the chunk's reads in L2.
+// ============================================================================
+constexpr int kChunkThreads = 1024;
+
+template <int KS>
+__global__ __launch_bounds__(kChunkThreads) void score_select_chunk_kernel(
+    const bf16_t* __restrict__ src, int ld, const uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv,
+    int Scap, int C, int d, int r, int k, int ldc, int32_t* __restrict__ cidx, uint32_t* __restrict__ ckey,
+    const int32_t* __restrict__ lens) {
+  constexpr int NWV = kChunkThreads / 64;
+  constexpr int UK = 8 / KS;
+  constexpr int U = UK < 1 ? 1 : UK;  // tiles in flight per wave
+  constexpr int T = kSelChunk / kChunkThreads;  // keys per lane in the selection
+  extern __shared__ __align__(16) uint32_t lk[];  // [kSelChunk] keys
+  __shared__ uint32_t sel[kNB];
+  __shared__ uint32_t take[kSelChunk / 32];
+  __shared__ SelScratch<kChunkThreads> sh;
+  const int G = Hq / Hkv;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gh = slot % G, unit = (slot / G) * 8 + xcd;  // unit = (group, chunk)
+  if (unit >= B * Hkv * C) return;  // padding block (uniform)
+  const int gi = unit / C, c = unit - gi * C;
+  const int b = gi / Hkv, kv = gi - b * Hkv;
+  const int S = seq_len(lens, b, Scap);  // this sequence's tokens
+  const int base = c * kSelChunk;
+  const int L = min(kSelChunk, S - base);  // <= 0 past the sequence's end
+  const size_t row = (size_t)b * Hq + (size_t)kv * G + gh;
+  int32_t* oi = cidx + row * ldc + (size_t)c * k;
+  uint32_t* ok = ckey + row * ldc + (size_t)c * k;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, q = lane >> 4;
+  if (L <= 0) {
+    for (int j = tid; j < k; j += kChunkThreads) {
+      oi[j] = -1;
+      ok[j] = 0u;
+    }
+    return;
+  }
+
+  bf16x8_t qa[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qa[s] = q_rows(qsplit, row, d, 1, r, m, 32 * s + 8 * q);
+
+  // tiles of 16 tokens, wave w takes tiles w + NWV i in double-buffered
+  // batches of U; unconditional loads (token clamped into the chunk)
+  const bf16_t* cbase = src + ((size_t)gi * Scap + base) * ld;
+  const int nbat = ((L + 15) / 16 + NWV * U - 1) / (NWV * U);
+  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, L - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(cbase + (size_t)t * ld + min(32 * s + 8 * q, ld - 8));
+    }
+  };
+  auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const uint4 x = 32 * s + 8 * q < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
+      }
+      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token (lanes 0..15)
+      if (q == 0 && t < L) lk[t] = score_key(sum_split_rows(acc));
+    }
+  };
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);
+  for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
+    load_batch(bi + 1, a1);
+    score_batch(bi, a0);
+    load_batch(bi + 2, a0);
+    score_batch(bi + 1, a1);
+  }
+  __syncthreads();
+  if (L <= k) {  // the whole chunk is a candidate
+    for (int j = tid; j < k; j += kChunkThreads) {
+      oi[j] = j < L ? base + j : -1;
+      ok[j] = j < L ? lk[j] : 0u;
+    }
+    return;
+  }
+  uint32_t key[T];  // the selection's register layout
+  load_regs<T>(lk, L, key);
+  select_regs<kChunkThreads, T>(key, sel, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base);
+}
+
+// ============================================================================
 // Fused approximate scores + top-k for grouped heads (G even): one block of
 // 1024 threads per pair of query heads of a (b, kv) group, one block per CU.
 // A CU's vector-memory path, not HBM, limits a kernel in which each query
@@ -820,6 +918,41 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
     default: return hipErrorInvalidValue;
   }
 #undef LOKI_SS
+  return hipGetLastError();
+}
+
+bool score_select_chunk_fits(const DecodePlan& p) {
+  return p.dt == 1 && p.r <= 128 && p.d % 8 == 0;
+}
+
+hipError_t launch_score_select_chunk(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
+                                     int32_t* cidx, uint32_t* ckey, int ldc, hipStream_t st) {
+  if (!score_select_chunk_fits(p)) return hipErrorInvalidValue;
+  const int C = (p.S + kSelChunk - 1) / kSelChunk;
+  const long long units = (long long)p.B * p.Hkv * C;
+  const long long nblk = (units + 7) / 8 * 8 * p.G;
+  if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+  const size_t lds = (size_t)kSelChunk * sizeof(uint32_t);
+  const dim3 grid((unsigned)nblk), block(kChunkThreads);
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  const int ks = (p.r + 31) / 32;
+  hipError_t e = hipSuccess;
+#define LOKI_SC(K)                                                                                       \
+  case K:                                                                                                \
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_chunk_kernel<K>),                \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                       \
+    if (e != hipSuccess) return e;                                                                       \
+    hipLaunchKernelGGL((score_select_chunk_kernel<K>), grid, block, lds, st, s, ld, qsplit, p.B, p.Hq,   \
+                       p.Hkv, p.S, C, p.d, p.r, p.k, ldc, cidx, ckey, p.lens);                           \
+    break;
+  switch (ks) {
+    LOKI_SC(1)
+    LOKI_SC(2)
+    LOKI_SC(3)
+    LOKI_SC(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef LOKI_SC
   return hipGetLastError();
 }
 

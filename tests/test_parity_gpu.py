@@ -393,6 +393,7 @@ VARLEN = [
     ("regs16_two_kernel", 9, 8, 2, 4000, 128, "bf16", 32, 300, 32),
     ("regs32_two_kernel", 9, 4, 2, 20000, 64, "bf16", 16, 700, None),
     ("chunked", 9, 4, 2, 40000, 128, "bf16", 16, 1500, 16),
+    ("chunked_fused", 4, 32, 8, 40000, 128, "bf16", 16, 1500, 16),
     ("global", 9, 2, 1, 40000, 64, "bf16", 16, 20000, None),
     ("f32", 9, 6, 2, 1200, 64, "f32", 8, 50, None),
 ]
@@ -472,6 +473,9 @@ EDGE = [
     ("G8_f32_d128", 1, 16, 2, 1111, 128, "f32", 24, 128),
     ("d64_bf16_r64", 3, 8, 8, 640, 64, "bf16", 64, 64),
     ("chunked_select", 1, 4, 2, 40000, 128, "bf16", 32, 1500),
+    # the first stage fused with the scores (>= 256 blocks of query head x chunk)
+    ("chunked_fused_r40", 2, 64, 8, 40000, 128, "bf16", 40, 1500),
+    ("chunked_fused_d64_G4", 3, 32, 8, 50000, 64, "bf16", 64, 3000),
     ("global_select", 1, 2, 1, 40000, 64, "bf16", 16, 20000),
     # fused score+select path (MHA, >= 256 heads, S <= 16384)
     ("fused_ragged_r24", 16, 16, 16, 1000, 128, "bf16", 24, 77),
