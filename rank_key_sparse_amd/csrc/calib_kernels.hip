@@ -325,8 +325,9 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   constexpr int NB = NP * (NP + 1) / 2;                          // 2 x 2 blocks j <= j2
   constexpr int NIDS = (NB + kJacobiThreads - 1) / kJacobiThreads;  // per thread
   extern __shared__ __align__(16) double sC[];
-  __shared__ double s_c[NP], s_s[NP], s_t[NP];
-  __shared__ int s_p[NP], s_q[NP];  // this round's pairs
+  __shared__ double2 s_cs[NP];  // this round's (c, s) per pair
+  __shared__ double s_t[NP];
+  __shared__ int2 s_pq[NP];     // this round's pairs (p < q)
   __shared__ int s_rot;
 
   const int kv = blockIdx.x, tid = threadIdx.x;
@@ -370,11 +371,9 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
           s = t * c;
           s_rot = 1;
         }
-        s_c[tid] = c;
-        s_s[tid] = s;
+        s_cs[tid] = make_double2(c, s);
         s_t[tid] = t;
-        s_p[tid] = p;
-        s_q[tid] = q;
+        s_pq[tid] = make_int2(p, q);
         lg[(size_t)round * NP + tid] = make_double2(c, s);
       }
       __syncthreads();
@@ -382,8 +381,10 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
       for (int u = 0; u < NIDS; ++u) {
         const int j = bj[u], j2 = bj2[u];
         if (j < 0) break;
-        const int p = s_p[j], q = s_q[j];
-        const double c = s_c[j], s = s_s[j];
+        const int2 pq = s_pq[j];
+        const int p = pq.x, q = pq.y;
+        const double2 cs = s_cs[j];
+        const double c = cs.x, s = cs.y;
         if (j == j2) {
           if (s != 0.0) {
             const double t = s_t[j], g = U(p, q);
@@ -393,8 +394,10 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
           }
           continue;
         }
-        const int p2 = s_p[j2], q2 = s_q[j2];
-        const double c2 = s_c[j2], s2 = s_s[j2];
+        const int2 pq2 = s_pq[j2];
+        const int p2 = pq2.x, q2 = pq2.y;
+        const double2 cs2 = s_cs[j2];
+        const double c2 = cs2.x, s2 = cs2.y;
         const double m00 = U(p, p2), m01 = U(p, q2), m10 = U(q, p2), m11 = U(q, q2);
         // rows: J^T M; columns: (J^T M) J'
         const double l00 = c * m00 - s * m10, l01 = c * m01 - s * m11;
