@@ -322,8 +322,10 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   constexpr int DS = D + 1;
   constexpr double kTol = 1e-14;
   constexpr double kTiny = 1e-300;
-  constexpr int NB = NP * (NP + 1) / 2;                          // 2 x 2 blocks j <= j2
-  constexpr int NIDS = (NB + kJacobiThreads - 1) / kJacobiThreads;  // per thread
+  constexpr int NOFF = NP * (NP - 1) / 2;  // off-diagonal 2 x 2 blocks j < j2
+  constexpr int NDT = NP / 2;              // threads holding the diagonal blocks, two each
+  static_assert(NOFF <= 2 * kJacobiThreads, "at most two off-diagonal blocks per thread");
+  static_assert(NOFF - kJacobiThreads <= kJacobiThreads - NDT, "diagonal threads hold at most one off-diagonal block");
   extern __shared__ __align__(16) double sC[];
   __shared__ double2 s_cs[NP];  // this round's (c, s) per pair
   __shared__ double s_t[NP];
@@ -333,18 +335,22 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   const int kv = blockIdx.x, tid = threadIdx.x;
   const double* Ch = Cg + (size_t)kv * D * D;
   double2* lg = rlog + (size_t)kv * jacobi_max_rounds(D) * NP;
-  // this thread's blocks (the same every round): the upper triangle of
-  // blocks packed densely over the threads -- fold i holds row i
-  // (j2 = i .. NP-1) and row NP-1-i (j2 = NP-1-i .. NP-1)
-  int bj[NIDS], bj2[NIDS];
+  // this thread's blocks (the same every round).  The off-diagonal blocks
+  // are packed densely over the threads, at most two each (fold i holds row
+  // i, j2 = i+1 .. NP-1, and row NP-1-i, j2 = NP-i .. NP-1); the NP cheap
+  // diagonal blocks go two each to the last NP/2 threads, which hold at most
+  // one off-diagonal block, so that no thread updates three blocks a round
+  // and the block loop has no branch between the two kinds.
+  int bj[2], bj2[2];
 #pragma unroll
-  for (int u = 0; u < NIDS; ++u) {
+  for (int u = 0; u < 2; ++u) {
     const int id = tid + u * kJacobiThreads;
-    const int fi = id / (NP + 1), fc = id - fi * (NP + 1);
-    const bool lo = fc < NP - fi;
-    bj[u] = id < NB ? (lo ? fi : NP - 1 - fi) : -1;
-    bj2[u] = lo ? fi + fc : fc - 1;
+    const int fi = id / (NP - 1), fc = id - fi * (NP - 1);
+    const bool lo = fc < NP - 1 - fi;
+    bj[u] = id < NOFF ? (lo ? fi : NP - 1 - fi) : -1;
+    bj2[u] = lo ? fi + 1 + fc : fc + 1;
   }
+  const int jd = 2 * (tid - (kJacobiThreads - NDT));  // this thread's diagonal blocks jd, jd + 1 (if >= 0)
   auto U = [&](int x, int y) -> double& { return sC[min(x, y) * DS + max(x, y)]; };
 
   for (int e = tid; e < D * D; e += kJacobiThreads) {
@@ -378,22 +384,13 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
       }
       __syncthreads();
 #pragma unroll
-      for (int u = 0; u < NIDS; ++u) {
+      for (int u = 0; u < 2; ++u) {
         const int j = bj[u], j2 = bj2[u];
         if (j < 0) break;
         const int2 pq = s_pq[j];
         const int p = pq.x, q = pq.y;
         const double2 cs = s_cs[j];
         const double c = cs.x, s = cs.y;
-        if (j == j2) {
-          if (s != 0.0) {
-            const double t = s_t[j], g = U(p, q);
-            U(p, p) -= t * g;
-            U(q, q) += t * g;
-            U(p, q) = 0.0;
-          }
-          continue;
-        }
         const int2 pq2 = s_pq[j2];
         const int p2 = pq2.x, q2 = pq2.y;
         const double2 cs2 = s_cs[j2];
@@ -406,6 +403,20 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
         U(p, q2) = s2 * l00 + c2 * l01;
         U(q, p2) = c2 * l10 - s2 * l11;
         U(q, q2) = s2 * l10 + c2 * l11;
+      }
+      if (jd >= 0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int j = jd + e;
+          const int2 pq = s_pq[j];
+          const int p = pq.x, q = pq.y;
+          if (s_cs[j].y != 0.0) {
+            const double t = s_t[j], g = U(p, q);
+            U(p, p) -= t * g;
+            U(q, q) += t * g;
+            U(p, q) = 0.0;
+          }
+        }
       }
       __syncthreads();
     }
