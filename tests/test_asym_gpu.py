@@ -81,6 +81,11 @@ CASES = {
     "mha_fused": CONFIGS["C2"].scaled(S=2048, B=8),
     "r64": CONFIGS["C5"].scaled(S=4096, B=1),
     "f32": CONFIGS["C1"].replace(B=2, Hq=4, Hkv=2),
+    # heads over 32768 tokens: two-stage selection over 16384-token chunks,
+    # with the first stage in its own kernel (96 head x chunk blocks) and
+    # fused with the scores (288 blocks)
+    "long_chunked": CONFIGS["C4"].scaled(S=40000),
+    "long_chunked_fused": CONFIGS["C4"].scaled(S=40000, B=3),
 }
 
 
