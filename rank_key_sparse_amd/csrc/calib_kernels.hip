@@ -752,12 +752,15 @@ bool make_asym_plan(AsymPlan& p, int N, int Hq, int B, int Hkv, int S, int d, in
   auto take = [&](size_t n) { const size_t o = off; off = align_up(off + n, 256); return o; };
   p.off_part = take(part);
   p.off_Cqh = take((size_t)Hq * dd);
-  p.off_log = take((size_t)Hkv * jacobi_max_rounds(d) * (d / 2) * 2 * sizeof(double));
-  p.off_nr = take((size_t)Hkv * sizeof(int));
-  p.off_lam = take((size_t)Hkv * d * sizeof(double));
+  // the eigensolver's scratch for 2 Hkv heads: Cq and Ck are diagonalised in one launch
+  p.off_log = take((size_t)2 * Hkv * jacobi_max_rounds(d) * (d / 2) * 2 * sizeof(double));
+  p.off_nr = take((size_t)2 * Hkv * sizeof(int));
+  p.off_lam = take((size_t)2 * Hkv * d * sizeof(double));
+  p.off_V2 = take((size_t)2 * Hkv * dd);
   for (int m = 0; m < kAsymMats; ++m) p.off_mat[m] = take((size_t)Hkv * dd);
   p.bytes = off;
-  return true;
+  // that launch reads Cq and Ck as one [2 Hkv, d, d] array
+  return p.off_mat[1] == p.off_mat[0] + (size_t)Hkv * dd;
 }
 
 hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const void* K, void* A, void* Bm, void* ws,
@@ -783,9 +786,9 @@ hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const
   hipLaunchKernelGGL(pool_kernel, dim3((DD + 255) / 256, H), dim3(256), 0, st, Cqh, Ck, 1, DD, 1.0 / (double)p.BS);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 mg(D, H), mb(D);
-  auto psd = [&](const double* Vv, double* out, int mode) {
-    if (D == 128) hipLaunchKernelGGL(psd_fn_kernel<128>, mg, mb, 0, st, Vv, lam, out, mode);
-    else hipLaunchKernelGGL(psd_fn_kernel<64>, mg, mb, 0, st, Vv, lam, out, mode);
+  auto psd = [&](const double* Vv, const double* lv, double* out, int mode) {
+    if (D == 128) hipLaunchKernelGGL(psd_fn_kernel<128>, mg, mb, 0, st, Vv, lv, out, mode);
+    else hipLaunchKernelGGL(psd_fn_kernel<64>, mg, mb, 0, st, Vv, lv, out, mode);
     return hipGetLastError();
   };
   auto mm = [&](const double* X, const double* Y, double* out, int tx) {
@@ -793,11 +796,14 @@ hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const
     else hipLaunchKernelGGL(matmul_kernel<64>, mg, mb, 0, st, X, Y, out, tx);
     return hipGetLastError();
   };
-  // Cq^{1/2}, Cq^{-1/2}, Ck^{1/2}, Ck^{-1/2}
-  if ((e = launch_sym_eig(D, H, Cq, rlog, nr, lam, Vq, st)) != hipSuccess) return e;
-  if ((e = psd(Vq, Sq, 0)) != hipSuccess || (e = psd(Vq, Sqi, 1)) != hipSuccess) return e;
-  if ((e = launch_sym_eig(D, H, Ck, rlog, nr, lam, Vq, st)) != hipSuccess) return e;
-  if ((e = psd(Vq, Sk, 0)) != hipSuccess || (e = psd(Vq, Ski, 1)) != hipSuccess) return e;
+  // Cq^{1/2}, Cq^{-1/2}, Ck^{1/2}, Ck^{-1/2}: Cq and Ck (adjacent) diagonalised in one launch of
+  // 2 H heads, Cq's eigenpairs first
+  double* V2 = reinterpret_cast<double*>(w + p.off_V2);
+  if ((e = launch_sym_eig(D, 2 * H, Cq, rlog, nr, lam, V2, st)) != hipSuccess) return e;
+  const double* Vk = V2 + (size_t)H * DD;
+  const double* lamk = lam + (size_t)H * D;
+  if ((e = psd(V2, lam, Sq, 0)) != hipSuccess || (e = psd(V2, lam, Sqi, 1)) != hipSuccess) return e;
+  if ((e = psd(Vk, lamk, Sk, 0)) != hipSuccess || (e = psd(Vk, lamk, Ski, 1)) != hipSuccess) return e;
   // W = Cq^{1/2} Ck^{1/2}; V, S^2 from W^T W
   if ((e = mm(Sq, Sk, W, 0)) != hipSuccess || (e = mm(W, W, WtW, 1)) != hipSuccess) return e;
   if ((e = launch_sym_eig(D, H, WtW, rlog, nr, lam, Vq, st)) != hipSuccess) return e;

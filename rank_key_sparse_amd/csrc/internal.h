@@ -143,7 +143,7 @@ struct AsymPlan {
   CalibPlan qp, kp;
   int Hq, Hkv, G, d, r, dt, N;
   long long BS;  // key rows per head
-  size_t off_part, off_Cqh, off_log, off_nr, off_lam, off_mat[kAsymMats], bytes;
+  size_t off_part, off_Cqh, off_log, off_nr, off_lam, off_V2, off_mat[kAsymMats], bytes;
 };
 bool make_asym_plan(AsymPlan& p, int N, int Hq, int B, int Hkv, int S, int d, int r, int dt);
 hipError_t launch_calibrate_asym(const AsymPlan& p, const void* q_samples, const void* K, void* A, void* Bm, void* ws,
