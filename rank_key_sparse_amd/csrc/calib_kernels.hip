@@ -37,6 +37,7 @@ constexpr int kGramFlush = 8;       // tiles summed in fp32 before adding into f
 constexpr int kGramBlocks = 512;    // Gram blocks per call (all heads), before rounding
 constexpr int kJacobiThreads = 1024;
 constexpr int kJacobiMaxSweeps = 48;
+constexpr double kJacobiSmallT = 1e-4;  // a sweep whose rotations all had |tan| below this may end the iteration
 
 // Rounds of the rotation log per head (d - 1 rounds per sweep).
 __host__ __device__ constexpr int jacobi_max_rounds(int D) { return kJacobiMaxSweeps * (D - 1); }
@@ -302,7 +303,8 @@ template <> __device__ __forceinline__ bf16_t from_f64<bf16_t>(double x) {
 // pairs at once: one thread per 2 x 2 block between pairs j <= j' (the
 // upper triangle of blocks packed densely over the threads).  The
 // rotations (c, s) of every round go to a log in the workspace.  Sweeps
-// repeat until one rotates nothing (at most kJacobiMaxSweeps).
+// repeat while some pair passes the rotation test (tested on the whole
+// matrix before each sweep; at most kJacobiMaxSweeps).
 //
 // jacobi_v_kernel (one wave per row of V): V = I J_1 J_2 ... from the log,
 // partner columns exchanged by lane permutes.
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   __shared__ double2 s_cs[NP];  // this round's (c, s) per pair
   __shared__ double s_t[NP];
   __shared__ int2 s_pq[NP];     // this round's pairs (p < q)
-  __shared__ int s_rot;
+  __shared__ int s_rot, s_big;
 
   const int kv = blockIdx.x, tid = threadIdx.x;
   const double* Ch = Cg + (size_t)kv * D * D;
@@ -352,30 +354,63 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
   }
   const int jd = 2 * (tid - (kJacobiThreads - NDT));  // this thread's diagonal blocks jd, jd + 1 (if >= 0)
   auto U = [&](int x, int y) -> double& { return sC[min(x, y) * DS + max(x, y)]; };
+  // the rotation test of a pair (a, b its diagonal entries, g the off-diagonal one)
+  auto rotates = [](double a, double b, double g) {
+    return fabs(g) > kTiny && fabs(g) > kTol * sqrt(fabs(a)) * sqrt(fabs(b));
+  };
 
   for (int e = tid; e < D * D; e += kJacobiThreads) {
     const int i = e / D, j = e - i * D;
     if (i <= j) sC[i * DS + j] = Ch[e];
   }
-  if (tid == 0) s_rot = 0;
+  if (tid == 0) {
+    s_rot = 0;
+    s_big = 0;
+  }
   __syncthreads();
 
   int round = 0;
-  bool still = true;
-  for (int sweep = 0; sweep < kJacobiMaxSweeps && still; ++sweep) {
+  double tmax = 0.0;  // lanes tid < NP: the largest |t| this lane applied in the last sweep
+  for (int sweep = 0; sweep < kJacobiMaxSweeps; ++sweep) {
+    // A sweep rotates nothing exactly when no pair passes the rotation test
+    // on the current matrix (then nothing changes during it), so one pass
+    // over the pairs decides that instead of running such a sweep.  The pass
+    // runs before the first sweep and after a sweep whose rotations were all
+    // small (near convergence, where the next sweep may be empty); otherwise
+    // the sweep simply runs.
+    if (tid < NP && tmax >= kJacobiSmallT) s_big = 1;
+    __syncthreads();
+    if (s_big == 0) {  // the same value in every thread
+      bool any = false;
+      for (int e = tid; e < D * D; e += kJacobiThreads) {
+        const int x = e / D, y = e - x * D;
+        if (x < y && rotates(sC[x * DS + x], sC[y * DS + y], sC[x * DS + y])) any = true;
+      }
+      if (any) s_rot = 1;
+      __syncthreads();
+      const bool go = s_rot != 0;  // the same value in every thread
+      __syncthreads();
+      if (!go) break;
+    }
+    __syncthreads();  // every thread has read s_big and s_rot
+    if (tid == 0) {
+      s_big = 0;
+      s_rot = 0;
+    }
+    tmax = 0.0;
     for (int r = 0; r < D - 1; ++r, ++round) {
       if (tid < NP) {
         int p, q;
         jacobi_pair(r, tid, D, p, q);
         const double a = U(p, p), b = U(q, q), g = U(p, q);
         double c = 1.0, s = 0.0, t = 0.0;
-        if (fabs(g) > kTiny && fabs(g) > kTol * sqrt(fabs(a)) * sqrt(fabs(b))) {
+        if (rotates(a, b, g)) {
           const double tau = (b - a) / (2.0 * g);
           t = (fabs(tau) > 1e150) ? 0.5 / tau
                                   : (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
           c = 1.0 / sqrt(1.0 + t * t);
           s = t * c;
-          s_rot = 1;
+          tmax = fmax(tmax, fabs(t));
         }
         s_cs[tid] = make_double2(c, s);
         s_t[tid] = t;
@@ -420,12 +455,8 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_c_kernel(const double* 
       }
       __syncthreads();
     }
-    still = s_rot != 0;  // the same value in every thread
-    __syncthreads();
-    if (tid == 0) s_rot = 0;
-    __syncthreads();
   }
-  if (tid == 0) nrounds[kv] = still ? round : round - (D - 1);  // a last sweep without rotations is not replayed
+  if (tid == 0) nrounds[kv] = round;
   if (tid < D) lam_raw[(size_t)kv * D + tid] = sC[tid * DS + tid];
 }
 
