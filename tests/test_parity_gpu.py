@@ -476,6 +476,8 @@ EDGE = [
     # the first stage fused with the scores (>= 256 blocks of query head x chunk)
     ("chunked_fused_r40", 2, 64, 8, 40000, 128, "bf16", 40, 1500),
     ("chunked_fused_d64_G4", 3, 32, 8, 50000, 64, "bf16", 64, 3000),
+    # k near the largest two-stage k (C k <= 32768): the last chunk (7232 tokens) is all candidates; r = d
+    ("chunked_fused_k10000_r128", 3, 32, 8, 40000, 128, "bf16", 128, 10000),
     ("global_select", 1, 2, 1, 40000, 64, "bf16", 16, 20000),
     # fused score+select path (MHA, >= 256 heads, S <= 16384)
     ("fused_ragged_r24", 16, 16, 16, 1000, 128, "bf16", 24, 77),
