@@ -947,7 +947,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the decode shards over (batch, kv head) groups with no exchange; see the design notes)",
+              f"(the decode shards over (batch, kv head) groups with no exchange between GPUs)",
               file=sys.stderr)
         return 2
     if args.calibrate_copy:

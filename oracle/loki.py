@@ -21,8 +21,7 @@ What is computed, and where the pages say so:
   :func:`decode`; :func:`decode_varlen` for a batch of sequences of
   different lengths (each one a decode over its own prefix).
 
-Readings taken where the pages leave a step open (each is listed with its
-reason in the design notes):
+Readings taken where the pages leave a step open:
 
 1. "Slicing off the trailing dimensions" keeps the LEADING ``r`` rotated
    dimensions (the first columns of ``P`` carry the most key variance).
