@@ -50,9 +50,16 @@ def query_dims(q, P, r: int):
 def approx_scores(q, P, K_rot, r: int) -> np.ndarray:
     """``s[b,h,j] = sum_{c in I_h} q_rot[b,h,c] K_rot[b,kv,j,c]``, I_h the
     head's magnitude-selected dimensions."""
+    return scores_on_dims(q, P, K_rot, query_dims(q, P, r))
+
+
+def scores_on_dims(q, P, K_rot, dims) -> np.ndarray:
+    """The approximate scores of each query head on a given set of rotated
+    dimensions ``dims [B, Hq, r]``: ``s[b,h,j] = sum_{c in dims[b,h]}
+    q_rot[b,h,c] K_rot[b,kv,j,c]``."""
     B, Hq, Hkv, S, d, G = _shapes(q, K_rot)
     qr = rotate_queries(q, P)
-    dims = query_dims(q, P, r)
+    dims = np.asarray(dims)
     s = np.empty((B, Hq, S), dtype=np.float64)
     for b in range(B):
         for kv in range(Hkv):

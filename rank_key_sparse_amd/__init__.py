@@ -116,19 +116,29 @@ def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None):
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None, shape=None):
+    """Metadata checks of one tensor argument: type, dtype, rank, exact shape
+    (every buffer the kernels write is sized from the call's sizes, so an
+    output of another shape would be written out of bounds), contiguity and
+    the device of the call.  That the call's device is a GPU is checked once
+    per call by _gpu, after all of these."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device")
-    if device is not None and t.device != device:
-        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _gpu(t: torch.Tensor, name: str) -> None:
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -149,35 +159,30 @@ def loki_project_keys(K: torch.Tensor, P: torch.Tensor, K_rot: torch.Tensor | No
         if R is None:
             raise ValueError("lead_only needs R")
         _need(K, "K", ndim=4)
-        _need(P, "P", dtype=K.dtype, ndim=3, device=K.device)
         B, Hkv, S, d = K.shape
-        if tuple(P.shape) != (Hkv, d, d):
-            raise ValueError("P must be [Hkv, d, d]")
+        _need(P, "P", dtype=K.dtype, device=K.device, shape=(Hkv, d, d))
         if K_lead is None:
             K_lead = torch.empty((B, Hkv, S, R), dtype=K.dtype, device=K.device)
-        _need(K_lead, "K_lead", dtype=K.dtype, ndim=4, device=K.device)
-        if tuple(K_lead.shape) != (B, Hkv, S, R):
-            raise ValueError("K_lead must be [B, Hkv, S, R]")
+        _need(K_lead, "K_lead", dtype=K.dtype, device=K.device, shape=(B, Hkv, S, R))
+        _gpu(K, "K")
         _check(load_library().loki_project_keys_lead(_ptr(K), _ptr(P), None, _ptr(K_lead), R, B, Hkv, S, d,
                                                      _dtype_code(K), _stream(K)))
         return K_lead
     _need(K, "K", ndim=4)
-    _need(P, "P", dtype=K.dtype, ndim=3, device=K.device)
     B, Hkv, S, d = K.shape
-    if tuple(P.shape) != (Hkv, d, d):
-        raise ValueError("P must be [Hkv, d, d]")
+    _need(P, "P", dtype=K.dtype, device=K.device, shape=(Hkv, d, d))
     if K_rot is None:
         K_rot = torch.empty_like(K)
-    _need(K_rot, "K_rot", dtype=K.dtype, ndim=4, device=K.device)
+    _need(K_rot, "K_rot", dtype=K.dtype, device=K.device, shape=K.shape)
+    if R is not None:
+        if K_lead is None:
+            K_lead = torch.empty((B, Hkv, S, R), dtype=K.dtype, device=K.device)
+        _need(K_lead, "K_lead", dtype=K.dtype, device=K.device, shape=(B, Hkv, S, R))
+    _gpu(K, "K")
     lib = load_library()
     if R is None:
         _check(lib.loki_project_keys(_ptr(K), _ptr(P), _ptr(K_rot), B, Hkv, S, d, _dtype_code(K), _stream(K)))
         return K_rot
-    if K_lead is None:
-        K_lead = torch.empty((B, Hkv, S, R), dtype=K.dtype, device=K.device)
-    _need(K_lead, "K_lead", dtype=K.dtype, ndim=4, device=K.device)
-    if tuple(K_lead.shape) != (B, Hkv, S, R):
-        raise ValueError("K_lead must be [B, Hkv, S, R]")
     _check(lib.loki_project_keys_lead(_ptr(K), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, B, Hkv, S, d,
                                       _dtype_code(K), _stream(K)))
     return K_rot, K_lead
@@ -189,27 +194,22 @@ def loki_decode_aqua(q, P, K_rot, V, r: int, k: int, lens=None, out=None, idx=No
     rotated dims where the query is largest in magnitude (the token selection
     and exact attention are as in :func:`loki_decode`).  Returns ``(out, idx,
     dims [B,Hq,r] int32, info_loss [B,Hq] float32)``."""
-    _need(q, "q", ndim=3)
+    B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
     dev = q.device
-    B, Hq, d = q.shape
-    _need(P, "P", dtype=q.dtype, ndim=3, device=dev)
-    _need(K_rot, "K_rot", dtype=q.dtype, ndim=4, device=dev)
-    _need(V, "V", dtype=q.dtype, ndim=4, device=dev)
-    Hkv, S = K_rot.shape[1], K_rot.shape[2]
-    if tuple(K_rot.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d) or tuple(P.shape) != (Hkv, d, d):
-        raise ValueError("inconsistent shapes")
+    _need(V, "V", dtype=q.dtype, device=dev, shape=K_rot.shape)
     out = torch.empty_like(q) if out is None else out
     idx = torch.empty((B, Hq, k), dtype=torch.int32, device=dev) if idx is None else idx
     dims = torch.empty((B, Hq, r), dtype=torch.int32, device=dev) if dims is None else dims
     info_loss = torch.empty((B, Hq), dtype=torch.float32, device=dev) if info_loss is None else info_loss
-    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
-    _need(idx, "idx", dtype=torch.int32, ndim=3, device=dev)
-    _need(dims, "dims", dtype=torch.int32, ndim=3, device=dev)
-    _need(info_loss, "info_loss", dtype=torch.float32, ndim=2, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev, shape=(B, Hq, d))
+    _need(idx, "idx", dtype=torch.int32, device=dev, shape=(B, Hq, k))
+    _need(dims, "dims", dtype=torch.int32, device=dev, shape=(B, Hq, r))
+    _need(info_loss, "info_loss", dtype=torch.float32, device=dev, shape=(B, Hq))
     if lens is not None:
-        _need(lens, "lens", dtype=torch.int32, ndim=1, device=dev)
-        if lens.shape[0] != B:
-            raise ValueError("lens must be [B] int32")
+        _need(lens, "lens", dtype=torch.int32, device=dev, shape=(B,))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    _gpu(q, "q")
     dt = _dtype_code(q)
     lib = load_library()
     if workspace is None:
@@ -233,24 +233,21 @@ def loki_decode_asym(q, A, K_idx, K, V, r: int, k: int, lens=None, out=None, idx
     K_idx[..., :r]``, the k best tokens, exact attention with ``q`` over the
     unrotated keys ``K``.  A [Hkv,d,d] (first r columns used), K_idx
     [B,Hkv,S,R].  Returns ``(out, idx)``."""
-    _need(q, "q", ndim=3)
+    B, Hq, Hkv, S, d = _shapes(q, A, K, "A", "K")
     dev = q.device
-    B, Hq, d = q.shape
-    for t, n in ((A, "A"), (K_idx, "K_idx"), (K, "K"), (V, "V")):
-        _need(t, n, dtype=q.dtype, device=dev)
-    Hkv, S = K.shape[1], K.shape[2]
+    _need(K_idx, "K_idx", dtype=q.dtype, ndim=4, device=dev)
     R = K_idx.shape[3]
-    if (tuple(A.shape) != (Hkv, d, d) or tuple(K.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d)
-            or tuple(K_idx.shape[:3]) != (B, Hkv, S)):
-        raise ValueError("inconsistent shapes")
+    _need(K_idx, "K_idx", shape=(B, Hkv, S, R))
+    _need(V, "V", dtype=q.dtype, device=dev, shape=K.shape)
     out = torch.empty_like(q) if out is None else out
     idx = torch.empty((B, Hq, k), dtype=torch.int32, device=dev) if idx is None else idx
-    _need(out, "out", dtype=q.dtype, ndim=3, device=dev)
-    _need(idx, "idx", dtype=torch.int32, ndim=3, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev, shape=(B, Hq, d))
+    _need(idx, "idx", dtype=torch.int32, device=dev, shape=(B, Hq, k))
     if lens is not None:
-        _need(lens, "lens", dtype=torch.int32, ndim=1, device=dev)
-        if lens.shape[0] != B:
-            raise ValueError("lens must be [B] int32")
+        _need(lens, "lens", dtype=torch.int32, device=dev, shape=(B,))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    _gpu(q, "q")
     lib = load_library()
     if workspace is None:
         workspace = torch.empty(max(1, loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, q.dtype)),
@@ -280,8 +277,11 @@ def loki_calibrate_asym(q_samples, K, r: int, A=None, Bm=None, workspace=None):
         raise ValueError("inconsistent head dims")
     A = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev) if A is None else A
     Bm = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev) if Bm is None else Bm
-    _need(A, "A", dtype=K.dtype, ndim=3, device=dev)
-    _need(Bm, "Bm", dtype=K.dtype, ndim=3, device=dev)
+    _need(A, "A", dtype=K.dtype, device=dev, shape=(Hkv, d, d))
+    _need(Bm, "Bm", dtype=K.dtype, device=dev, shape=(Hkv, d, d))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    _gpu(K, "K")
     lib = load_library()
     if workspace is None:
         nb = int(lib.loki_calibrate_asym_workspace_bytes(N, Hq, B, Hkv, S, d, r))
@@ -307,19 +307,17 @@ def loki_calibrate_pca(K: torch.Tensor, P: torch.Tensor | None = None, eigvals: 
     dev = K.device
     if P is None:
         P = torch.empty((Hkv, d, d), dtype=K.dtype, device=dev)
-    _need(P, "P", dtype=K.dtype, ndim=3, device=dev)
-    if tuple(P.shape) != (Hkv, d, d):
-        raise ValueError("P must be [Hkv, d, d]")
+    _need(P, "P", dtype=K.dtype, device=dev, shape=(Hkv, d, d))
     if eigvals is None:
         eigvals = torch.empty((Hkv, d), dtype=torch.float64, device=dev)
-    _need(eigvals, "eigvals", dtype=torch.float64, ndim=2, device=dev)
-    if tuple(eigvals.shape) != (Hkv, d):
-        raise ValueError("eigvals must be [Hkv, d]")
+    _need(eigvals, "eigvals", dtype=torch.float64, device=dev, shape=(Hkv, d))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    _gpu(K, "K")
     lib = load_library()
     nbytes = int(lib.loki_calibrate_workspace_bytes(B, Hkv, S, d))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", dtype=torch.uint8, device=dev)
     if events is None:
         _check(lib.loki_calibrate_pca(_ptr(K), _ptr(P), _ptr(eigvals), B, Hkv, S, d, _dtype_code(K),
                                       _ptr(workspace), workspace.numel(), _stream(K)))
@@ -340,22 +338,20 @@ def loki_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, P: torch.Tensor, po
     device tensor [B]; positions outside [0, S) write nothing."""
     _need(k_new, "k_new", ndim=3)
     dev = k_new.device
-    _need(v_new, "v_new", dtype=k_new.dtype, ndim=3, device=dev)
-    _need(P, "P", dtype=k_new.dtype, ndim=3, device=dev)
-    _need(pos, "pos", dtype=torch.int32, ndim=1, device=dev)
-    _need(K_rot, "K_rot", dtype=k_new.dtype, ndim=4, device=dev)
-    _need(V, "V", dtype=k_new.dtype, ndim=4, device=dev)
     B, Hkv, d = k_new.shape
+    _need(K_rot, "K_rot", dtype=k_new.dtype, ndim=4, device=dev)
     S = K_rot.shape[2]
-    if tuple(v_new.shape) != (B, Hkv, d) or tuple(P.shape) != (Hkv, d, d) or tuple(pos.shape) != (B,) \
-            or tuple(K_rot.shape) != (B, Hkv, S, d) or tuple(V.shape) != (B, Hkv, S, d):
-        raise ValueError("shape mismatch: k_new, v_new [B,Hkv,d], P [Hkv,d,d], pos [B], K_rot, V [B,Hkv,S,d]")
+    _need(K_rot, "K_rot", shape=(B, Hkv, S, d))
+    _need(v_new, "v_new", dtype=k_new.dtype, device=dev, shape=(B, Hkv, d))
+    _need(P, "P", dtype=k_new.dtype, device=dev, shape=(Hkv, d, d))
+    _need(pos, "pos", dtype=torch.int32, device=dev, shape=(B,))
+    _need(V, "V", dtype=k_new.dtype, device=dev, shape=(B, Hkv, S, d))
     R = 0
     if K_lead is not None:
         _need(K_lead, "K_lead", dtype=k_new.dtype, ndim=4, device=dev)
         R = K_lead.shape[-1]
-        if tuple(K_lead.shape) != (B, Hkv, S, R):
-            raise ValueError("K_lead must be [B, Hkv, S, R]")
+        _need(K_lead, "K_lead", shape=(B, Hkv, S, R))
+    _gpu(k_new, "k_new")
     _check(load_library().loki_append_kv(_ptr(k_new), _ptr(v_new), _ptr(P), _ptr(pos), _ptr(K_rot), _ptr(V),
                                          _ptr(K_lead), R, B, Hkv, S, d, _dtype_code(k_new), _stream(k_new)))
 
@@ -364,21 +360,21 @@ def loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dtype) -> int:
     return int(load_library().loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, _DT[dtype]))
 
 
-def _shapes(q, P, K_rot):
+def _shapes(q, P, K_rot, pname="P", kname="K_rot"):
+    """Sizes of a decode-family call from q [B,Hq,d] and the cache [B,Hkv,S,d];
+    the basis (or query-side matrix) must be [Hkv,d,d]."""
     _need(q, "q", ndim=3)
-    _need(P, "P", dtype=q.dtype, ndim=3, device=q.device)
-    _need(K_rot, "K_rot", dtype=q.dtype, ndim=4, device=q.device)
+    _need(K_rot, kname, dtype=q.dtype, ndim=4, device=q.device)
     B, Hq, d = q.shape
-    Bk, Hkv, S, dk = K_rot.shape
-    if Bk != B or dk != d or tuple(P.shape) != (Hkv, d, d):
-        raise ValueError("shape mismatch between q [B,Hq,d], P [Hkv,d,d] and K_rot [B,Hkv,S,d]")
+    Hkv, S = K_rot.shape[1], K_rot.shape[2]
+    _need(K_rot, kname, shape=(B, Hkv, S, d))
+    _need(P, pname, dtype=q.dtype, device=q.device, shape=(Hkv, d, d))
     return B, Hq, Hkv, S, d
 
 
 def _workspace(nbytes: int, device, workspace):
     if workspace is None:
         return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
-    _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=device)
     return workspace
 
 
@@ -394,27 +390,26 @@ def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=No
     tokens; idx rows of sequences shorter than k end with -1.
     """
     B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
-    _need(V, "V", dtype=q.dtype, ndim=4, device=q.device)
-    if tuple(V.shape) != tuple(K_rot.shape):
-        raise ValueError("V must have K_rot's shape")
-    lib = load_library()
-    dt = _dtype_code(q)
-    nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dt))
-    ws = _workspace(nbytes, q.device, workspace)
+    dev = q.device
+    _need(V, "V", dtype=q.dtype, device=dev, shape=K_rot.shape)
     if out is None:
         out = torch.empty_like(q)
     if idx is None:
-        idx = torch.empty((B, Hq, k), dtype=torch.int32, device=q.device)
-    _need(out, "out", dtype=q.dtype, ndim=3, device=q.device)
-    _need(idx, "idx", dtype=torch.int32, ndim=3, device=q.device)
+        idx = torch.empty((B, Hq, k), dtype=torch.int32, device=dev)
+    _need(out, "out", dtype=q.dtype, device=dev, shape=(B, Hq, d))
+    _need(idx, "idx", dtype=torch.int32, device=dev, shape=(B, Hq, k))
     if K_lead is not None:
-        _need(K_lead, "K_lead", dtype=q.dtype, ndim=4, device=q.device)
-        if tuple(K_lead.shape[:3]) != (B, Hkv, S):
-            raise ValueError("K_lead must be [B, Hkv, S, R]")
+        _need(K_lead, "K_lead", dtype=q.dtype, ndim=4, device=dev)
+        _need(K_lead, "K_lead", shape=(B, Hkv, S, K_lead.shape[3]))
     if lens is not None:
-        _need(lens, "lens", dtype=torch.int32, ndim=1, device=q.device)
-        if lens.shape[0] != B:
-            raise ValueError("lens must be [B] int32")
+        _need(lens, "lens", dtype=torch.int32, device=dev, shape=(B,))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=dev)
+    _gpu(q, "q")
+    lib = load_library()
+    dt = _dtype_code(q)
+    nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, r, k, dt))
+    ws = _workspace(nbytes, dev, workspace)
     if events is not None:
         if len(events) != 6:
             raise ValueError("events must hold 6 torch.cuda.Event objects")
@@ -440,6 +435,9 @@ def loki_decode(q, P, K_rot, V, r: int, k: int, out=None, idx=None, workspace=No
 def loki_scores(q, P, K_rot, r: int, workspace=None):
     """Approximate scores ``[B,Hq,S]`` fp32 over the leading ``r`` rotated dims."""
     B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+    _gpu(q, "q")
     lib = load_library()
     dt = _dtype_code(q)
     nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, max(1, min(r, d)), 1, dt))
@@ -453,8 +451,13 @@ def loki_scores(q, P, K_rot, r: int, workspace=None):
 def loki_select_topk(scores: torch.Tensor, k: int, workspace=None) -> torch.Tensor:
     """Top-k indices (ascending, ties -> lower index) of each row of fp32 ``scores [..., S]``."""
     _need(scores, "scores", dtype=torch.float32)
+    if scores.dim() < 1:
+        raise ValueError("scores must have a last (token) dim")
     S = scores.shape[-1]
     rows = scores.numel() // max(S, 1)
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=scores.device)
+    _gpu(scores, "scores")
     lib = load_library()
     nbytes = int(lib.loki_select_workspace_bytes(rows, S, k))
     ws = _workspace(nbytes, scores.device, workspace)
@@ -467,9 +470,13 @@ def loki_select_topk(scores: torch.Tensor, k: int, workspace=None) -> torch.Tens
 def loki_attend(q, P, K_rot, V, idx, workspace=None):
     """Exact softmax attention over a given kept set ``idx [B,Hq,k]`` (int32)."""
     B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
-    _need(V, "V", dtype=q.dtype, ndim=4, device=q.device)
+    _need(V, "V", dtype=q.dtype, device=q.device, shape=K_rot.shape)
     _need(idx, "idx", dtype=torch.int32, ndim=3, device=q.device)
     k = idx.shape[-1]
+    _need(idx, "idx", shape=(B, Hq, k))
+    if workspace is not None:
+        _need(workspace, "workspace", dtype=torch.uint8, ndim=1, device=q.device)
+    _gpu(q, "q")
     lib = load_library()
     dt = _dtype_code(q)
     nbytes = int(lib.loki_decode_workspace_bytes(B, Hq, Hkv, S, d, d, k, dt))

@@ -433,11 +433,25 @@ __global__ __launch_bounds__(kSelThreads) void select_merge_kernel(const uint32_
   }
   for (int w = threadIdx.x; w < W; w += kSelThreads) brow[w] = 0u;  // ordered before the bits by the barriers below
   // every chunk filled its k slots (free ones with key 0, below every score's
-  // key), and the head has more than k real candidates: none is chosen
+  // key), and the head has more than k real candidates: none is chosen.  The
+  // value bins span the real candidates' keys only (key 0 decodes to NaN and
+  // would make the range degenerate); free slots fall into bin 0.
+  __shared__ uint32_t smm[2];
   uint32_t key[T];
   load_regs<T>(ckey + (size_t)row * ldc, S2, key);
+  {
+    const int nv = regs_valid<T>(S2);
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      if (i < nv && key[i] != 0u) { mn = min(mn, key[i]); mx = max(mx, key[i]); }
+    uint32_t kmin, kmax;
+    block_minmax<kSelThreads>(mn, mx, sh, kmin, kmax);
+    if (threadIdx.x == 0) { smm[0] = kmin; smm[1] = kmax; }
+    __syncthreads();  // sh.red is read by every thread before select_regs reuses sh
+  }
   select_regs<kSelThreads, T>(key, lds, take, S2, k, 2 * ((S2 + 63) / 64), orow, nullptr, sh,
-                              cidx + (size_t)row * ldc);
+                              cidx + (size_t)row * ldc, nullptr, 0, smm);
   __syncthreads();  // every thread's idx entries written
   for (int i = threadIdx.x; i < k; i += kSelThreads) {
     const int j = orow[i];

@@ -108,10 +108,12 @@ struct Binner {
     degenerate = !(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f);
   }
   // bin of a score value (the same map as of its key: key_score(score_key(s))
-  // is s, with -0 read as +0, which bins alike)
+  // is s, with -0 read as +0, which bins alike).  A value below fmin, or the
+  // NaN that key 0 (an empty candidate slot) decodes to, goes to bin 0: the
+  // max with 0 returns its non-NaN operand.
   __device__ __forceinline__ int of_score(float s) const {
     if (degenerate) return 0;
-    const int b = (int)((s - fmin) * scale);
+    const int b = (int)fmaxf((s - fmin) * scale, 0.f);
     return b < kNB - 1 ? b : kNB - 1;
   }
   __device__ __forceinline__ int operator()(uint32_t key) const { return of_score(key_score(key)); }

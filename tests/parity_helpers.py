@@ -46,3 +46,34 @@ def max_abs(a, b) -> float:
     a = a.double().cpu().numpy() if isinstance(a, torch.Tensor) else np.asarray(a, dtype=np.float64)
     b = b.double().cpu().numpy() if isinstance(b, torch.Tensor) else np.asarray(b, dtype=np.float64)
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def oracle_attend_rows(q, P, K_rot, V, idx, rows, lens=None) -> dict:
+    """The oracle's exact attention of each listed (b, h) row over the kept set
+    that ``idx[b, h]`` gives (entries < 0 dropped), on that row's own prefix
+    when ``lens`` is given: ``{(b, h): out [d] float64}``.  Each row is one
+    oracle call on its own (query head, key head) slice, so the other rows'
+    sets take no part."""
+    import oracle
+    Hq, Hkv, S = q.shape[1], K_rot.shape[1], K_rot.shape[2]
+    G = Hq // Hkv
+    res = {}
+    for b, h in rows:
+        kv = h // G
+        L = S if lens is None else min(max(int(lens[b]), 1), S)
+        sel = np.asarray(idx[b, h]).astype(np.int64)
+        sel = sel[sel >= 0]
+        o = oracle.attend(q[b:b + 1, h:h + 1], P[kv:kv + 1], K_rot[b:b + 1, kv:kv + 1, :L],
+                          V[b:b + 1, kv:kv + 1, :L], sel[None, None, :])
+        res[(b, h)] = o[0, 0]
+    return res
+
+
+def check_band_rows(out_gpu: np.ndarray, idx_gpu: np.ndarray, rows, q, P, K_rot, V, tol: float, lens=None):
+    """Rows whose kept set legitimately differs from the oracle's (inside the
+    tie band): the GPU output must be the oracle's attention over the GPU's
+    own kept set, to the output tolerance."""
+    want = oracle_attend_rows(q, P, K_rot, V, idx_gpu, rows, lens)
+    for (b, h), o in want.items():
+        err = float(np.max(np.abs(out_gpu[b, h] - o)))
+        assert err <= tol, f"band row {(b, h)}: output max-abs {err} > {tol} against the oracle on its own set"

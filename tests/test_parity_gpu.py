@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from loki_inputs import CONFIGS, make_inputs, make_integer_inputs
-from parity_helpers import OUT_TOL, check_index_sets, max_abs
+from parity_helpers import OUT_TOL, check_band_rows, check_index_sets, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -47,15 +47,9 @@ def run_decode(rks, x, r, k, check_out=True, R=None):
     if check_out:
         err = float(np.max(np.abs(og - out_o)[same])) if same.any() else 0.0
         assert err <= tol, f"output max-abs {err} > {tol}"
-    if differ:
-        # rows whose kept set legitimately differs (inside the tie band): the
-        # decode output must be the attention over ITS set, and the attention
-        # stage must match the oracle on the oracle's set
-        again = rks.loki_attend(q, P, Kr, V, idx_g)
-        on_o = rks.loki_attend(q, P, Kr, V, torch.from_numpy(idx_o.astype(np.int32)).to("cuda"))
-        for b, h in differ:
-            assert torch.equal(again[b, h], out_g[b, h])
-            assert max_abs(on_o[b, h], out_o[b, h]) <= tol
+    # rows whose kept set legitimately differs (inside the tie band): the
+    # output is the oracle's attention over the GPU's own set
+    check_band_rows(og, ig, differ, x["q"], x["P"], x["K_rot"], x["V"], tol)
     return out_g, idx_g, differ
 
 
@@ -338,6 +332,12 @@ def test_decode_graph_replay(gpu_lib, shape):
             gpu_lib.loki_decode(q, P, Kr, V, cfg.r, cfg.k, out=out, idx=idx, workspace=ws, K_lead=Kl)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    # the oracle's step for each query (selection with scores, attention)
+    ref = {}
+    for tag, qq in (("q", x["q"]), ("q2", q2.cpu())):
+        idx_o, s_o = oracle.select(qq, x["P"], x["K_rot"], cfg.r, cfg.k, return_scores=True)
+        ref[tag] = (qq, idx_o, s_o, oracle.attend(qq, x["P"], x["K_rot"], x["V"], idx_o))
+    tol = OUT_TOL[x["q"].dtype]
     q_orig = q.clone()
     for rep, tag in enumerate(("q", "q", "q2", "q", "q2")):
         q.copy_(q_orig if tag == "q" else q2)
@@ -349,6 +349,17 @@ def test_decode_graph_replay(gpu_lib, shape):
         o, i = want[tag]
         assert torch.equal(idx, i), (rep, tag)
         assert torch.equal(out.view(torch.int16), o.view(torch.int16)), (rep, tag)
+        # and against the oracle: kept sets by the tie-band rule, outputs to
+        # the tolerance (band rows on their own sets)
+        qq, idx_o, s_o, out_o = ref[tag]
+        ig = idx.cpu().numpy().astype(np.int64)
+        og = as_np(out)
+        differ = check_index_sets(ig, idx_o, s_o, cfg.k)
+        same = np.ones(og.shape[:2], dtype=bool)
+        for b, h in differ:
+            same[b, h] = False
+        assert float(np.max(np.abs(og - out_o)[same])) <= tol, (rep, tag)
+        check_band_rows(og, ig, differ, qq, x["P"], x["K_rot"], x["V"], tol)
 
 
 def run_decode_varlen(rks, x, lens, r, k, R=None):
@@ -377,12 +388,7 @@ def run_decode_varlen(rks, x, lens, r, k, R=None):
         same[b, h] = False
     err = float(np.max(np.abs(og - out_o)[same])) if same.any() else 0.0
     assert err <= tol, f"output max-abs {err} > {tol}"
-    if differ:
-        again = rks.loki_attend(q, P, Kr, V, idx_g)
-        on_o = rks.loki_attend(q, P, Kr, V, torch.from_numpy(idx_o.astype(np.int32)).to("cuda"))
-        for b, h in differ:
-            assert torch.equal(again[b, h], out_g[b, h])
-            assert max_abs(on_o[b, h], out_o[b, h]) <= tol
+    check_band_rows(og, ig, differ, x["q"], x["P"], x["K_rot"], x["V"], tol, lens=lens)
     return out_g, idx_g
 
 
@@ -440,6 +446,109 @@ def test_project_then_decode_c5_shape(gpu_lib):
     y = dict(x)
     y["K_rot"] = torch.from_numpy(exact).to(torch.bfloat16)
     run_decode(gpu_lib, y, cfg.r, cfg.k)
+
+
+# ---------------------------------------------------------------- planted boundary ties
+
+
+def _bits_step(row: torch.Tensor, c: int, step: int) -> torch.Tensor:
+    """A copy of the 1-D stored row with element c moved `step` representable
+    values in magnitude (sign-magnitude formats: +1 on the bit pattern is the
+    next value away from zero)."""
+    out = row.clone()
+    iv = out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32)
+    iv[c] += step
+    return out
+
+
+def plant_boundary_ties(x, cfg, max_groups=16):
+    """For one query head per (b, kv) group (up to max_groups groups), copies
+    the leading r dims of the head's k-th best token (by the oracle's
+    approximate scores) onto two tokens ranked below it: the first copy is an
+    exact tie with the k-th score; the second moves one to three of those dims
+    by one or two storage ulps each, chosen so that its score differs by the
+    smallest non-zero amount (far below 1e-5 relative).  Returns the new
+    inputs and the planted (b, h, jk, ja, jb)."""
+    import itertools
+    Kr = x["K_rot"].clone()
+    B, Hkv, S, _ = Kr.shape
+    G, k, r = cfg.Hq // cfg.Hkv, cfg.k, cfg.r
+    qr = oracle.rotate_queries(x["q"], x["P"])
+    s = oracle.approx_scores(x["q"], x["P"], Kr, r)
+    steps = (-2, -1, 1, 2)
+    planted = []
+    for gi in range(min(B * Hkv, max_groups)):
+        b, kv = divmod(gi, Hkv)
+        h = kv * G + gi % G
+        if k + 100 >= S:
+            continue
+        order = np.argsort(-s[b, h], kind="stable")
+        jk, ja, jb = (int(order[i]) for i in (k - 1, k + 40, k + 90))
+        row = Kr[b, kv, jk, :r].clone()
+        vals = row.double().numpy()
+        # score change of each single move (dim c, step), exact in float64
+        a = np.zeros((r, len(steps)))
+        for c in range(r):
+            if abs(vals[c]) < 1e-20:
+                continue  # no steps at zero (they would leave the normal range)
+            for si, st in enumerate(steps):
+                a[c, si] = qr[b, h, c] * (float(_bits_step(row, c, st)[c]) - vals[c])
+        best = (np.inf, ())
+        dims = [c for c in range(r) if abs(vals[c]) >= 1e-20]
+        for n in (1, 2, 3):
+            if n == 3 and r > 16:
+                break
+            for cs in itertools.combinations(dims, n):
+                for sis in itertools.product(range(len(steps)), repeat=n):
+                    dlt = sum(a[c, si] for c, si in zip(cs, sis))
+                    if dlt != 0.0 and abs(dlt) < best[0]:
+                        best = (abs(dlt), tuple(zip(cs, (steps[si] for si in sis))))
+        near = row
+        for c, st in best[1]:
+            near = _bits_step(near, c, st)
+        Kr[b, kv, ja, :r] = row
+        Kr[b, kv, jb, :r] = near
+        planted.append((b, h, jk, ja, jb))
+    y = dict(x)
+    y["K_rot"] = Kr
+    return y, planted
+
+
+PLANT = [
+    # (label, B, Hq, Hkv, S, d, dtype, r, k, R) -- one shape per dispatch path
+    ("pair_fused", 16, 32, 8, 2048, 128, "bf16", 32, 100, 32),
+    ("mha_fused", 16, 16, 16, 1500, 128, "bf16", 24, 77, None),
+    ("regs16_two_kernel", 9, 8, 2, 4000, 128, "bf16", 32, 300, 32),
+    ("regs32_two_kernel", 9, 4, 2, 20000, 64, "bf16", 16, 700, None),
+    ("chunked", 9, 4, 2, 40000, 128, "bf16", 16, 1500, 16),
+    ("chunked_fused", 4, 32, 8, 40000, 128, "bf16", 16, 1500, 16),
+    ("global", 3, 2, 1, 60000, 64, "bf16", 16, 17000, None),
+    ("f32", 9, 6, 2, 1200, 64, "f32", 8, 50, None),
+]
+
+
+@pytest.mark.parametrize("case", PLANT, ids=[c[0] for c in PLANT])
+def test_decode_planted_boundary_ties(gpu_lib, case):
+    label, B, Hq, Hkv, S, d, dt, r, k, R = case
+    print(f"\n[ties {label}] B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} {dt} r={r} k={k} R={R}", flush=True)
+    cfg = CONFIGS["C3"].replace(name=label, cfg_no=57, B=B, Hq=Hq, Hkv=Hkv, S=S, d=d, dtype=dt, r=r, k=k)
+    y, planted = plant_boundary_ties(make_inputs(cfg), cfg)
+    assert planted
+    # the planted ties sit at each planted head's k-th score, inside the band
+    _, s_o = oracle.select(y["q"], y["P"], y["K_rot"], r, k, return_scores=True)
+    for b, h, jk, ja, jb in planted:
+        sstar = np.sort(s_o[b, h])[::-1][k - 1]
+        assert s_o[b, h, ja] == s_o[b, h, jk]
+        assert abs(s_o[b, h, jb] - s_o[b, h, jk]) <= 1e-5 * abs(sstar)
+        assert abs(s_o[b, h, jk] - sstar) <= 1e-5 * abs(sstar)
+    _, idx_g, differ = run_decode(gpu_lib, y, r, k, R=R)
+    ig = idx_g.cpu().numpy()
+    # exact ties go to the lower index: of jk and ja, only the lower one can
+    # be kept without the other (bit-exact rule, no band needed)
+    for b, h, jk, ja, jb in planted:
+        lo, hi = min(jk, ja), max(jk, ja)
+        assert not (hi in ig[b, h] and lo not in ig[b, h]), (b, h)
+    print(f"[ties {label}] planted heads {len(planted)}, rows with band-equivalent sets: {len(differ)}", flush=True)
 
 
 # ---------------------------------------------------------------- decode parity
