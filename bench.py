@@ -48,7 +48,8 @@ STAGES = ["qrot", "scores", "select", "attend", "merge"]
 
 
 # the sources of the decode kernels whose counters profiles/traffic_*.json holds
-DECODE_SOURCES = ("common.h", "select_core.h", "mfma_kernels.hip", "decode_kernels.hip")
+DECODE_SOURCES = ("common.h", "select_core.h", "mfma_common.h", "mfma_kernels.hip", "pair_kernels.hip",
+                  "decode_kernels.hip")
 
 
 def kernel_source_hash() -> str:
@@ -284,6 +285,21 @@ def run(args) -> dict:
     ms_per_step = 1e3 * wall / args.steps
     print(f"[bench] region A: {args.steps} steps in {wall * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
+    # region A': the same plain steps with one event between consecutive
+    # steps (no events inside a step): per-step percentiles of the headline
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e_ in ev_a:
+        e_.record()
+    torch.cuda.synchronize()
+    ev_a[0].record()
+    for i in range(args.steps):
+        headline(i)
+        ev_a[i + 1].record()
+    torch.cuda.synchronize()
+    plain_us = np.sort([1e3 * ev_a[i].elapsed_time(ev_a[i + 1]) for i in range(args.steps)])
+    pct_plain = {"p10": float(np.percentile(plain_us, 10)), "p50": float(np.percentile(plain_us, 50)),
+                 "p90": float(np.percentile(plain_us, 90))}
+
     # region B: per-kernel durations from stage events on the library's stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for row in evs:  # create the underlying events
@@ -322,7 +338,10 @@ def run(args) -> dict:
     by_gather = U * cfg.d * 2 * e
     by_step = by_prefix + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
         + cfg.B * cfg.Hq * cfg.k * 4
-    per_kernel_bytes = {"scores": by_prefix, "attend": by_gather}
+    whole = score_stage_kernel(cfg) == "score_select_pair_kernel"
+    # the pair kernel runs the whole step (its later stage events are empty):
+    # its bytes per launch are the step's
+    per_kernel_bytes = {"scores": by_step if whole else by_prefix, "attend": by_gather}
     dom = max(("scores", "attend"), key=lambda s: stage_us[s])
     dom_kernel = {"scores": score_stage_kernel(cfg), "attend": "attend_mfma_kernel"}[dom]
     achieved = per_kernel_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
@@ -357,6 +376,7 @@ def run(args) -> dict:
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "frac_of_read_ceiling_step": round(step_gbs / READ_CEILING_GBS, 4),
+        "step_us_plain": {k_: round(v_, 2) for k_, v_ in pct_plain.items()},
         "step_us_events": {k_: round(v_, 2) for k_, v_ in pct.items()},
         "recall_at_k_vs_exact_topk": round(recall, 4),
         "alg_bytes_per_step": by_step,

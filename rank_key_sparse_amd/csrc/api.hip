@@ -197,12 +197,20 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     ld = d;
   }
   if (ev) LOKI_HIP(hipEventRecord(ev[0], stream));
-  if (!pair) LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
+  if (pair) {
+    // the whole step of each pair of heads in one kernel (rotation, scores,
+    // selection, exact attention); the later stage events follow it
+    if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
+    LOKI_HIP(launch_decode_pair(p, src, ld, q, P, K_rot, V, out, idx, plain_attn, stream));
+    if (ev)
+      for (int i = 2; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
+    return LOKI_OK;
+  }
+  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
   if (aqua) LOKI_HIP(launch_qdims(p, q, qrot, qrot_s, qsplit_s, dims, info, aqua_r, stream));
   if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
-  if (fused || pair) {
-    if (fused) LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
-    else LOKI_HIP(launch_score_select_pair(p, src, ld, q, P, qrot, qsplit, idx, bitmap, stream));
+  if (fused) {
+    LOKI_HIP(launch_score_select(p, src, ld, qsplit, idx, bitmap, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
   } else if (chunk) {
     int32_t* cidx = at<int32_t>(workspace, p.off_cidx);

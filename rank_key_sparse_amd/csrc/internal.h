@@ -102,6 +102,13 @@ bool score_select_pair_fits(const DecodePlan& p);
 hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
                                     float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
                                     hipStream_t st);
+// The whole decode of pairs of heads of a group in one launch (bf16, G even,
+// S <= kFusedMaxS, d 64 or 128): rotation, scores, selection into idx, and
+// the exact attention of both heads over their kept tokens into out.  With
+// plain, the exact stage takes the query itself against Kx = the unrotated
+// keys (asymmetric index); else q P against Kx = K_rot.
+hipError_t launch_decode_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                              const void* Kx, const void* V, void* out, int32_t* idx, bool plain, hipStream_t st);
 // Long heads (bf16): fused scores + the first selection stage, one block per
 // (query head, chunk of kSelChunk tokens), into the candidate lists cidx /
 // ckey (ldc words per row); then launch_select_merge finishes the selection.

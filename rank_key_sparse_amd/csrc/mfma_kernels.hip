@@ -30,75 +30,10 @@
 
 #include "common.h"
 #include "internal.h"
+#include "mfma_common.h"
 #include "select_core.h"
 
 namespace loki {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Lane n (< 4) of each 16-lane row receives x[n] + x[n+4] + x[n+8] + x[n+12]
-// of its row: DPP row_shl:4 then row_shl:8 (lane i reads lane i + k of its
-// row; reads past the row's end give 0).
-__device__ __forceinline__ float add_split_columns(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xF, 0xF, false));
-  return x;
-}
-
-// B operand of column group `grp` for the 8 dims starting at dim0 (a
-// multiple of 8): column n = head 4 grp + (n % 4), split part n / 4 (part 3
-// is the zero row), read with one 16-byte load from qsplit[row][part][d].
-// Elements at dims >= r are zeroed.
-__device__ __forceinline__ bf16x8_t q_operand(const uint16_t* __restrict__ qsplit, size_t head0, int d,
-                                              int G, int r, int grp, int n, int dim0) {
-  const int g = 4 * grp + (n & 3), part = n >> 2;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (g < G && dim0 < r) v = ldg16(qsplit + ((head0 + g) * 4 + part) * (size_t)d + dim0);
-  const int valid = r - dim0;
-  if (valid < 8) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t keep = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
-      w[e] &= keep;
-    }
-    v = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  return as_bf16x8(v);
-}
-
-// A operand of the transposed product (heads in rows, tokens in columns):
-// row m = 4 h + part holds split part `part` of head head0 + h (part 3 is the
-// zero row), for the 8 dims starting at dim0; one 16-byte load.  Rows of
-// heads >= NH and dims >= r are zero.  Lane l of the result then holds, in
-// its four accumulators, the split partial products of head l / 16 for token
-// (column) l % 16, so one lane finishes one score with two adds.
-__device__ __forceinline__ bf16x8_t q_rows(const uint16_t* __restrict__ qsplit, size_t head0, int d, int NH,
-                                           int r, int m, int dim0) {
-  const int h = m >> 2, part = m & 3;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (h < NH && dim0 < r) v = ldg16(qsplit + ((head0 + h) * 4 + part) * (size_t)d + dim0);
-  const int valid = r - dim0;
-  if (valid < 8) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t keep = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
-      w[e] &= keep;
-    }
-    v = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-  return as_bf16x8(v);
-}
-
-// The score of a lane's (head, token) from the split partial products:
-// (h + m) + (l + 0), the same grouping as add_split_columns.
-__device__ __forceinline__ float sum_split_rows(const floatx4_t& acc) {
-  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
 
 // ============================================================================
 // Approximate scores, bf16 source (K_rot with ld = d, or K_lead with ld = R).
@@ -397,180 +332,6 @@ __global__ __launch_bounds__(kChunkThreads) void score_select_chunk_kernel(
   uint32_t key[T];  // the selection's register layout
   load_regs<T>(lk, L, key);
   select_regs<kChunkThreads, T>(key, sel, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base);
-}
-
-// ============================================================================
-// Fused approximate scores + top-k for grouped heads (G even): one block of
-// 1024 threads per pair of query heads of a (b, kv) group, one block per CU.
-// A CU's vector-memory path, not HBM, limits a kernel in which each query
-// head re-reads its group's source, so the pair shares one read: the MFMA A
-// operand carries both heads' split rows, the two heads' scores (2 x S words)
-// go to LDS, and one two-head selection (select_regs2) keeps the k best of
-// each.  The G / 2 pairs of a group get block ids with the same value mod 8
-// (one XCD) and consecutive dispatch order, so their reads of the group's
-// source share L2.
-// ============================================================================
-template <int KS, int U>
-__global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
-    const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P,
-    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int Scap, int Sp, int d,
-    int r, int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap,
-    const int32_t* __restrict__ lens) {
-  constexpr int NWV = kPairThreads / 64;
-  constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
-  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
-  __shared__ __align__(16) uint32_t sel[2][kNB];
-  __shared__ uint32_t take[2][kFusedMaxS / 32];
-  __shared__ SelScratch<kPairThreads> sh[2];
-  __shared__ uint32_t smm[2][2];  // per head {min, max} key
-  __shared__ __align__(16) uint16_t sqs[2 * 4 * 128];  // the pair's split rows [h][part][d]
-  const int G = Hq / Hkv, NP = G / 2;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
-  if (gi >= B * Hkv) return;  // padding block (uniform)
-  const int b = gi / Hkv, kv = gi - b * Hkv;
-  const int S = seq_len(lens, b, Scap);  // this sequence's tokens
-  const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int m = lane & 15, q4 = lane >> 4;
-
-  // Wave w takes tiles w + NWV i (16 tokens each) in batches of U, double
-  // buffered: the next batch is in flight while this one is multiplied.
-  // Loads are unconditional (token clamped to S - 1, dims to the row) so
-  // that each tile waits only for its own data; dims >= r are zeroed at the
-  // MFMA, tiles past S are dropped at the store.
-  const bf16_t* base = src + (size_t)gi * Scap * ld;  // rows of the cache (capacity Scap)
-  const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
-  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q4, ld - 8));
-    }
-  };
-  // the pair's query rotation q_rot = q P[kv], with the arithmetic of
-  // qrot_kernel (d / 8-term FMA chains over eight j-slices, added in slice
-  // order): q_rot and its split go to the workspace for the attention, the
-  // split rows also to LDS as this block's A operands.  The P column slice
-  // and q are requested first, together, then the first K batch.
-  const int J = d / 8, pc = tid % d, js = tid / d;
-  bf16_t pv[16];  // P[kv][js J + jj][pc], J <= 16
-  {
-    const bf16_t* Pc = P + (size_t)kv * d * d + pc;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) pv[jj] = Pc[(size_t)min(js * J + jj, d - 1) * d];  // clamped: always in bounds
-  }
-  float* sq = reinterpret_cast<float*>(lk);  // [2][d]
-  float* sred = sq + 2 * d;                  // [8][2][d]
-  if (tid < 2 * d) sq[tid] = to_f32(q[row0 * d + tid]);  // the pair's heads are adjacent rows
-  uint4 a0[U][KS], a1[U][KS];
-  load_batch(0, a0);  // in flight during the rotation
-  {
-    __syncthreads();
-    if (js < 8) {
-      float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        if (jj < J) {
-          const int j = js * J + jj;
-          const float pj = to_f32(pv[jj]);
-          r0 = fmaf(sq[j], pj, r0);
-          r1 = fmaf(sq[d + j], pj, r1);
-        }
-      }
-      const int c = pc;
-      sred[(2 * js) * d + c] = r0;
-      sred[(2 * js + 1) * d + c] = r1;
-    }
-    __syncthreads();
-    if (tid < 2 * d) {
-      const int h = tid / d, cc = tid - h * d;
-      float v = sred[h * d + cc];
-      for (int t = 1; t < 8; ++t) v += sred[(2 * t + h) * d + cc];
-      qrot[(row0 + h) * d + cc] = v;
-      const bf16_t hi = f32_to_bf16(v);
-      const float e1 = v - to_f32(hi);
-      const bf16_t mid = f32_to_bf16(e1);
-      const bf16_t lo = f32_to_bf16(e1 - to_f32(mid));
-      const bf16_t part[4] = {hi, mid, lo, 0};
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        qsplit[((row0 + h) * 4 + pt) * d + cc] = part[pt];
-        sqs[(h * 4 + pt) * d + cc] = part[pt];
-      }
-    }
-    __syncthreads();
-  }
-
-  if (k >= S) {
-    keep_all<kPairThreads>(S, k, W, idx + row0 * k, bitmap + row0 * W);
-    keep_all<kPairThreads>(S, k, W, idx + (row0 + 1) * k, bitmap + (row0 + 1) * W);
-    return;
-  }
-
-  // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
-  bf16x8_t qa[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) qa[s] = q_rows(sqs, 0, d, 2, r, m, 32 * s + 8 * q4);
-
-  // the key range of each head, gathered while the keys are made (the
-  // selection then needs no pass of its own for it)
-  uint32_t kmn = 0xffffffffu, kmx = 0u;
-  auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const uint4 x = 32 * s + 8 * q4 < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
-      }
-      const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
-      if (q4 < 2 && t < S) {
-        const float sc = sum_split_rows(acc);
-        const uint32_t key = score_key(sc);
-        lk[q4 * Sp + t] = __float_as_uint(sc);  // the selection bins the value itself
-        kmn = min(kmn, key);
-        kmx = max(kmx, key);
-      }
-    }
-  };
-  // the selection's scratch is cleared now, under the score phase
-  for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
-  for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
-  if (tid < 2) {
-    smm[tid][0] = 0xffffffffu;
-    smm[tid][1] = 0u;
-    sh[tid].ccount = 0;
-  }
-  __syncthreads();  // orders the initialisation before the atomics below
-  for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
-    load_batch(bi + 1, a1);
-    score_batch(bi, a0);
-    load_batch(bi + 2, a0);
-    score_batch(bi + 1, a1);
-  }
-#pragma unroll
-  for (int x = 1; x < 16; x <<= 1) {  // over the 16 lanes of a head's row
-    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
-    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, x));
-  }
-  if (m == 0 && q4 < 2) {
-    atomicMin(&smm[q4][0], kmn);
-    atomicMax(&smm[q4][1], kmx);
-  }
-  __syncthreads();
-  uint32_t key[2][T];
-  load_regs<T>(lk, S, key[0]);
-  load_regs<T>(lk + Sp, S, key[1]);
-  uint32_t* const lds2[2] = {sel[0], sel[1]};
-  uint32_t* const take2[2] = {take[0], take[1]};
-  int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
-  uint32_t* const brow2[2] = {bitmap + row0 * W, bitmap + (row0 + 1) * W};
-  SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
-  const uint32_t* const kmm2[2] = {smm[0], smm[1]};
-  select_regs2<kPairThreads, T>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
 }
 
 // ============================================================================
@@ -953,41 +714,6 @@ hipError_t launch_score_select_chunk(const DecodePlan& p, const void* src, int l
     default: return hipErrorInvalidValue;
   }
 #undef LOKI_SC
-  return hipGetLastError();
-}
-
-bool score_select_pair_fits(const DecodePlan& p) {
-  return p.dt == 1 && p.G >= 2 && p.G % 2 == 0 && p.S <= kFusedMaxS && p.r <= 128 && p.d <= 128 && p.d % 8 == 0;
-}
-
-hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
-                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
-                                    hipStream_t st) {
-  if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
-  // keys [2][Sp], at least the rotation scratch [2 + 16][d] words
-  const size_t lds = (size_t)max(2 * p.Sp, 18 * p.d) * sizeof(uint32_t);
-  const int ngroups = p.B * p.Hkv;
-  const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
-  const bf16_t* s = static_cast<const bf16_t*>(src);
-  const int ks = (p.r + 31) / 32;
-  hipError_t e = hipSuccess;
-#define LOKI_SP(K)                                                                                      \
-  case K:                                                                                               \
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_pair_kernel<K, 8 / K>),        \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
-    if (e != hipSuccess) return e;                                                                      \
-    hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K>), grid, block, lds, st, s, ld,                \
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B,  \
-                       p.Hq, p.Hkv, p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap, p.lens);               \
-    break;
-  switch (ks) {
-    LOKI_SP(1)
-    LOKI_SP(2)
-    LOKI_SP(3)
-    LOKI_SP(4)
-    default: return hipErrorInvalidValue;
-  }
-#undef LOKI_SP
   return hipGetLastError();
 }
 

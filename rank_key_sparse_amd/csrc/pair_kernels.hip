@@ -1,0 +1,444 @@
+// Decode of grouped query heads two at a time (bf16 caches, G even, a
+// head's keys fit in LDS): one block of 1024 threads per pair of query heads
+// of a (b, kv) group rotates the pair's queries, scores every cached token
+// for both heads from one read of the group's score source, selects each
+// head's k best tokens and, in the fused form, runs the exact attention of
+// both heads over their kept tokens and writes the outputs: the whole decode
+// step of the pair in one launch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+#include "mfma_common.h"
+#include "select_core.h"
+
+namespace loki {
+
+// Max over the aligned 16-lane rows of a wave (every lane of a row ends with
+// the row's max): quad swaps, then the half-row and row mirrors.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  return v;
+}
+
+// ============================================================================
+// Pair kernel: one block of 1024 threads per pair of query heads of a
+// (b, kv) group, one block per CU.  A CU's vector-memory path, not HBM,
+// limits a kernel in which each query head re-reads its group's source, so
+// the pair shares one read: the MFMA A operand carries both heads' split
+// rows, the two heads' scores (2 x S words) go to LDS, and one two-head
+// selection (select_regs2) keeps the k best of each.  The G / 2 pairs of a
+// group get block ids with the same value mod 8 (one XCD) and consecutive
+// dispatch order, so their reads of the group's source share L2.
+//
+// MODE 0: the selection's kept-token bitmaps, q_rot and its split go to the
+//         workspace for the separate attention kernels.
+// MODE 1: the fused decode.  The bitmaps stay in LDS; the block lists the
+//         union of the pair's kept tokens in ascending order and runs the
+//         exact attention of both heads over it (section below), writing
+//         the pair's outputs.  Nothing else goes to global memory but idx.
+// MODE 2: MODE 1 with the exact stage taken by the query itself against
+//         unrotated keys (the asymmetric index: the scores used q A).
+// ============================================================================
+template <int KS, int U, int D, int MODE>
+__global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
+    const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P,
+    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int Scap, int Sp, int r,
+    int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap, const bf16_t* __restrict__ Kx,
+    const bf16_t* __restrict__ V, bf16_t* __restrict__ out, float scale_log2, const int32_t* __restrict__ lens) {
+  constexpr int NWV = kPairThreads / 64;
+  constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
+  constexpr int d = D;
+  extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
+  __shared__ __align__(16) uint32_t sel[2][kNB];
+  __shared__ __align__(16) uint32_t take[2][kFusedMaxS / 32];
+  __shared__ SelScratch<kPairThreads> sh[2];
+  __shared__ uint32_t smm[2][2];  // per head {min, max} key
+  __shared__ __align__(16) uint16_t sqs[2 * 4 * D];  // the pair's split rows [h][part][d]
+  __shared__ __align__(16) uint16_t sqp[MODE == 2 ? 2 * 4 * D : 8];  // the query itself, split
+  __shared__ int s_n;
+  const int G = Hq / Hkv, NP = G / 2;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int gp = slot % NP, gi = (slot / NP) * 8 + xcd;
+  if (gi >= B * Hkv) return;  // padding block (uniform)
+  const int b = gi / Hkv, kv = gi - b * Hkv;
+  const int S = seq_len(lens, b, Scap);  // this sequence's tokens
+  const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m = lane & 15, q4 = lane >> 4;
+  uint32_t* const brow2[2] = {MODE == 0 ? bitmap + row0 * W : take[0],
+                              MODE == 0 ? bitmap + (row0 + 1) * W : take[1]};
+
+  // Wave w takes tiles w + NWV i (16 tokens each) in batches of U, double
+  // buffered: the next batch is in flight while this one is multiplied.
+  // Loads are unconditional (token clamped to S - 1, dims to the row) so
+  // that each tile waits only for its own data; dims >= r are zeroed at the
+  // MFMA, tiles past S are dropped at the store.
+  const bf16_t* base = src + (size_t)gi * Scap * ld;  // rows of the cache (capacity Scap)
+  const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
+  auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q4, ld - 8));
+    }
+  };
+  // the pair's query rotation q_rot = q P[kv], with the arithmetic of
+  // qrot_kernel (d / 8-term FMA chains over eight j-slices, added in slice
+  // order): the split rows go to LDS as this block's A operands (MODE 0: q_rot
+  // and its split also to the workspace for the attention kernels).  The P
+  // column slice and q are requested first, together, then the first K batch.
+  const int J = d / 8, pc = tid % d, js = tid / d;
+  bf16_t pv[16];  // P[kv][js J + jj][pc], J <= 16
+  {
+    const bf16_t* Pc = P + (size_t)kv * d * d + pc;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) pv[jj] = Pc[(size_t)min(js * J + jj, d - 1) * d];  // clamped: always in bounds
+  }
+  float* sq = reinterpret_cast<float*>(lk);  // [2][d]
+  float* sred = sq + 2 * d;                  // [8][2][d]
+  if (tid < 2 * d) sq[tid] = to_f32(q[row0 * d + tid]);  // the pair's heads are adjacent rows
+  uint4 a0[U][KS], a1[U][KS];
+  load_batch(0, a0);  // in flight during the rotation (unused when every token is kept)
+  {
+    __syncthreads();
+    if (js < 8) {
+      float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        if (jj < J) {
+          const int j = js * J + jj;
+          const float pj = to_f32(pv[jj]);
+          r0 = fmaf(sq[j], pj, r0);
+          r1 = fmaf(sq[d + j], pj, r1);
+        }
+      }
+      const int c = pc;
+      sred[(2 * js) * d + c] = r0;
+      sred[(2 * js + 1) * d + c] = r1;
+    }
+    __syncthreads();
+    if (tid < 2 * d) {
+      const int h = tid / d, cc = tid - h * d;
+      float v = sred[h * d + cc];
+      for (int t = 1; t < 8; ++t) v += sred[(2 * t + h) * d + cc];
+      const bf16_t hi = f32_to_bf16(v);
+      const float e1 = v - to_f32(hi);
+      const bf16_t mid = f32_to_bf16(e1);
+      const bf16_t lo = f32_to_bf16(e1 - to_f32(mid));
+      const bf16_t part[4] = {hi, mid, lo, 0};
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) sqs[(h * 4 + pt) * d + cc] = part[pt];
+      if constexpr (MODE == 0) {
+        qrot[(row0 + h) * d + cc] = v;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) qsplit[((row0 + h) * 4 + pt) * d + cc] = part[pt];
+      }
+      if constexpr (MODE == 2) {
+        // the query itself: a bf16 value is its own first split part
+        sqp[(h * 4) * d + cc] = q[row0 * d + tid];
+#pragma unroll
+        for (int pt = 1; pt < 4; ++pt) sqp[(h * 4 + pt) * d + cc] = 0;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (k >= S) {
+    keep_all<kPairThreads>(S, k, W, idx + row0 * k, brow2[0]);
+    keep_all<kPairThreads>(S, k, W, idx + (row0 + 1) * k, brow2[1]);
+    if constexpr (MODE == 0) return;
+  } else {
+    // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
+    bf16x8_t qa[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qa[s] = q_rows(sqs, 0, d, 2, r, m, 32 * s + 8 * q4);
+
+    // the key range of each head, gathered while the keys are made (the
+    // selection then needs no pass of its own for it)
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint4 x = 32 * s + 8 * q4 < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
+        }
+        const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
+        if (q4 < 2 && t < S) {
+          const float sc = sum_split_rows(acc);
+          const uint32_t key = score_key(sc);
+          lk[q4 * Sp + t] = __float_as_uint(sc);  // the selection bins the value itself
+          kmn = min(kmn, key);
+          kmx = max(kmx, key);
+        }
+      }
+    };
+    // the selection's scratch is cleared now, under the score phase
+    for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
+    for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
+    if (tid < 2) {
+      smm[tid][0] = 0xffffffffu;
+      smm[tid][1] = 0u;
+      sh[tid].ccount = 0;
+    }
+    __syncthreads();  // orders the initialisation before the atomics below
+    for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
+      load_batch(bi + 1, a1);
+      score_batch(bi, a0);
+      load_batch(bi + 2, a0);
+      score_batch(bi + 1, a1);
+    }
+#pragma unroll
+    for (int x = 1; x < 16; x <<= 1) {  // over the 16 lanes of a head's row
+      kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
+      kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, x));
+    }
+    if (m == 0 && q4 < 2) {
+      atomicMin(&smm[q4][0], kmn);
+      atomicMax(&smm[q4][1], kmx);
+    }
+    __syncthreads();
+    uint32_t key[2][T];
+    load_regs<T>(lk, S, key[0]);
+    load_regs<T>(lk + Sp, S, key[1]);
+    uint32_t* const lds2[2] = {sel[0], sel[1]};
+    uint32_t* const take2[2] = {take[0], take[1]};
+    int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
+    SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
+    const uint32_t* const kmm2[2] = {smm[0], smm[1]};
+    select_regs2<kPairThreads, T>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
+  }
+  if constexpr (MODE != 0) {
+    // ========================================================================
+    // Exact attention of the pair's two heads over their kept tokens.
+    // The union of the two kept sets is listed in ascending token order
+    // (entry = token | kept-by-head-0 << 30 | kept-by-head-1 << 31) in the
+    // LDS that held the keys.  Wave w then takes 16-row tiles w + 16 i of
+    // the list in one pass, double buffered: for a tile, the K rows (MFMA B
+    // operand, 64 contiguous bytes of each of 16 rows per load instruction)
+    // and the V rows (16-byte granules, RL lanes per row) are requested
+    // together, one tile ahead of the one being used.  Per tile: the exact
+    // scores of both heads from MFMA (the heads' split rows in A rows 0..7:
+    // lane l holds head l / 16's score of row l % 16), scaled to log2 units,
+    // -inf where the head did not keep the token; an online softmax per head
+    // (running max and sum; the accumulators are rescaled when the max
+    // grows); each lane's V granules weighted by both heads' weights of
+    // their rows (read from the score lanes by lane permutes).  The 16
+    // waves' (max, sum, acc) of each head are merged by log-sum-exp.
+    // ========================================================================
+    __syncthreads();  // the bitmaps (take) are complete
+    uint32_t* list = lk;
+    {
+      uint32_t u0 = 0u, u1 = 0u;
+      if (tid < W) {
+        u0 = take[0][tid];
+        u1 = take[1][tid];
+      }
+      uint32_t u = u0 | u1;
+      const int c = __popc(u);
+      const int incl = block_incl_scan<kPairThreads>(c, sh[0]);
+      if (tid == kPairThreads - 1) s_n = incl;
+      int pos = incl - c;
+      while (u) {
+        const int j = __ffs(u) - 1;
+        u &= u - 1u;
+        list[pos++] = (uint32_t)(32 * tid + j) | (((u0 >> j) & 1u) << 30) | (((u1 >> j) & 1u) << 31);
+      }
+    }
+    __syncthreads();
+    const int n = s_n;  // >= 1: each head keeps min(k, S) >= 1 tokens
+    const int ntile = (n + 15) >> 4;
+    constexpr int KSD = D / 32;   // k-steps of the exact dot
+    constexpr int RL = D / 8;     // lanes per V row
+    constexpr int RPW = 64 / RL;  // V rows per wave pass
+    constexpr int VP = 16 / RPW;  // V passes per tile
+    constexpr uint32_t TOK = 0x3fffffffu;
+    // the A operands (both heads' split rows over all D dims) are read from
+    // LDS per tile rather than held in registers
+    const uint16_t* qx = MODE == 2 ? sqp : sqs;
+    const size_t cb = (size_t)gi * Scap * D;  // this group's rows of K and V
+    const int lg = lane / RL, li = lane % RL;
+    auto load_tile = [&](int t, uint4 (&kb)[KSD], uint4 (&vb)[VP]) {
+      const uint32_t tk = list[min(16 * t + m, n - 1)] & TOK;
+      const bf16_t* kr = Kx + cb + (size_t)tk * D + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < KSD; ++s) kb[s] = ldg16(kr + 32 * s);
+#pragma unroll
+      for (int u = 0; u < VP; ++u) {
+        const uint32_t tv = list[min(16 * t + RPW * u + lg, n - 1)] & TOK;
+        vb[u] = ldg16(V + cb + (size_t)tv * D + 8 * li);
+      }
+    };
+    float acc[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    float mr0 = -INFINITY, mr1 = -INFINITY;  // running maxima (the same in every lane)
+    float lp = 0.f;                          // this lane's share of its head's weight sum
+    auto proc_tile = [&](int t, const uint4 (&kb)[KSD], const uint4 (&vb)[VP]) {
+      floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSD; ++s)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_rows(qx, 0, D, 2, D, m, 32 * s + 8 * q4), as_bf16x8(kb[s]),
+                                                       sacc, 0, 0, 0);
+      const int p = 16 * t + m;
+      const uint32_t ent = list[min(p, n - 1)];
+      const bool kept = q4 < 2 && p < n && ((ent >> (30 + (q4 & 1))) & 1u);
+      const float e = kept ? sum_split_rows(sacc) * scale_log2 : -INFINITY;
+      const float tm = row16_max(e);
+      const float n0 = fmaxf(mr0, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tm), 0)));
+      const float n1 = fmaxf(mr1, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tm), 16)));
+      const float c0 = (n0 == -INFINITY) ? 1.f : exp2f(mr0 - n0);
+      const float c1 = (n1 == -INFINITY) ? 1.f : exp2f(mr1 - n1);
+      mr0 = n0;
+      mr1 = n1;
+      const float w = kept ? exp2f(e - (q4 == 0 ? n0 : n1)) : 0.f;
+      lp = fmaf(lp, q4 == 0 ? c0 : c1, w);
+      float wv[2][VP];
+#pragma unroll
+      for (int u = 0; u < VP; ++u) {
+        wv[0][u] = __shfl(w, RPW * u + lg);
+        wv[1][u] = __shfl(w, 16 + RPW * u + lg);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc[0][i] *= c0;
+        acc[1][i] *= c1;
+      }
+#pragma unroll
+      for (int u = 0; u < VP; ++u) {
+        float x[8];
+        Gran<bf16_t>::unpack(vb[u], x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[0][i] = fmaf(wv[0][u], x[i], acc[0][i]);
+          acc[1][i] = fmaf(wv[1][u], x[i], acc[1][i]);
+        }
+      }
+    };
+    {
+      uint4 ka[KSD], va[VP], kb2[KSD], vb2[VP];
+      load_tile(min(wave, ntile - 1), ka, va);
+      for (int t = wave; t < ntile; t += 2 * NWV) {  // unconditional loads: tiles past the end repeat the last
+        load_tile(min(t + NWV, ntile - 1), kb2, vb2);
+        proc_tile(t, ka, va);
+        if (t + NWV >= ntile) break;  // uniform across the wave
+        load_tile(min(t + 2 * NWV, ntile - 1), ka, va);
+        proc_tile(t + NWV, kb2, vb2);
+      }
+    }
+    // per head: the weight sum over its 16 score lanes; per dim: the sum of
+    // the accumulators over the lanes holding other rows of the same dims
+    lp = group_sum<16>(lp);
+    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), 0));
+    const float l1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), 16));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = acc[h][i];
+        // lane ^ 8 and lane ^ 16 by ds_swizzle (bit-mask mode, no address), lane ^ 32 by bpermute
+        if constexpr (RL <= 8) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+        v += __shfl_xor(v, 32);
+        acc[h][i] = v;
+      }
+    // merge the 16 waves by log-sum-exp (the selection's LDS is free now)
+    float* s_acc = reinterpret_cast<float*>(&sel[0][0]);  // [NWV][2][D]
+    float* s_ml = reinterpret_cast<float*>(&take[0][0]);  // [NWV][2][2] (max, sum)
+    static_assert(NWV * 2 * D <= 2 * kNB, "merge buffer fits the selection's LDS");
+    // (take and sel were last read before the barrier that follows the list)
+    if (lg == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_acc[(wave * 2 + h) * D + li * 8 + i] = acc[h][i];
+    }
+    if (lane == 0) {
+      s_ml[wave * 4 + 0] = mr0;
+      s_ml[wave * 4 + 1] = l0;
+      s_ml[wave * 4 + 2] = mr1;
+      s_ml[wave * 4 + 3] = l1;
+    }
+    __syncthreads();
+    if (tid < 2 * D) {
+      const int h = tid / D, c = tid - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_ml[w * 4 + 2 * h]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        const float mw = s_ml[w * 4 + 2 * h];
+        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        L = fmaf(s_ml[w * 4 + 2 * h + 1], f, L);
+        A = fmaf(s_acc[(w * 2 + h) * D + c], f, A);
+      }
+      out[(row0 + h) * D + c] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+    }
+  }
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+bool score_select_pair_fits(const DecodePlan& p) {
+  return p.dt == 1 && p.G >= 2 && p.G % 2 == 0 && p.S <= kFusedMaxS && p.r <= 128 && (p.d == 64 || p.d == 128);
+}
+
+template <int MODE>
+static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                              float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap, const void* Kx,
+                              const void* V, void* out, hipStream_t st) {
+  if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
+  // keys [2][Sp] (then the union list, <= Sp entries), at least the rotation scratch [2 + 16][d] words
+  const size_t lds = (size_t)max(2 * p.Sp, 18 * p.d) * sizeof(uint32_t);
+  const int ngroups = p.B * p.Hkv;
+  const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d));
+  const bf16_t* s = static_cast<const bf16_t*>(src);
+  auto go = [&](auto ks, auto dd) {
+    constexpr int K = decltype(ks)::value, D = decltype(dd)::value;
+    const void* fn = reinterpret_cast<const void*>(&score_select_pair_kernel<K, 8 / K, D, MODE>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K, D, MODE>), grid, block, lds, st, s, ld,
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B, p.Hq,
+                       p.Hkv, p.S, p.Sp, p.r, p.k, p.W, idx, bitmap, static_cast<const bf16_t*>(Kx),
+                       static_cast<const bf16_t*>(V), static_cast<bf16_t*>(out), scale_log2, p.lens);
+    return hipGetLastError();
+  };
+  auto by_d = [&](auto ks) {
+    return p.d == 64 ? go(ks, std::integral_constant<int, 64>{}) : go(ks, std::integral_constant<int, 128>{});
+  };
+  switch ((p.r + 31) / 32) {
+    case 1: return by_d(std::integral_constant<int, 1>{});
+    case 2: return by_d(std::integral_constant<int, 2>{});
+    case 3: return by_d(std::integral_constant<int, 3>{});
+    case 4: return by_d(std::integral_constant<int, 4>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
+                                    hipStream_t st) {
+  return launch_pair<0>(p, src, ld, q, P, qrot, qsplit, idx, bitmap, nullptr, nullptr, nullptr, st);
+}
+
+hipError_t launch_decode_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
+                              const void* Kx, const void* V, void* out, int32_t* idx, bool plain, hipStream_t st) {
+  return plain ? launch_pair<2>(p, src, ld, q, P, nullptr, nullptr, idx, nullptr, Kx, V, out, st)
+               : launch_pair<1>(p, src, ld, q, P, nullptr, nullptr, idx, nullptr, Kx, V, out, st);
+}
+
+}  // namespace loki

@@ -699,17 +699,18 @@ def test_decode_all_equal_keys_pair(gpu_lib):
 
 
 def test_pair_fused_matches_two_kernel_path(gpu_lib):
-    # grouped heads: 512 query heads (one fused block per pair of heads) against
-    # the first 256 of them (scores and selection in two kernels)
+    # grouped heads: 512 query heads (the whole step of each pair of heads in
+    # one kernel) against the first 256 of them (rotation, scores, selection
+    # and attention kernels).  The score arithmetic is the same, so the kept
+    # sets are bit-identical; the attention sums in another order, so each
+    # output is checked against the oracle
     cfg = cfg_case("C3", S=4096, B=16)
     x = make_inputs(cfg)
-    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
-    Kl = Kr[..., :cfg.r].contiguous()
-    o_all, i_all = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k, K_lead=Kl)
-    o_half, i_half = gpu_lib.loki_decode(q[:8].contiguous(), P, Kr[:8].contiguous(), V[:8].contiguous(),
-                                         r=cfg.r, k=cfg.k, K_lead=Kl[:8].contiguous())
+    o_all, i_all, _ = run_decode(gpu_lib, x, cfg.r, cfg.k, R=cfg.r)
+    half = {n: x[n][:8].contiguous() for n in ("q", "K_rot", "V")}
+    half["P"] = x["P"]
+    o_half, i_half, _ = run_decode(gpu_lib, half, cfg.r, cfg.k, R=cfg.r)
     assert torch.equal(i_all[:8], i_half)
-    assert torch.equal(o_all[:8].view(torch.int16), o_half.view(torch.int16))
 
 
 def test_decode_deterministic(gpu_lib):
