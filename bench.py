@@ -280,6 +280,7 @@ def run(args) -> dict:
     t0 = time.perf_counter()
     for i in range(args.steps):
         headline(i)
+    t_enq = time.perf_counter() - t0  # host time to enqueue the steps (diagnostic)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
@@ -377,6 +378,7 @@ def run(args) -> dict:
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
         "frac_of_read_ceiling_step": round(step_gbs / READ_CEILING_GBS, 4),
         "step_us_plain": {k_: round(v_, 2) for k_, v_ in pct_plain.items()},
+        "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "step_us_events": {k_: round(v_, 2) for k_, v_ in pct.items()},
         "recall_at_k_vs_exact_topk": round(recall, 4),
         "alg_bytes_per_step": by_step,

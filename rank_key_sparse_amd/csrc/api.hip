@@ -2,12 +2,41 @@
 // workspace carving, and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/loki.h"
 #include "internal.h"
 
 using namespace loki;
+
+namespace loki {
+
+hipError_t ensure_dynamic_lds(const void* fn, int bytes) {
+  struct Entry {
+    const void* fn;
+    int dev, bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (Entry& x : done)
+    if (x.fn == fn && x.dev == dev) {
+      if (x.bytes >= bytes) return hipSuccess;
+      if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) == hipSuccess)
+        x.bytes = bytes;
+      return e;
+    }
+  if ((e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) == hipSuccess)
+    done.push_back(Entry{fn, dev, bytes});
+  return e;
+}
+
+}  // namespace loki
 
 namespace {
 

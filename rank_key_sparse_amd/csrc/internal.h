@@ -18,6 +18,11 @@ constexpr int kSelChunk = 16384;        // long heads: tokens per first-stage se
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device, calling the runtime only the first time a (kernel, device) pair
+// needs a larger limit (a decode then makes no attribute call per launch).
+hipError_t ensure_dynamic_lds(const void* fn, int bytes);
+
 // Everything a decode-family launch needs, derived from the sizes alone.
 struct DecodePlan {
   int B, Hq, Hkv, S, d, r, k, G, dt;  // dt: 0 fp32, 1 bf16

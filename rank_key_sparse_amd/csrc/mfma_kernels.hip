@@ -665,8 +665,7 @@ hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, con
   hipError_t e = hipSuccess;
 #define LOKI_SS(K)                                                                                     \
   case K:                                                                                              \
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_kernel<K>),                    \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                     \
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&score_select_kernel<K>), (int)lds);        \
     if (e != hipSuccess) return e;                                                                     \
     hipLaunchKernelGGL((score_select_kernel<K>), grid, block, lds, st, s, ld, qsplit, p.B, p.Hq, p.Hkv, \
                        p.S, p.Sp, p.d, p.r, p.k, p.W, idx, bitmap, p.lens);                            \
@@ -700,8 +699,7 @@ hipError_t launch_score_select_chunk(const DecodePlan& p, const void* src, int l
   hipError_t e = hipSuccess;
 #define LOKI_SC(K)                                                                                       \
   case K:                                                                                                \
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_select_chunk_kernel<K>),                \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                       \
+    e = ensure_dynamic_lds(reinterpret_cast<const void*>(&score_select_chunk_kernel<K>), (int)lds);    \
     if (e != hipSuccess) return e;                                                                       \
     hipLaunchKernelGGL((score_select_chunk_kernel<K>), grid, block, lds, st, s, ld, qsplit, p.B, p.Hq,   \
                        p.Hkv, p.S, C, p.d, p.r, p.k, ldc, cidx, ckey, p.lens);                           \

@@ -214,14 +214,17 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
     SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
     const uint32_t* const kmm2[2] = {smm[0], smm[1]};
-    select_regs2<kPairThreads, T>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
+    // the fused form writes idx itself while listing the kept tokens
+    select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
   }
   if constexpr (MODE != 0) {
     // ========================================================================
     // Exact attention of the pair's two heads over their kept tokens.
     // The union of the two kept sets is listed in ascending token order
     // (entry = token | kept-by-head-0 << 30 | kept-by-head-1 << 31) in the
-    // LDS that held the keys.  Wave w then takes 16-row tiles w + 16 i of
+    // LDS that held the keys; thread w lists bitmap word w, at offsets from
+    // block scans of the union's and of each head's counts, and writes each
+    // head's kept tokens to its idx row (ascending) at the same time.  Wave w then takes 16-row tiles w + 16 i of
     // the list in one pass, double buffered: for a tile, the K rows (MFMA B
     // operand, 64 contiguous bytes of each of 16 rows per load instruction)
     // and the V rows (16-byte granules, RL lanes per row) are requested
@@ -243,14 +246,22 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
         u1 = take[1][tid];
       }
       uint32_t u = u0 | u1;
-      const int c = __popc(u);
+      const int c = __popc(u), c0 = __popc(u0), c1 = __popc(u1);
       const int incl = block_incl_scan<kPairThreads>(c, sh[0]);
+      // both heads' counts in one scan, 16 bits each (a head keeps <= 16384)
+      const int incl01 = block_incl_scan<kPairThreads>(c0 | (c1 << 16), sh[1]);
       if (tid == kPairThreads - 1) s_n = incl;
-      int pos = incl - c;
+      int pos = incl - c, p0 = (incl01 & 0xffff) - c0, p1 = (incl01 >> 16) - c1;
+      int32_t* const o0 = idx + row0 * k;
+      int32_t* const o1 = idx + (row0 + 1) * k;
+      const bool wr = k < S;  // else keep_all wrote idx (with the -1 padding)
       while (u) {
         const int j = __ffs(u) - 1;
         u &= u - 1u;
-        list[pos++] = (uint32_t)(32 * tid + j) | (((u0 >> j) & 1u) << 30) | (((u1 >> j) & 1u) << 31);
+        const uint32_t t = (uint32_t)(32 * tid + j), b0 = (u0 >> j) & 1u, b1 = (u1 >> j) & 1u;
+        list[pos++] = t | (b0 << 30) | (b1 << 31);
+        if (wr && b0) o0[p0++] = (int32_t)t;
+        if (wr && b1) o1[p1++] = (int32_t)t;
       }
     }
     __syncthreads();
@@ -409,7 +420,8 @@ static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, cons
   auto go = [&](auto ks, auto dd) {
     constexpr int K = decltype(ks)::value, D = decltype(dd)::value;
     const void* fn = reinterpret_cast<const void*>(&score_select_pair_kernel<K, 8 / K, D, MODE>);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    // the limit covers every call of this kernel: keys of the longest head it takes
+    hipError_t e = ensure_dynamic_lds(fn, (int)max(lds, (size_t)2 * kFusedMaxS * sizeof(uint32_t)));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K, D, MODE>), grid, block, lds, st, s, ld,
                        static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B, p.Hq,

@@ -161,11 +161,12 @@ __device__ __forceinline__ int opaque(int x) {
 // of dependent LDS round trips.
 template <int NTHR, typename F>
 __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32_t* ci, int nc, int need,
-                                                F&& set) {
+                                                F&& set, int t0 = 0) {
   auto beats = [](uint32_t vc, uint32_t ic, uint32_t vi, uint32_t ii) {
     return (int)((vc > vi) || (vc == vi && ic < ii));
   };
-  for (int i = threadIdx.x; i < nc; i += NTHR) {
+  // threads t0 .. t0 + NTHR - 1 take part (NTHR may be a part of the block)
+  for (int i = (int)threadIdx.x - t0; i >= 0 && i < nc; i += NTHR) {
     const uint32_t vi = ck[i], ii = ci[i];
     int rank = 0;
     const int n4 = nc & ~3;
@@ -372,9 +373,11 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 // S < 65536.  The caller zeroes hist[h] (kNB words) and take[h] (W words),
 // sets sh[h].ccount = 0 and provides kmm[h] = {min, max} of head h's keys,
 // all ordered before the call by a barrier.  lds[h] / take[h] / sh[h] are
-// separate per head.  Output per head as for select_regs (no map / okeys).
+// separate per head.  Output per head as for select_regs (no map / okeys);
+// without EMIT only the kept-token bitmaps brow[h] are written (a caller
+// that lists the kept tokens itself) and orow is not used.
 // ============================================================================
-template <int NTHR, int T>
+template <int NTHR, int T, bool EMIT = true>
 __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint32_t* const (&lds)[2],
                                              uint32_t* const (&take)[2], int S, int k, int W,
                                              int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
@@ -455,14 +458,16 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
   }
   __syncthreads();
 
-  // 3. the need best tokens of each threshold bin
+  // 3. the need best tokens of each threshold bin (head h ranked by the
+  // threads of half h of the block: nc <= kRankMax <= NTHR / 2)
+  static_assert(kRankMax <= NTHR / 2, "one thread per candidate");
   if (rank_path[0] || rank_path[1]) {  // uniform
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       if (rank_path[h]) {
         uint32_t* tk = take[h];
-        rank_candidates<NTHR>(lds[h], lds[h] + kCap, nc[h], need[h],
-                              [&](uint32_t ii) { atomicOr(&tk[ii >> 5], 1u << (ii & 31)); });
+        rank_candidates<NTHR / 2>(lds[h], lds[h] + kCap, nc[h], need[h],
+                                  [&](uint32_t ii) { atomicOr(&tk[ii >> 5], 1u << (ii & 31)); }, h * (NTHR / 2));
       }
     __syncthreads();
     const int st = wave * T + lane;
@@ -519,6 +524,13 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
   }
 
   // 4. emit both heads: one scan of (count0 | count1 << 16)
+  if constexpr (!EMIT) {
+    const int st = wave * T + lane;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow[h] + 2 * st) = make_uint2(klo[h], khi[h]);
+    return;
+  }
   const int cnt = (lane < T) ? ((__popc(klo[0]) + __popc(khi[0])) | ((__popc(klo[1]) + __popc(khi[1])) << 16)) : 0;
   const int incl = wave_incl_scan(cnt);
   if (lane == 63) sh[0]->wsel[wave] = incl;
