@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma_common.h"
@@ -159,10 +161,14 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) qa[s] = q_rows(sqs, 0, d, 2, r, m, 32 * s + 8 * q4);
 
-    // the key range of each head, gathered while the keys are made (the
-    // selection then needs no pass of its own for it)
+    // Both heads' histograms are built while the keys are made, over value
+    // bins fixed by the range of the first batch's keys (later keys outside
+    // it fall into the end bins; the map stays monotone, so the selection is
+    // exact whatever the range, which only sets how many keys share the
+    // threshold bin): the selection then needs no histogram pass of its own.
     uint32_t kmn = 0xffffffffu, kmx = 0u;
-    auto score_batch = [&](int bi, const uint4 (&a)[U][KS]) {
+    Binner bq;  // this lane's head's bins (set after the first batch)
+    auto score_batch = [&](int bi, const uint4 (&a)[U][KS], auto binning) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -174,14 +180,18 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
         const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
         if (q4 < 2 && t < S) {
           const float sc = sum_split_rows(acc);
-          const uint32_t key = score_key(sc);
           lk[q4 * Sp + t] = __float_as_uint(sc);  // the selection bins the value itself
-          kmn = min(kmn, key);
-          kmx = max(kmx, key);
+          if constexpr (decltype(binning)::value) {
+            atomicAdd(&sel[q4][bq.of_score(sc)], 1u);
+          } else {
+            const uint32_t key = score_key(sc);
+            kmn = min(kmn, key);
+            kmx = max(kmx, key);
+          }
         }
       }
     };
-    // the selection's scratch is cleared now, under the score phase
+    // the histograms are cleared now, under the loads in flight
     for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
     for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
     if (tid < 2) {
@@ -190,12 +200,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       sh[tid].ccount = 0;
     }
     __syncthreads();  // orders the initialisation before the atomics below
-    for (int bi = 0; bi < nbat; bi += 2) {  // an odd last batch is followed by an empty one
-      load_batch(bi + 1, a1);
-      score_batch(bi, a0);
-      load_batch(bi + 2, a0);
-      score_batch(bi + 1, a1);
-    }
+    // the first batch: its keys' range per head fixes the bins
+    load_batch(1, a1);
+    score_batch(0, a0, std::false_type{});
 #pragma unroll
     for (int x = 1; x < 16; x <<= 1) {  // over the 16 lanes of a head's row
       kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
@@ -206,6 +213,20 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       atomicMax(&smm[q4][1], kmx);
     }
     __syncthreads();
+    bq.init(smm[q4 & 1][0], smm[q4 & 1][1]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // the first batch's keys, read back
+      const int t = 16 * (wave + NWV * u) + m;
+      if (q4 < 2 && t < S) atomicAdd(&sel[q4][bq.of_score(__uint_as_float(lk[q4 * Sp + t]))], 1u);
+    }
+    load_batch(2, a0);
+    for (int bi = 1; bi < nbat; bi += 2) {  // batches past the end score no token
+      score_batch(bi, a1, std::true_type{});
+      load_batch(bi + 2, a1);
+      score_batch(bi + 1, a0, std::true_type{});
+      load_batch(bi + 3, a0);
+    }
+    __syncthreads();  // every key and histogram count is in LDS
     uint32_t key[2][T];
     load_regs<T>(lk, S, key[0]);
     load_regs<T>(lk + Sp, S, key[1]);
@@ -215,7 +236,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
     const uint32_t* const kmm2[2] = {smm[0], smm[1]};
     // the fused form writes idx itself while listing the kept tokens
-    select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2);
+    select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2, true);
   }
   if constexpr (MODE != 0) {
     // ========================================================================
@@ -247,9 +268,10 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       }
       uint32_t u = u0 | u1;
       const int c = __popc(u), c0 = __popc(u0), c1 = __popc(u1);
-      const int incl = block_incl_scan<kPairThreads>(c, sh[0]);
-      // both heads' counts in one scan, 16 bits each (a head keeps <= 16384)
-      const int incl01 = block_incl_scan<kPairThreads>(c0 | (c1 << 16), sh[1]);
+      // the union's counts, and both heads' in 16 bits each (a head keeps
+      // <= 16384), scanned together
+      int incl = c, incl01 = c0 | (c1 << 16);
+      block_incl_scan2<kPairThreads>(incl, incl01, sh[0], sh[1]);
       if (tid == kPairThreads - 1) s_n = incl;
       int pos = incl - c, p0 = (incl01 & 0xffff) - c0, p1 = (incl01 >> 16) - c1;
       int32_t* const o0 = idx + row0 * k;

@@ -78,6 +78,21 @@ __device__ __forceinline__ int block_incl_scan(int v, SelScratch<NTHR>& sh) {
   return v + waves_below<NTHR>(sh.scan);
 }
 
+// Two inclusive prefix sums over the block at once, one barrier (each one's
+// per-wave totals in its own scratch).
+template <int NTHR>
+__device__ __forceinline__ void block_incl_scan2(int& a, int& b, SelScratch<NTHR>& sa, SelScratch<NTHR>& sb) {
+  a = wave_incl_scan(a);
+  b = wave_incl_scan(b);
+  if ((threadIdx.x & 63) == 63) {
+    sa.scan[threadIdx.x >> 6] = a;
+    sb.scan[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  a += waves_below<NTHR>(sa.scan);
+  b += waves_below<NTHR>(sb.scan);
+}
+
 // Find, scanning bins from the top, the bin holding the `want`-th largest key
 // (1-based).  Sets sh.t to that bin, sh.above to the count in higher bins and
 // sh.nt to the count in bin t (so that callers need not read hist again).
@@ -372,7 +387,11 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 // one block scan with the two counts packed in 16-bit halves, which needs
 // S < 65536.  The caller zeroes hist[h] (kNB words) and take[h] (W words),
 // sets sh[h].ccount = 0 and provides kmm[h] = {min, max} of head h's keys,
-// all ordered before the call by a barrier.  lds[h] / take[h] / sh[h] are
+// all ordered before the call by a barrier.  With prebuilt, lds[h] already
+// holds head h's histogram over bins of the range kmm[h] (the caller's own
+// range, e.g. of the first keys made; keys outside it fall into the end
+// bins, which keeps the map monotone, so the selection stays exact: only the
+// threshold bin's size depends on the range).  lds[h] / take[h] / sh[h] are
 // separate per head.  Output per head as for select_regs (no map / okeys);
 // without EMIT only the kept-token bitmaps brow[h] are written (a caller
 // that lists the kept tokens itself) and orow is not used.
@@ -382,14 +401,15 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
                                              uint32_t* const (&take)[2], int S, int k, int W,
                                              int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
                                              SelScratch<NTHR>* const (&sh)[2],
-                                             const uint32_t* const (&kmm)[2]) {
+                                             const uint32_t* const (&kmm)[2], bool prebuilt = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Binner bin[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) bin[h].init(kmm[h][0], kmm[h][1]);
   auto key = [&](int h, int i) { return score_key(__uint_as_float(sbits[h][i])); };
 
-  // 1. both histograms; each score's bin stays in a register for step 2
+  // 1. both histograms (unless prebuilt); each score's bin stays in a
+  // register for step 2
   int kb[2][T];
   int nv = opaque(regs_valid<T>(S));
 #pragma unroll
@@ -398,9 +418,9 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
     for (int i = 0; i < T; ++i)
       if (i < nv) {
         kb[h][i] = bin[h].of_score(__uint_as_float(sbits[h][i]));
-        atomicAdd(&lds[h][kb[h][i]], 1u);
+        if (!prebuilt) atomicAdd(&lds[h][kb[h][i]], 1u);
       }
-  __syncthreads();
+  if (!prebuilt) __syncthreads();  // uniform
 
   // threshold bins: one scan of (count0 | count1 << 16) from the top bin
   {
