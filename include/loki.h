@@ -370,9 +370,9 @@ loki_status loki_calibrate_pca_profiled(const void* K, void* P, double* eigvals,
 /*
  * Calibration of the asymmetric scoring index taken by loki_decode_asym
  * (page "SAKI: Score-Aware Low-Rank Key Indexing with Random-Matrix Noise
- * Correction for KV Retrieval", abstract: the optimal rank-r factors of the
- * covariance-weighted score distortion come from the SVD of the
- * covariance-weighted query-key operator).  Per key/value head kv, with
+ * Correction for KV Retrieval", abstract: the rank-r query-side and
+ * key-side factors that minimise the score error weighted by the query and
+ * key second moments come from one SVD, written out below).  Per key/value head kv, with
  *   Cq = mean of q^T q over the query samples of the heads of kv's group,
  *   Ck = mean of k^T k over the key rows of all batch elements of kv,
  *   W  = Cq^{1/2} Ck^{1/2} = U S V^T,

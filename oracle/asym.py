@@ -5,11 +5,10 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 What is computed, and where the pages say so:
 
 * SAKI (page "SAKI: Score-Aware Low-Rank Key Indexing with Random-Matrix
-  Noise Correction for KV Retrieval", abstract): the expected
-  distortion of the attention scores under a rank-r key index is a
-  covariance-weighted low-rank objective, and its optimum is an asymmetric
-  factorisation read off the SVD of the covariance-weighted query-key
-  operator.  Written out: approximate scores are ``(q A_r) . (k B_r)``; with
+  Noise Correction for KV Retrieval", abstract): the mean squared error
+  of the scores under a rank-r key index, weighted by the query and key
+  second moments, is minimised by two different (query-side, key-side)
+  rank-r factors, both taken from one SVD: that of ``Cq^1/2 Ck^1/2``.  Written out: approximate scores are ``(q A_r) . (k B_r)``; with
   query and key second moments ``Cq = E[q^T q]``, ``Ck = E[k^T k]`` and
   independent q, k, the mean squared score error of ``M = A_r B_r^T`` is
   ``|| Cq^{1/2} (I - M) Ck^{1/2} ||_F^2``; by the Eckart-Young theorem the

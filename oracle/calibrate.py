@@ -4,12 +4,12 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 What is computed, and where the pages say so:
 
-* The basis is the set of principal directions of the keys: for a key matrix
-  ``A`` (one row per sampled key, ``d_head`` columns) with singular value
-  decomposition ``A = U Sigma V^T``, the columns of ``V`` are the principal
-  components, and projecting the rows of ``A`` on the first few of them keeps
-  the most energy (AQUA page, appendix on the SVD; the same appendix notes that
-  ``V`` can equally be found from the eigenvectors of ``A^T A``).  Loki uses an
+* The basis is the set of principal directions of the keys: write the sampled
+  keys as a matrix ``A`` (a row per key, ``d_head`` columns) and take its SVD
+  ``A = U Sigma V^T``; the right singular vectors (columns of ``V``) are the
+  key matrix's principal directions, and keeping the leading ones keeps the
+  largest share of the rows' energy (AQUA page, appendix on the SVD, which
+  also relates ``V`` to the eigenvectors of ``A^T A``).  Loki uses an
   offline-computed matrix of this kind and keeps the leading dimensions (AQUA
   page, related work "LoKi Attention"); AQUA calibrates it once on another
   dataset (AQUA page, information-retention paragraph and Figure 2).

@@ -1,6 +1,6 @@
 """Pins of the oracle's asymmetric scoring index (SAKI page, abstract: the
-optimum of the covariance-weighted score distortion is an asymmetric
-factorisation from the SVD of the weighted query-key operator) against facts
+score error weighted by the query and key second moments is minimised by
+different query-side and key-side rank-r factors from one SVD) against facts
 that do not come from it:
 
 * Eckart-Young: the distortion of the factors equals the sum of the squared
