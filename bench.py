@@ -21,7 +21,11 @@ Measurement:
   sample of the same workload (whole batch elements) on the host, and also
   confirms the GPU output on that sample.
 
-Also: ``--calibrate-copy`` runs a 1 GiB elementwise copy (torch.neg; for
+The line also reports the memory-system reference of this GPU, measured
+live with the library's own kernels: a plain streaming read of 2 GiB (the
+practical read ceiling next to the nominal peak) and a plain copy.
+
+Also: ``--calibrate-copy`` runs the library's copy kernel over 1 GiB (for
 rocprofv3 counter scaling), ``--summarize-trace DB`` and ``--summarize-pmc FETCH_DB WRITE_DB``
 turn rocprofv3 result databases into the summaries kept under profiles/.
 """
@@ -40,9 +44,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# plain streaming read measured on this part (a read-only micro-benchmark):
-# the practical ceiling next to the nominal peak
-READ_CEILING_GBS = 6390.0
 PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ["qrot", "scores", "select", "attend", "merge"]
 
@@ -95,8 +96,8 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 30) -> di
     kib = copy_bytes / 1024.0
 
     def copy_entry(d):
-        # the calibration copy: torch.neg over 1 GiB (one read, one write)
-        cands = [(v, k) for k, v in d.items() if "neg" in k[0]]
+        # the calibration copy: the library's copy kernel over 1 GiB (one read, one write)
+        cands = [(v, k) for k, v in d.items() if "bench_copy_kernel" in k[0]]
         return max(cands)[1] if cands else None
 
     cf, cw = copy_entry(fetch), copy_entry(write)
@@ -104,7 +105,7 @@ def summarize_pmc(fetch_db: str, write_db: str, copy_bytes: int = 1 << 30) -> di
     w_scale = kib / write[cw] if cw else None
     kernels = {}
     for (name, gs), v in fetch.items():
-        if "loki" not in name:
+        if "loki" not in name or "bench_" in name:
             continue
         w = write.get((name, gs))
         kernels[f"{name}|grid={gs}"] = {
@@ -134,6 +135,37 @@ def load_traffic(workload: str, kernel_name: str):
 
 
 # ----------------------------------------------------------------------------- benchmark
+
+
+def memory_reference(read_bytes: int = 2 << 30, copy_bytes: int = 1 << 30, reps: int = 5) -> dict:
+    """Rates of the library's own reference kernels on this GPU: a plain
+    streaming read of `read_bytes` (larger than the 256 MB Infinity Cache, so
+    it streams from HBM) and a plain copy of `copy_bytes` (read + write
+    counted), median of `reps` timed runs each (HIP events)."""
+    import numpy as np
+    import torch
+
+    import rank_key_sparse_amd as rks
+    src = torch.empty(read_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dst = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+
+    def timed(fn, n):
+        out = []
+        for _ in range(n + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out.append(1e-3 * e0.elapsed_time(e1))
+        return float(np.median(out[1:]))  # the first run warms up
+
+    t_read = timed(lambda: rks.loki_bench_read(src, sink), reps)
+    t_copy = timed(lambda: rks.loki_bench_copy(src[:copy_bytes], dst), reps)
+    del src, dst
+    return {"read_gbs": round(read_bytes / t_read / 1e9, 1), "copy_gbs": round(2 * copy_bytes / t_copy / 1e9, 1),
+            "read_bytes": read_bytes, "copy_bytes": copy_bytes}
 
 
 def union_rows(idx, G: int) -> int:
@@ -353,6 +385,7 @@ def run(args) -> dict:
                 "kernel": dom_kernel, "alg_bytes_per_launch": per_kernel_bytes[dom],
                 "avg_launch_us": round(stage_us[dom], 2)}
     step_gbs = by_step / (ms_per_step * 1e-3) / 1e9
+    mem = memory_reference()
 
     res = {
         "metric": "decode attention steps/s (all heads) and achieved HBM GB/s vs ~8 TB/s peak",
@@ -376,7 +409,8 @@ def run(args) -> dict:
                    f"ragged {lens_h[0]}..{lens_h[-1]} (mean {sum(lens_h) / len(lens_h):.0f})"},
         "hbm_gbs_step": round(step_gbs, 1),
         "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
-        "frac_of_read_ceiling_step": round(step_gbs / READ_CEILING_GBS, 4),
+        "frac_of_read_ceiling_step": round(step_gbs / mem["read_gbs"], 4),
+        "memory_reference": mem,
         "step_us_plain": {k_: round(v_, 2) for k_, v_ in pct_plain.items()},
         "host_enqueue_us_per_step": round(1e6 * t_enq / args.steps, 2),
         "step_us_events": {k_: round(v_, 2) for k_, v_ in pct.items()},
@@ -457,6 +491,18 @@ def run_project(args) -> dict:
             oracle.project(x["K"][n % cfg.B:n % cfg.B + 1, :1], x["P"][:1])
             n += 1
         per_slice = (time.perf_counter() - t) / n
+    # the reference copy of the same bytes (K in, K_rot out) with the library's own copy kernel
+    K0, Kr0, _ = bufs[0]
+    nb = K0.numel() * K0.element_size()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for i in range(args.steps):
+        rks.loki_bench_copy(bufs[i % len(bufs)][0], bufs[i % len(bufs)][1])
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb / (1e-3 * c0.elapsed_time(c1) / args.steps) / 1e9
+    step(0)
+    torch.cuda.synchronize()
     got = bufs[0][1][:1, :1].double().cpu().numpy()
     want = oracle.project(x["K"][:1, :1], x["P"][:1])
     ok = bool(np.max(np.abs(got - want)) <= 2e-2)
@@ -472,6 +518,8 @@ def run_project(args) -> dict:
                      "alg_bytes_per_launch": by, "avg_launch_us": round(us, 2)},
         "mfma": {"tflops": round(tflops, 2), "peak_tflops": 2500.0, "util": round(tflops / 2500.0, 4),
                  "flop_per_launch": flop},
+        "copy_reference": {"gbs": round(copy_gbs, 1), "bytes_moved": 2 * nb,
+                           "frac_of_copy": round(gbs / copy_gbs, 4)},
         "cpu_baseline": {"value": round(1.0 / (per_slice * cfg.B * cfg.Hkv), 4), "unit": "projections/s",
                          "cores": 1, "kind": "oracle",
                          "sample": f"{n} (b, kv) slices of {cfg.S}x{cfg.d} in float64, scaled to the cache",
@@ -974,10 +1022,12 @@ def main() -> int:
         return 2
     if args.calibrate_copy:
         import torch
+
+        import rank_key_sparse_amd as rks
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            torch.neg(src, out=dst)  # a plain elementwise kernel: 1 GiB read, 1 GiB written
+            rks.loki_bench_copy(src, dst)  # the library's copy kernel: 1 GiB read, 1 GiB written
         torch.cuda.synchronize()
     res = {"project": run_project, "append": run_append, "calibrate": run_calibrate, "aqua": run_aqua, "asym": run_asym}.get(args.op, run)(args)
     print(json.dumps(res))

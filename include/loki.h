@@ -24,6 +24,8 @@
  *   loki_scores, loki_select_topk, loki_attend
  *                                    the decode stages alone
  *   *_profiled                       the same work with stage events
+ *   loki_bench_copy, loki_bench_read memory-system reference kernels
+ *                                    (measurement; not part of the method)
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -395,6 +397,23 @@ size_t loki_calibrate_asym_workspace_bytes(int32_t N, int32_t Hq, int32_t B, int
 loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, void* Bm, int32_t N,
                                 int32_t Hq, int32_t B, int32_t Hkv, int32_t S, int32_t d, int32_t r,
                                 loki_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Memory-system reference kernels (measurement only; no step of the
+ * method).  They are the reference points of the decode's HBM figures: the
+ * rate a pure stream reaches on this part, and a kernel of known bytes that
+ * scales the hardware traffic counters.
+ *   loki_bench_copy: dst[0..bytes) = src[0..bytes)  (one read, one write of
+ *                    every byte; the ranges must not overlap)
+ *   loki_bench_read: reads src[0..bytes) once and XORs every 32-bit word of it
+ *                    into *sink (a DEVICE uint32 the caller initialises; the
+ *                    XOR keeps every load live)
+ * bytes must be a multiple of 16 (LOKI_ERR_SHAPE), src / dst 16-byte aligned
+ * (LOKI_ERR_ALIGN), sink 4-byte aligned, pointers non-NULL when bytes > 0
+ * (LOKI_ERR_NULL).  Asynchronous on `stream`; no workspace.
+ */
+loki_status loki_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+loki_status loki_bench_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,9 @@ mirror the C ABI (``include/loki.h``) name for name:
 * :func:`loki_append_kv` -- one decode step's new key (rotated) and value written into the caches;
 * :func:`loki_decode` -- one Loki decode step -> ``(out, idx)``;
 * :func:`loki_scores`, :func:`loki_select_topk`, :func:`loki_attend` -- the
-  decode stages alone (same kernels), for stage-level checks.
+  decode stages alone (same kernels), for stage-level checks;
+* :func:`loki_bench_copy`, :func:`loki_bench_read` -- memory-system reference
+  kernels (measurement only).
 
 If the built library is missing the calls raise; there is no fallback.
 """
@@ -79,6 +81,8 @@ _SIGS = {
     "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
+    "loki_bench_copy": ([_P, _P, _Z, _P], ctypes.c_int),
+    "loki_bench_read": ([_P, _Z, _P, _P], ctypes.c_int),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -485,3 +489,28 @@ def loki_attend(q, P, K_rot, V, idx, workspace=None):
     _check(lib.loki_attend(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(V), _ptr(idx), _ptr(out),
                            B, Hq, Hkv, S, d, k, dt, _ptr(ws), ws.numel(), _stream(q)))
     return out
+
+
+def loki_bench_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Plain copy of src's bytes into dst (same number of bytes, a multiple of
+    16): the reference kernel for the memory-system figures."""
+    _need(src, "src")
+    _need(dst, "dst", device=src.device)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _gpu(src, "src")
+    _check(load_library().loki_bench_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
+
+
+def loki_bench_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Plain streaming read of src's bytes; returns the device uint32 sink
+    (int32 tensor of one element, zeroed first) that holds the XOR of every
+    32-bit word read."""
+    _need(src, "src")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    _need(sink, "sink", dtype=torch.int32, device=src.device, shape=(1,))
+    _gpu(src, "src")
+    _check(load_library().loki_bench_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)))
+    return sink

@@ -19,8 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libloki.so")
 
-SOURCES = ["api.hip", "calib_kernels.hip", "decode_kernels.hip", "mfma_kernels.hip", "pair_kernels.hip",
-           "project_kernels.hip"]
+SOURCES = ["api.hip", "calib_kernels.hip", "decode_kernels.hip", "measure_kernels.hip", "mfma_kernels.hip",
+           "pair_kernels.hip", "project_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

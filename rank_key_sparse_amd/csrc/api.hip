@@ -552,4 +552,28 @@ loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, v
   }
 }
 
+loki_status loki_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
+  try {
+    if (bytes % 16 != 0) return LOKI_ERR_SHAPE;
+    if (bytes == 0) return LOKI_OK;
+    if (!src || !dst) return LOKI_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst)) return LOKI_ERR_ALIGN;
+    return from_hip(launch_bench_copy(src, dst, bytes, stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
+loki_status loki_bench_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  try {
+    if (bytes % 16 != 0) return LOKI_ERR_SHAPE;
+    if (bytes == 0) return LOKI_OK;
+    if (!src || !sink) return LOKI_ERR_NULL;
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return LOKI_ERR_ALIGN;
+    return from_hip(launch_bench_read(src, bytes, sink, stream));
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
 }  // extern "C"

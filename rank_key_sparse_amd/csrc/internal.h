@@ -131,6 +131,11 @@ hipError_t launch_append_kv(const void* k_new, const void* v_new, const void* P,
 hipError_t launch_project(const void* K, const void* P, void* K_rot, void* K_lead, int R, int B,
                           int Hkv, int S, int d, int dt, hipStream_t st);
 
+// Memory-system reference kernels: a copy of `bytes` (a multiple of 16) and a
+// streaming read that XORs every 32-bit word of src into *sink.
+hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+
 // Basis calibration (principal directions of the keys of each key head).
 struct CalibPlan {
   int B, Hkv, S, d, dt;

@@ -258,3 +258,17 @@ def test_calibrate_asym_rejects(lib):
     need = lib.loki_calibrate_asym_workspace_bytes(100, 4, 1, 2, 50, 128, 8)
     assert need > 0
     assert f(A, A, A, A, 100, 4, 1, 2, 50, 128, 8, BF16, A2, need - 1, NULLP) == WORKSPACE
+
+
+def test_bench_kernels_reject(lib):
+    Z = ctypes.c_size_t
+    assert lib.loki_bench_copy(A, A2, Z(100), NULLP) == SHAPE          # not a multiple of 16
+    assert lib.loki_bench_copy(NULLP, A2, Z(64), NULLP) == NULL
+    assert lib.loki_bench_copy(A, NULLP, Z(64), NULLP) == NULL
+    assert lib.loki_bench_copy(MIS, A2, Z(64), NULLP) == ALIGN
+    assert lib.loki_bench_copy(NULLP, NULLP, Z(0), NULLP) == OK         # nothing to do
+    assert lib.loki_bench_read(A, Z(24), A2, NULLP) == SHAPE
+    assert lib.loki_bench_read(NULLP, Z(64), A2, NULLP) == NULL
+    assert lib.loki_bench_read(A, Z(64), NULLP, NULLP) == NULL
+    assert lib.loki_bench_read(MIS, Z(64), A2, NULLP) == ALIGN
+    assert lib.loki_bench_read(A, Z(64), ctypes.c_void_p(0x20002), NULLP) == ALIGN

@@ -831,3 +831,20 @@ def test_concurrent_streams_match_sequential(gpu_lib):
         for i in range(len(inputs)):
             assert torch.equal(idxs[i], seq[i][1]), (rep, i)
             assert torch.equal(_bits(outs[i]), _bits(seq[i][0])), (rep, i)
+
+
+# ---------------------------------------------------------------- memory-system reference kernels
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000 + 16, 64 << 20])
+def test_bench_copy_and_read(gpu_lib, nbytes):
+    # the copy moves every byte; the read's sink is the XOR of every 32-bit word
+    g = torch.Generator().manual_seed(nbytes % 1000)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    s, d = dev(src), torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    gpu_lib.loki_bench_copy(s, d)
+    sink = gpu_lib.loki_bench_read(s)
+    torch.cuda.synchronize()
+    assert torch.equal(d.cpu(), src)
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
