@@ -399,6 +399,27 @@ loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, v
                                 loki_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): loki_decode_lead (K_lead may be NULL: then loki_decode) with
+ * the workspace taken from a fixed device array inside the library,
+ * LOKI_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine).  Sizes whose workspace
+ * (loki_decode_workspace_bytes) exceeds LOKI_NOALLOC_SCRATCH_BYTES return
+ * LOKI_ERR_WORKSPACE; everything else (arguments, outputs, errors) is as
+ * for loki_decode_lead.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (concurrent streams, or host threads) race and
+ * give undefined results; calls ordered on one stream are safe.  The array
+ * keeps the last call's contents; no decode reads scratch it has not
+ * written in the same call.
+ */
+#define LOKI_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+loki_status loki_decode_noalloc(const void* q, const void* P, const void* K_rot, const void* K_lead, int32_t R,
+                                const void* V, void* out, int32_t* idx, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t S, int32_t d, int32_t r, int32_t k, loki_dtype dt, hipStream_t stream);
+
+/*
  * Memory-system reference kernels (measurement only; no step of the
  * method).  They are the reference points of the decode's HBM figures: the
  * rate a pure stream reaches on this part, and a kernel of known bytes that

@@ -81,6 +81,8 @@ _SIGS = {
     "loki_calibrate_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "loki_calibrate_pca": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P], ctypes.c_int),
     "loki_calibrate_pca_profiled": ([_P, _P, _P, _I, _I, _I, _I, ctypes.c_int, _P, _Z, _P, _P], ctypes.c_int),
+    "loki_decode_noalloc": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_int, _P],
+                            ctypes.c_int),
     "loki_bench_copy": ([_P, _P, _Z, _P], ctypes.c_int),
     "loki_bench_read": ([_P, _Z, _P, _P], ctypes.c_int),
 }
@@ -514,3 +516,24 @@ def loki_bench_read(src: torch.Tensor, sink: torch.Tensor | None = None) -> torc
     _gpu(src, "src")
     _check(load_library().loki_bench_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)))
     return sink
+
+
+def loki_decode_noalloc(q, P, K_rot, V, r: int, k: int, out, idx, K_lead=None):
+    """loki_decode (with K_lead: loki_decode_lead) with the library's own fixed
+    device scratch instead of a workspace: for callers that cannot allocate.
+    out [B,Hq,d] and idx [B,Hq,k] int32 are the caller's; this call allocates
+    nothing.  Calls that overlap on one GPU share the scratch and race."""
+    B, Hq, Hkv, S, d = _shapes(q, P, K_rot)
+    dev = q.device
+    _need(V, "V", dtype=q.dtype, device=dev, shape=K_rot.shape)
+    _need(out, "out", dtype=q.dtype, device=dev, shape=(B, Hq, d))
+    _need(idx, "idx", dtype=torch.int32, device=dev, shape=(B, Hq, k))
+    R = 0
+    if K_lead is not None:
+        _need(K_lead, "K_lead", dtype=q.dtype, ndim=4, device=dev)
+        R = K_lead.shape[3]
+        _need(K_lead, "K_lead", shape=(B, Hkv, S, R))
+    _gpu(q, "q")
+    _check(load_library().loki_decode_noalloc(_ptr(q), _ptr(P), _ptr(K_rot), _ptr(K_lead), R, _ptr(V), _ptr(out),
+                                              _ptr(idx), B, Hq, Hkv, S, d, r, k, _dtype_code(q), _stream(q)))
+    return out, idx

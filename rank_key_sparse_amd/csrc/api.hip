@@ -552,6 +552,67 @@ loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, v
   }
 }
 
+// ---------------------------------------------------------------- no-allocation decode
+
+}  // extern "C"
+
+namespace {
+
+// The decode's scratch for callers that cannot allocate: one file-scope
+// device array (each GPU the library runs on holds its own copy, at its own
+// address, until the process ends).  Host code never uses the array's name
+// as an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoallocScratch = LOKI_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratch];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, or a non-success status.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+loki_status loki_decode_noalloc(const void* q, const void* P, const void* K_rot, const void* K_lead, int32_t R,
+                                const void* V, void* out, int32_t* idx, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t S, int32_t d, int32_t r, int32_t k, loki_dtype dt, hipStream_t stream) {
+  try {
+    // the sizes are validated first, as for every entry point; then their
+    // scratch need against the fixed array
+    LOKI_TRY(check_dtype(dt));
+    LOKI_TRY(check_sizes(B, Hq, Hkv, S, d));
+    if (r < 1 || r > d || k < 1 || k > S) return LOKI_ERR_RANGE;
+    DecodePlan p;
+    if (!make_decode_plan(p, B, Hq, Hkv, S, d, r, k, (int)dt)) return LOKI_ERR_INTERNAL;
+    if (p.bytes > kNoallocScratch) return LOKI_ERR_WORKSPACE;
+    void* ws = nullptr;
+    LOKI_HIP(scratch_on_current_device(&ws));
+    return decode_impl(q, P, K_rot, K_lead, K_lead ? R : 0, V, out, idx, B, Hq, Hkv, S, d, r, k, dt, ws,
+                       kNoallocScratch, stream);
+  } catch (...) {
+    return LOKI_ERR_INTERNAL;
+  }
+}
+
 loki_status loki_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t stream) {
   try {
     if (bytes % 16 != 0) return LOKI_ERR_SHAPE;

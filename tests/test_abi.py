@@ -272,3 +272,16 @@ def test_bench_kernels_reject(lib):
     assert lib.loki_bench_read(A, Z(64), NULLP, NULLP) == NULL
     assert lib.loki_bench_read(MIS, Z(64), A2, NULLP) == ALIGN
     assert lib.loki_bench_read(A, Z(64), ctypes.c_void_p(0x20002), NULLP) == ALIGN
+
+
+def test_decode_noalloc_rejects_before_hip(lib):
+    def call(B=1, Hq=4, Hkv=2, S=100, d=128, r=8, k=10, dt=BF16):
+        return lib.loki_decode_noalloc(A, A, A, NULLP, 0, A, A, A, B, Hq, Hkv, S, d, r, k, dt, NULLP)
+    assert call(B=0) == SHAPE
+    assert call(Hq=5) == SHAPE
+    assert call(d=96) == UNSUPPORTED
+    assert call(r=0) == RANGE and call(k=101) == RANGE
+    assert call(dt=7) == DTYPE
+    # a workspace beyond the fixed scratch (48 MiB) is rejected before any HIP call
+    assert lib.loki_decode_workspace_bytes(16, 32, 8, 65536, 128, 32, 1024, BF16) > (48 << 20)
+    assert call(B=16, Hq=32, Hkv=8, S=65536, r=32, k=1024) == WORKSPACE
