@@ -84,7 +84,14 @@ typedef enum {
   LOKI_ERR_INTERNAL = 9     /* unexpected internal failure                      */
 } loki_status;
 
+/* Storage dtype.  A C caller may pass any integer: C++ gives the enum a
+ * fixed 32-bit representation, so an unknown code is a value the library can
+ * test (LOKI_ERR_DTYPE) rather than an out-of-range enum. */
+#ifdef __cplusplus
+typedef enum : int32_t { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
+#else
 typedef enum { LOKI_F32 = 0, LOKI_BF16 = 1 } loki_dtype;
+#endif
 
 /* LOKI_ABI_VERSION of the built library. */
 int loki_abi_version(void);

@@ -91,11 +91,13 @@ EXPORTED = tuple(_SIGS)
 
 
 def load_library(path: str | None = None):
-    """Load (once) and return the ctypes handle of libloki.so."""
+    """Load (once) and return the ctypes handle of libloki.so (the in-tree
+    build, or the file that the LOKI_LIBRARY environment variable names, e.g.
+    a host-sanitized build of the same sources)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("LOKI_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libloki.so not built ({p}); run `python -m rank_key_sparse_amd.build`")
     lib = ctypes.CDLL(p)

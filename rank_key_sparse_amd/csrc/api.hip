@@ -2,6 +2,7 @@
 // workspace carving, and the launch sequence of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -71,7 +72,28 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-loki_status from_hip(hipError_t e) { return e == hipSuccess ? LOKI_OK : LOKI_ERR_HIP; }
+// LOKI_DEBUG=1 in the environment (read once): after every launch step the
+// entry point waits for its stream and takes the runtime's last error, so a
+// kernel that faults is reported as LOKI_ERR_HIP by the call that launched it
+// (slow; not for use under graph capture, where waiting is not allowed).
+bool debug_mode() {
+  static const bool on = [] {
+    const char* v = getenv("LOKI_DEBUG");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+  }();
+  return on;
+}
+
+// The status of a launch step (one or more kernels or an event record).
+loki_status after_launch(hipError_t e, hipStream_t st) {
+  if (e != hipSuccess) return LOKI_ERR_HIP;
+  if (debug_mode()) {
+    e = hipStreamSynchronize(st);
+    const hipError_t last = hipGetLastError();
+    if (e != hipSuccess || last != hipSuccess) return LOKI_ERR_HIP;
+  }
+  return LOKI_OK;
+}
 
 #define LOKI_TRY(expr)                          \
   do {                                          \
@@ -79,10 +101,10 @@ loki_status from_hip(hipError_t e) { return e == hipSuccess ? LOKI_OK : LOKI_ERR
     if (s_ != LOKI_OK) return s_;               \
   } while (0)
 
-#define LOKI_HIP(expr)                          \
-  do {                                          \
-    const hipError_t e_ = (expr);               \
-    if (e_ != hipSuccess) return LOKI_ERR_HIP;  \
+#define LOKI_HIP(expr)                                  \
+  do {                                                  \
+    const loki_status s_ = after_launch((expr), stream); \
+    if (s_ != LOKI_OK) return s_;                       \
   } while (0)
 
 }  // namespace
@@ -131,7 +153,7 @@ loki_status loki_project_keys(const void* K, const void* P, void* K_rot, int32_t
                               int32_t S, int32_t d, loki_dtype dt, hipStream_t stream) {
   try {
     LOKI_TRY(check_project(K, P, K_rot, B, Hkv, S, d, dt));
-    return from_hip(launch_project(K, P, K_rot, nullptr, 0, B, Hkv, S, d, (int)dt, stream));
+    return after_launch(launch_project(K, P, K_rot, nullptr, 0, B, Hkv, S, d, (int)dt, stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }
@@ -144,7 +166,7 @@ loki_status loki_project_keys_lead(const void* K, const void* P, void* K_rot, vo
     // K_rot may be NULL (only the lead dims wanted); K_lead stands in for its checks
     LOKI_TRY(check_project(K, P, K_rot ? K_rot : K_lead, B, Hkv, S, d, dt));
     LOKI_TRY(check_lead(K_lead, R, d, 0, dt));
-    return from_hip(launch_project(K, P, K_rot, K_lead, R, B, Hkv, S, d, (int)dt, stream));
+    return after_launch(launch_project(K, P, K_rot, K_lead, R, B, Hkv, S, d, (int)dt, stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }
@@ -158,8 +180,8 @@ loki_status loki_append_kv(const void* k_new, const void* v_new, const void* P, 
     if (!v_new || !pos || !V) return LOKI_ERR_NULL;
     if (!aligned16(v_new) || !aligned16(V)) return LOKI_ERR_ALIGN;
     if (K_lead) LOKI_TRY(check_lead(K_lead, R, d, 0, dt));
-    return from_hip(launch_append_kv(k_new, v_new, P, pos, K_rot, V, K_lead, K_lead ? R : 0, B, Hkv, S, d, (int)dt,
-                                     stream));
+    return after_launch(launch_append_kv(k_new, v_new, P, pos, K_rot, V, K_lead, K_lead ? R : 0, B, Hkv, S, d, (int)dt,
+                                     stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }
@@ -485,7 +507,7 @@ static loki_status calibrate_impl(const void* K, void* P, double* eigvals, int32
   CalibPlan p;
   if (!make_calib_plan(p, B, Hkv, S, d, (int)dt)) return LOKI_ERR_INTERNAL;
   LOKI_TRY(check_workspace(ws, wsb, p.bytes));
-  return from_hip(launch_calibrate(p, K, P, eigvals, ws, stream, ev));
+  return after_launch(launch_calibrate(p, K, P, eigvals, ws, stream, ev), stream);
 }
 
 size_t loki_calibrate_workspace_bytes(int32_t B, int32_t Hkv, int32_t S, int32_t d) {
@@ -546,7 +568,7 @@ loki_status loki_calibrate_asym(const void* q_samples, const void* K, void* A, v
     AsymPlan p;
     if (!make_asym_plan(p, N, Hq, B, Hkv, S, d, r, (int)dt)) return LOKI_ERR_INTERNAL;
     LOKI_TRY(check_workspace(workspace, workspace_bytes, p.bytes));
-    return from_hip(launch_calibrate_asym(p, q_samples, K, A, Bm, workspace, stream));
+    return after_launch(launch_calibrate_asym(p, q_samples, K, A, Bm, workspace, stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }
@@ -619,7 +641,7 @@ loki_status loki_bench_copy(const void* src, void* dst, size_t bytes, hipStream_
     if (bytes == 0) return LOKI_OK;
     if (!src || !dst) return LOKI_ERR_NULL;
     if (!aligned16(src) || !aligned16(dst)) return LOKI_ERR_ALIGN;
-    return from_hip(launch_bench_copy(src, dst, bytes, stream));
+    return after_launch(launch_bench_copy(src, dst, bytes, stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }
@@ -631,7 +653,7 @@ loki_status loki_bench_read(const void* src, size_t bytes, uint32_t* sink, hipSt
     if (bytes == 0) return LOKI_OK;
     if (!src || !sink) return LOKI_ERR_NULL;
     if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return LOKI_ERR_ALIGN;
-    return from_hip(launch_bench_read(src, bytes, sink, stream));
+    return after_launch(launch_bench_read(src, bytes, sink, stream), stream);
   } catch (...) {
     return LOKI_ERR_INTERNAL;
   }

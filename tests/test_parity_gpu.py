@@ -848,3 +848,38 @@ def test_bench_copy_and_read(gpu_lib, nbytes):
     assert torch.equal(d.cpu(), src)
     want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
+
+
+_DEBUG_RUN = """
+import sys, torch
+sys.path.insert(0, {root!r})
+import rank_key_sparse_amd as rks
+from loki_inputs import CONFIGS, make_inputs
+cfg = CONFIGS["C3"].scaled(S=2048, B={B})
+x = {{n: v.to("cuda") for n, v in make_inputs(cfg).items() if n in ("q", "P", "K_rot", "V")}}
+out, idx = rks.loki_decode(x["q"], x["P"], x["K_rot"], x["V"], cfg.r, cfg.k)
+torch.cuda.synchronize()
+torch.save({{"out": out.cpu(), "idx": idx.cpu()}}, {path!r})
+"""
+
+
+@pytest.mark.parametrize("B", [2, 16])  # two-kernel path, and the fused pair path
+def test_debug_mode_same_results(gpu_lib, B, tmp_path):
+    # LOKI_DEBUG=1 waits for the stream after every launch step and checks the
+    # runtime's error; the results are the default mode's, bit for bit
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = str(tmp_path / "dbg.pt")
+    env = dict(os.environ, LOKI_DEBUG="1")
+    r = subprocess.run([sys.executable, "-c", _DEBUG_RUN.format(root=root, B=B, path=path)], env=env,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    got = torch.load(path, weights_only=True)
+    cfg = CONFIGS["C3"].scaled(S=2048, B=B)
+    x = make_inputs(cfg)
+    out, idx = gpu_lib.loki_decode(dev(x["q"]), dev(x["P"]), dev(x["K_rot"]), dev(x["V"]), cfg.r, cfg.k)
+    torch.cuda.synchronize()
+    assert torch.equal(got["idx"], idx.cpu())
+    assert torch.equal(got["out"].view(torch.int16), out.cpu().view(torch.int16))
