@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libloki.so")
 
 SOURCES = ["api.hip", "calib_kernels.hip", "decode_kernels.hip", "measure_kernels.hip", "mfma_kernels.hip",
-           "pair_kernels.hip", "project_kernels.hip"]
+           "pair_kernels.hip", "project_kernels.hip", "select_attend_kernels.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

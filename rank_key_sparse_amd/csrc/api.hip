@@ -268,11 +268,28 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     uint32_t* ckey = at<uint32_t>(workspace, p.off_ckey);
     LOKI_HIP(launch_score_select_chunk(ps, src, ld, qsplit_s, cidx, ckey, ldc, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+    if (select_attend_fits(p)) {
+      // the second stage and the attention of each head in one launch
+      if (plain_attn) LOKI_HIP(launch_qplain(p, q, qrot, qsplit, stream));
+      LOKI_HIP(launch_select_attend(p, ckey, cidx, ldc, ldc, qsplit, K_rot, V, out, idx, stream));
+      if (ev)
+        for (int i = 3; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
+      return LOKI_OK;
+    }
     LOKI_HIP(launch_select_merge(B * Hq, S, k, p.W, ldc, ckey, cidx, idx, bitmap, lens, Hq, stream));
   } else {
     uint2* mm = select_needs_minmax(S) ? at<uint2>(workspace, p.off_mm) : nullptr;
     LOKI_HIP(launch_scores(ps, src, ld, qrot_s, qsplit_s, keys, true, p.Sp, mm, stream));
     if (ev) LOKI_HIP(hipEventRecord(ev[2], stream));
+    if (select_attend_fits(p) && !select_needs_minmax(S)) {
+      // heads whose keys fit the register selection: selection and attention
+      // of each head in one launch
+      if (plain_attn) LOKI_HIP(launch_qplain(p, q, qrot, qsplit, stream));
+      LOKI_HIP(launch_select_attend(p, keys, nullptr, p.Sp, 0, qsplit, K_rot, V, out, idx, stream));
+      if (ev)
+        for (int i = 3; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
+      return LOKI_OK;
+    }
     LOKI_HIP(launch_select(B * Hq, S, p.Sp, k, p.W, keys, mm, p.NSC, at<uint32_t>(workspace, p.off_masks),
                            idx, bitmap, stream, at<int32_t>(workspace, p.off_cidx),
                            at<uint32_t>(workspace, p.off_ckey), lens, Hq));

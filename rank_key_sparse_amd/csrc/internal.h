@@ -114,6 +114,15 @@ hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld
 // keys (asymmetric index); else q P against Kx = K_rot.
 hipError_t launch_decode_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
                               const void* Kx, const void* V, void* out, int32_t* idx, bool plain, hipStream_t st);
+// Selection and exact attention of each query head in one launch (bf16, d 64
+// or 128): one block per query head over its keys keys[row][0..S) (row
+// stride ldk, S <= 32768), or, with cidx, over its chunk winners
+// keys / cidx[row][0..S2) (row stride ldk); writes idx and out.  qsplit is
+// the exact stage's split query.
+bool select_attend_fits(const DecodePlan& p);
+hipError_t launch_select_attend(const DecodePlan& p, const uint32_t* keys, const int32_t* cidx, int ldk, int S2,
+                                const uint16_t* qsplit, const void* Kx, const void* V, void* out, int32_t* idx,
+                                hipStream_t st);
 // Long heads (bf16): fused scores + the first selection stage, one block per
 // (query head, chunk of kSelChunk tokens), into the candidate lists cidx /
 // ckey (ldc words per row); then launch_select_merge finishes the selection.

@@ -10,22 +10,13 @@
 
 #include <type_traits>
 
+#include "attend_core.h"
 #include "common.h"
 #include "internal.h"
 #include "mfma_common.h"
 #include "select_core.h"
 
 namespace loki {
-
-// Max over the aligned 16-lane rows of a wave (every lane of a row ends with
-// the row's max): quad swaps, then the half-row and row mirrors.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
-  return v;
-}
 
 // ============================================================================
 // Pair kernel: one block of 1024 threads per pair of query heads of a
@@ -240,23 +231,13 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   }
   if constexpr (MODE != 0) {
     // ========================================================================
-    // Exact attention of the pair's two heads over their kept tokens.
-    // The union of the two kept sets is listed in ascending token order
-    // (entry = token | kept-by-head-0 << 30 | kept-by-head-1 << 31) in the
-    // LDS that held the keys; thread w lists bitmap word w, at offsets from
-    // block scans of the union's and of each head's counts, and writes each
-    // head's kept tokens to its idx row (ascending) at the same time.  Wave w then takes 16-row tiles w + 16 i of
-    // the list in one pass, double buffered: for a tile, the K rows (MFMA B
-    // operand, 64 contiguous bytes of each of 16 rows per load instruction)
-    // and the V rows (16-byte granules, RL lanes per row) are requested
-    // together, one tile ahead of the one being used.  Per tile: the exact
-    // scores of both heads from MFMA (the heads' split rows in A rows 0..7:
-    // lane l holds head l / 16's score of row l % 16), scaled to log2 units,
-    // -inf where the head did not keep the token; an online softmax per head
-    // (running max and sum; the accumulators are rescaled when the max
-    // grows); each lane's V granules weighted by both heads' weights of
-    // their rows (read from the score lanes by lane permutes).  The 16
-    // waves' (max, sum, acc) of each head are merged by log-sum-exp.
+    // Exact attention of the pair's two heads over their kept tokens.  The
+    // union of the two kept sets is listed in ascending token order (entry =
+    // token | kept-by-head-0 << 30 | kept-by-head-1 << 31) in the LDS that
+    // held the keys; thread w lists bitmap word w, at offsets from block
+    // scans of the union's and of each head's counts, and writes each head's
+    // kept tokens to its idx row (ascending) at the same time.  attend_list
+    // (attend_core.h) then runs both heads' attention in one pass over it.
     // ========================================================================
     __syncthreads();  // the bitmaps (take) are complete
     uint32_t* list = lk;
@@ -287,137 +268,11 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       }
     }
     __syncthreads();
-    const int n = s_n;  // >= 1: each head keeps min(k, S) >= 1 tokens
-    const int ntile = (n + 15) >> 4;
-    constexpr int KSD = D / 32;   // k-steps of the exact dot
-    constexpr int RL = D / 8;     // lanes per V row
-    constexpr int RPW = 64 / RL;  // V rows per wave pass
-    constexpr int VP = 16 / RPW;  // V passes per tile
-    constexpr uint32_t TOK = 0x3fffffffu;
-    // the A operands (both heads' split rows over all D dims) are read from
-    // LDS per tile rather than held in registers
-    const uint16_t* qx = MODE == 2 ? sqp : sqs;
+    // the attention itself (both heads, one pass over the list); its merge
+    // scratch follows the list (<= Sp entries) in the LDS that held the keys
     const size_t cb = (size_t)gi * Scap * D;  // this group's rows of K and V
-    const int lg = lane / RL, li = lane % RL;
-    auto load_tile = [&](int t, uint4 (&kb)[KSD], uint4 (&vb)[VP]) {
-      const uint32_t tk = list[min(16 * t + m, n - 1)] & TOK;
-      const bf16_t* kr = Kx + cb + (size_t)tk * D + 8 * q4;
-#pragma unroll
-      for (int s = 0; s < KSD; ++s) kb[s] = ldg16(kr + 32 * s);
-#pragma unroll
-      for (int u = 0; u < VP; ++u) {
-        const uint32_t tv = list[min(16 * t + RPW * u + lg, n - 1)] & TOK;
-        vb[u] = ldg16(V + cb + (size_t)tv * D + 8 * li);
-      }
-    };
-    float acc[2][8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-    float mr0 = -INFINITY, mr1 = -INFINITY;  // running maxima (the same in every lane)
-    float lp = 0.f;                          // this lane's share of its head's weight sum
-    auto proc_tile = [&](int t, const uint4 (&kb)[KSD], const uint4 (&vb)[VP]) {
-      floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KSD; ++s)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_rows(qx, 0, D, 2, D, m, 32 * s + 8 * q4), as_bf16x8(kb[s]),
-                                                       sacc, 0, 0, 0);
-      const int p = 16 * t + m;
-      const uint32_t ent = list[min(p, n - 1)];
-      const bool kept = q4 < 2 && p < n && ((ent >> (30 + (q4 & 1))) & 1u);
-      const float e = kept ? sum_split_rows(sacc) * scale_log2 : -INFINITY;
-      const float tm = row16_max(e);
-      const float n0 = fmaxf(mr0, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tm), 0)));
-      const float n1 = fmaxf(mr1, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tm), 16)));
-      const float c0 = (n0 == -INFINITY) ? 1.f : exp2f(mr0 - n0);
-      const float c1 = (n1 == -INFINITY) ? 1.f : exp2f(mr1 - n1);
-      mr0 = n0;
-      mr1 = n1;
-      const float w = kept ? exp2f(e - (q4 == 0 ? n0 : n1)) : 0.f;
-      lp = fmaf(lp, q4 == 0 ? c0 : c1, w);
-      float wv[2][VP];
-#pragma unroll
-      for (int u = 0; u < VP; ++u) {
-        wv[0][u] = __shfl(w, RPW * u + lg);
-        wv[1][u] = __shfl(w, 16 + RPW * u + lg);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[0][i] *= c0;
-        acc[1][i] *= c1;
-      }
-#pragma unroll
-      for (int u = 0; u < VP; ++u) {
-        float x[8];
-        Gran<bf16_t>::unpack(vb[u], x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          acc[0][i] = fmaf(wv[0][u], x[i], acc[0][i]);
-          acc[1][i] = fmaf(wv[1][u], x[i], acc[1][i]);
-        }
-      }
-    };
-    {
-      uint4 ka[KSD], va[VP], kb2[KSD], vb2[VP];
-      load_tile(min(wave, ntile - 1), ka, va);
-      for (int t = wave; t < ntile; t += 2 * NWV) {  // unconditional loads: tiles past the end repeat the last
-        load_tile(min(t + NWV, ntile - 1), kb2, vb2);
-        proc_tile(t, ka, va);
-        if (t + NWV >= ntile) break;  // uniform across the wave
-        load_tile(min(t + 2 * NWV, ntile - 1), ka, va);
-        proc_tile(t + NWV, kb2, vb2);
-      }
-    }
-    // per head: the weight sum over its 16 score lanes; per dim: the sum of
-    // the accumulators over the lanes holding other rows of the same dims
-    lp = group_sum<16>(lp);
-    const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), 0));
-    const float l1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp), 16));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float v = acc[h][i];
-        // lane ^ 8 and lane ^ 16 by ds_swizzle (bit-mask mode, no address), lane ^ 32 by bpermute
-        if constexpr (RL <= 8) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F));
-        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-        v += __shfl_xor(v, 32);
-        acc[h][i] = v;
-      }
-    // merge the 16 waves by log-sum-exp (the selection's LDS is free now)
-    float* s_acc = reinterpret_cast<float*>(&sel[0][0]);  // [NWV][2][D]
-    float* s_ml = reinterpret_cast<float*>(&take[0][0]);  // [NWV][2][2] (max, sum)
-    static_assert(NWV * 2 * D <= 2 * kNB, "merge buffer fits the selection's LDS");
-    // (take and sel were last read before the barrier that follows the list)
-    if (lg == 0) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s_acc[(wave * 2 + h) * D + li * 8 + i] = acc[h][i];
-    }
-    if (lane == 0) {
-      s_ml[wave * 4 + 0] = mr0;
-      s_ml[wave * 4 + 1] = l0;
-      s_ml[wave * 4 + 2] = mr1;
-      s_ml[wave * 4 + 3] = l1;
-    }
-    __syncthreads();
-    if (tid < 2 * D) {
-      const int h = tid / D, c = tid - h * D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) M = fmaxf(M, s_ml[w * 4 + 2 * h]);
-      float L = 0.f, A = 0.f;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) {
-        const float mw = s_ml[w * 4 + 2 * h];
-        const float f = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        L = fmaf(s_ml[w * 4 + 2 * h + 1], f, L);
-        A = fmaf(s_acc[(w * 2 + h) * D + c], f, A);
-      }
-      out[(row0 + h) * D + c] = f32_to_bf16(L > 0.f ? A / L : 0.f);
-    }
+    attend_list<D, 2, kPairThreads>(list, s_n, MODE == 2 ? sqp : sqs, Kx + cb, V + cb, scale_log2, out + row0 * D,
+                                    reinterpret_cast<float*>(lk + Sp));
   }
 }
 
@@ -433,8 +288,10 @@ static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, cons
                               float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap, const void* Kx,
                               const void* V, void* out, hipStream_t st) {
   if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
-  // keys [2][Sp] (then the union list, <= Sp entries), at least the rotation scratch [2 + 16][d] words
-  const size_t lds = (size_t)max(2 * p.Sp, 18 * p.d) * sizeof(uint32_t);
+  // keys [2][Sp] (then the union list, <= Sp entries, and the attention's
+  // merge scratch), at least the rotation scratch [2 + 16][d] words
+  const int merge = p.d == 64 ? attend_merge_words<64, 2, kPairThreads>() : attend_merge_words<128, 2, kPairThreads>();
+  const size_t lds = (size_t)max(max(2 * p.Sp, 18 * p.d), p.Sp + merge) * sizeof(uint32_t);
   const int ngroups = p.B * p.Hkv;
   const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d));
