@@ -89,8 +89,14 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
 // ============================================================================
 // host side
 // ============================================================================
+// One CU sustains ~40 GB/s of gathered rows (its outstanding misses, not
+// HBM, bound it), so one block per head only pays when the blocks fill the
+// chip or a head's kept rows are small; otherwise the attention kernel that
+// spreads a group's rows over many blocks is faster.
 bool select_attend_fits(const DecodePlan& p) {
-  return p.dt == 1 && (p.d == 64 || p.d == 128);
+  const size_t head_rows_bytes = (size_t)p.k * p.d * 2 * 2;  // K and V rows of one head, bf16
+  return p.dt == 1 && (p.d == 64 || p.d == 128) &&
+         ((size_t)p.B * p.Hq >= 256 || head_rows_bytes <= ((size_t)256 << 10));
 }
 
 hipError_t launch_select_attend(const DecodePlan& p, const uint32_t* keys, const int32_t* cidx, int ldk, int S2,

@@ -657,15 +657,18 @@ def test_decode_all_equal_keys_fused(gpu_lib):
 
 
 def test_fused_matches_two_kernel_path(gpu_lib):
-    # the same heads decoded with 256 (fused) and 128 (two kernels) query heads
+    # the same heads decoded with 256 query heads (scores and selection fused
+    # per head) and 128 (scores, then selection and attention per head): the
+    # score arithmetic is the same, so the kept sets are bit-identical; the
+    # attention sums in another order, so each output is checked against the
+    # oracle
     cfg = cfg_case("C2", S=4096, B=8)
     x = make_inputs(cfg)
-    q, P, Kr, V = (dev(x[n]) for n in ("q", "P", "K_rot", "V"))
-    o_all, i_all = gpu_lib.loki_decode(q, P, Kr, V, r=cfg.r, k=cfg.k)
-    o_half, i_half = gpu_lib.loki_decode(q[:4].contiguous(), P, Kr[:4].contiguous(), V[:4].contiguous(),
-                                         r=cfg.r, k=cfg.k)
+    _, i_all, _ = run_decode(gpu_lib, x, cfg.r, cfg.k)
+    half = {n: x[n][:4].contiguous() for n in ("q", "K_rot", "V")}
+    half["P"] = x["P"]
+    _, i_half, _ = run_decode(gpu_lib, half, cfg.r, cfg.k)
     assert torch.equal(i_all[:4], i_half)
-    assert torch.equal(o_all[:4].view(torch.int16), o_half.view(torch.int16))
 
 
 def test_pair_fused_rank_and_radix_heads(gpu_lib):
