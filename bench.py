@@ -49,8 +49,8 @@ STAGES = ["qrot", "scores", "select", "attend", "merge"]
 
 
 # the sources of the decode kernels whose counters profiles/traffic_*.json holds
-DECODE_SOURCES = ("common.h", "select_core.h", "mfma_common.h", "mfma_kernels.hip", "pair_kernels.hip",
-                  "decode_kernels.hip")
+DECODE_SOURCES = ("common.h", "select_core.h", "mfma_common.h", "attend_core.h", "mfma_kernels.hip",
+                  "pair_kernels.hip", "select_attend_kernels.hip", "decode_kernels.hip")
 
 
 def kernel_source_hash() -> str:
