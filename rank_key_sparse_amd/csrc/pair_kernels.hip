@@ -218,9 +218,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       load_batch(bi + 3, a0);
     }
     __syncthreads();  // every key and histogram count is in LDS
-    uint32_t key[2][T];
-    load_regs<T>(lk, S, key[0]);
-    load_regs<T>(lk + Sp, S, key[1]);
+    const uint32_t* const key[2] = {lk, lk + Sp};  // the scores stay in LDS
     uint32_t* const lds2[2] = {sel[0], sel[1]};
     uint32_t* const take2[2] = {take[0], take[1]};
     int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};

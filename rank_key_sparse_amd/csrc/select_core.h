@@ -378,10 +378,11 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 }
 
 // ============================================================================
-// Two heads at once (same S, k, W; scores in registers as for select_regs,
-// but as raw fp32 bits: bins come straight from the value, and the
-// order-preserving key is formed only where a total order is needed, for
-// the threshold bin's candidates and the radix tie path):
+// Two heads at once (same S, k, W; the scores as raw fp32 bits in LDS,
+// sbits[h][token], read in the register layout of select_regs: bins come
+// straight from the value and stay in registers, and the order-preserving
+// key is formed only where a total order is needed, for the threshold bin's
+// candidates and the radix tie path; sbits must not change during the call):
 // every step handles both heads between shared barriers, so a pair costs
 // the barriers and latencies of one selection.  Both histograms go through
 // one block scan with the two counts packed in 16-bit halves, which needs
@@ -397,7 +398,7 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
 // that lists the kept tokens itself) and orow is not used.
 // ============================================================================
 template <int NTHR, int T, bool EMIT = true>
-__device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint32_t* const (&lds)[2],
+__device__ __forceinline__ void select_regs2(const uint32_t* const (&sbits)[2], uint32_t* const (&lds)[2],
                                              uint32_t* const (&take)[2], int S, int k, int W,
                                              int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
                                              SelScratch<NTHR>* const (&sh)[2],
@@ -406,20 +407,25 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
   Binner bin[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) bin[h].init(kmm[h][0], kmm[h][1]);
-  auto key = [&](int h, int i) { return score_key(__uint_as_float(sbits[h][i])); };
+  // the scores stay in LDS (sbits[h][token], fp32 bits) and are read where a
+  // key is needed; only each score's bin is held in registers, so the mask
+  // pass never recomputes bins
+  const int tok0 = opaque(regs_tok0<T>());
+  auto key = [&](int h, int i) { return score_key(__uint_as_float(sbits[h][min(tok0 + 64 * i, S - 1)])); };
 
   // 1. both histograms (unless prebuilt); each score's bin stays in a
-  // register for step 2
+  // register for step 2 (-1 for a slot past S: the reads are clamped in
+  // bounds, so the bins are computed without a branch)
   int kb[2][T];
   int nv = opaque(regs_valid<T>(S));
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < T; ++i)
-      if (i < nv) {
-        kb[h][i] = bin[h].of_score(__uint_as_float(sbits[h][i]));
-        if (!prebuilt) atomicAdd(&lds[h][kb[h][i]], 1u);
-      }
+    for (int i = 0; i < T; ++i) {
+      const int b = bin[h].of_score(__uint_as_float(sbits[h][min(tok0 + 64 * i, S - 1)]));
+      kb[h][i] = i < nv ? b : -1;
+      if (!prebuilt && i < nv) atomicAdd(&lds[h][b], 1u);
+    }
   if (!prebuilt) __syncthreads();  // uniform
 
   // threshold bins: one scan of (count0 | count1 << 16) from the top bin
@@ -459,14 +465,13 @@ __device__ __forceinline__ void select_regs2(const uint32_t (&sbits)[2][T], uint
   // 2. above-masks and threshold-bin candidates of both heads
   uint32_t klo[2] = {0u, 0u}, khi[2] = {0u, 0u};
   nv = opaque(nv);
-  const int tok0 = opaque(regs_tok0<T>());
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     uint32_t* ck = lds[h];
     uint32_t* ci = lds[h] + kCap;
 #pragma unroll
     for (int i = 0; i < T; ++i) {
-      const int bj = (i < nv) ? kb[h][i] : -1;
+      const int bj = kb[h][i];  // -1 past S
       const uint64_t mab = __ballot(bj > tb[h]);
       if (lane == i) { klo[h] = (uint32_t)mab; khi[h] = (uint32_t)(mab >> 32); }
       if (rank_path[h] && bj == tb[h]) {
