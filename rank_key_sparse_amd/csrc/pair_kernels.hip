@@ -211,11 +211,24 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       if (q4 < 2 && t < S) atomicAdd(&sel[q4][bq.of_score(__uint_as_float(lk[q4 * Sp + t]))], 1u);
     }
     load_batch(2, a0);
-    for (int bi = 1; bi < nbat; bi += 2) {  // batches past the end score no token
+    // batch bi is in a1 and bi + 1 in a0 at the top of each step; the steady
+    // loop only requests batches that exist, and the last one to three are
+    // scored after it, so that no load is left in flight past the scores
+    // (batches past the end, here and for nbat <= 2, score no token)
+    int bi = 1;
+    for (; bi + 3 < nbat; bi += 2) {
       score_batch(bi, a1, std::true_type{});
       load_batch(bi + 2, a1);
       score_batch(bi + 1, a0, std::true_type{});
       load_batch(bi + 3, a0);
+    }
+    score_batch(bi, a1, std::true_type{});
+    if (bi + 2 < nbat) {  // uniform
+      load_batch(bi + 2, a1);
+      score_batch(bi + 1, a0, std::true_type{});
+      score_batch(bi + 2, a1, std::true_type{});
+    } else {
+      score_batch(bi + 1, a0, std::true_type{});
     }
     __syncthreads();  // every key and histogram count is in LDS
     const uint32_t* const key[2] = {lk, lk + Sp};  // the scores stay in LDS

@@ -115,19 +115,24 @@ __device__ __forceinline__ void find_threshold(const uint32_t* hist, int want, S
 
 struct Binner {
   float fmin, scale;
-  bool degenerate;
+  // A degenerate range (every key equal, or a range or scale that is not a
+  // positive finite number) gets scale 0, which puts every value in bin 0
+  // with no branch in of_score.
   __device__ __forceinline__ void init(uint32_t kmin, uint32_t kmax) {
     fmin = key_score(kmin);
     const float range = key_score(kmax) - fmin;
     scale = (float)kNB / range;
-    degenerate = !(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f);
+    if (!(range > 0.f) || !isfinite(range) || !isfinite(scale) || !(scale > 0.f)) {
+      fmin = 0.f;
+      scale = 0.f;
+    }
   }
   // bin of a score value (the same map as of its key: key_score(score_key(s))
   // is s, with -0 read as +0, which bins alike).  A value below fmin, or the
-  // NaN that key 0 (an empty candidate slot) decodes to, goes to bin 0: the
-  // max with 0 returns its non-NaN operand.
+  // NaN that key 0 (an empty candidate slot) decodes to -- and, under scale
+  // 0, every finite value -- goes to bin 0: the max with 0 returns its
+  // non-NaN operand.
   __device__ __forceinline__ int of_score(float s) const {
-    if (degenerate) return 0;
     const int b = (int)fmaxf((s - fmin) * scale, 0.f);
     return b < kNB - 1 ? b : kNB - 1;
   }
