@@ -257,7 +257,10 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
       for (int i = 2; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
     return LOKI_OK;
   }
-  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream));
+  uint32_t* scnt = at<uint32_t>(workspace, p.off_scnt);
+  float* spart = at<float>(workspace, p.off_spart);
+  // the rotation launch also clears the split attention's counters
+  LOKI_HIP(launch_qrot(p, q, P, qrot, qsplit, stream, scnt, p.NSPL > 1 ? B * Hq : 0));
   if (aqua) LOKI_HIP(launch_qdims(p, q, qrot, qrot_s, qsplit_s, dims, info, aqua_r, stream));
   if (ev) LOKI_HIP(hipEventRecord(ev[1], stream));
   if (fused) {
@@ -271,7 +274,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
     if (select_attend_fits(p)) {
       // the second stage and the attention of each head in one launch
       if (plain_attn) LOKI_HIP(launch_qplain(p, q, qrot, qsplit, stream));
-      LOKI_HIP(launch_select_attend(p, ckey, cidx, ldc, ldc, qsplit, K_rot, V, out, idx, stream));
+      LOKI_HIP(launch_select_attend(p, ckey, cidx, ldc, ldc, qsplit, K_rot, V, out, idx, spart, scnt, stream));
       if (ev)
         for (int i = 3; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
       return LOKI_OK;
@@ -285,7 +288,7 @@ static loki_status decode_impl(const void* q, const void* P, const void* K_rot, 
       // heads whose keys fit the register selection: selection and attention
       // of each head in one launch
       if (plain_attn) LOKI_HIP(launch_qplain(p, q, qrot, qsplit, stream));
-      LOKI_HIP(launch_select_attend(p, keys, nullptr, p.Sp, 0, qsplit, K_rot, V, out, idx, stream));
+      LOKI_HIP(launch_select_attend(p, keys, nullptr, p.Sp, 0, qsplit, K_rot, V, out, idx, spart, scnt, stream));
       if (ev)
         for (int i = 3; i < 6; ++i) LOKI_HIP(hipEventRecord(ev[i], stream));
       return LOKI_OK;

@@ -15,7 +15,8 @@
 // and sum; the accumulators are rescaled when the max grows); each lane's V
 // granules weighted by the heads' weights of their rows (read from the score
 // lanes by lane permutes).  The waves' (max, sum, acc) of each head are then
-// merged by log-sum-exp and head h's output row is written to out + h D.
+// merged by log-sum-exp and handed on: as head h's normalised output row at
+// out + h D, or as the block's partial when blocks share a head's list.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -48,10 +49,13 @@ constexpr int attend_merge_words() {
 // list.  qx: the heads' split query rows in LDS or global memory, [NH][4][D]
 // (part 3 zero); Kx, V: this key/value head's rows [S][D]; scratch: LDS of
 // attend_merge_words() floats that no thread reads or writes meanwhile.
-template <int D, int NH, int NTHR>
-__device__ __forceinline__ void attend_list(const uint32_t* list, int n, const uint16_t* qx,
-                                            const bf16_t* __restrict__ Kx, const bf16_t* __restrict__ V,
-                                            float scale_log2, bf16_t* __restrict__ out, float* scratch) {
+// emit(h, c, M, L, A) receives, for head h and dim c, the block's running
+// max M (log2 units), weight sum L and weighted sum A of V[.][c]; every
+// (h, c) once, by some thread of the block.
+template <int D, int NH, int NTHR, typename Emit>
+__device__ __forceinline__ void attend_list_core(const uint32_t* list, int n, const uint16_t* qx,
+                                                 const bf16_t* __restrict__ Kx, const bf16_t* __restrict__ V,
+                                                 float scale_log2, float* scratch, Emit&& emit) {
   static_assert(NH == 1 || NH == 2, "one or two heads per block");
   constexpr int NWV = NTHR / 64;
   constexpr int KSD = D / 32;   // k-steps of the exact dot
@@ -180,8 +184,18 @@ __device__ __forceinline__ void attend_list(const uint32_t* list, int n, const u
       L = fmaf(s_ml[w * 4 + 2 * h + 1], f, L);
       A = fmaf(s_acc[(w * NH + h) * D + cdim], f, A);
     }
-    out[(size_t)h * D + cdim] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+    emit(h, cdim, M, L, A);
   }
+}
+
+// The heads' normalised outputs, head h's row at out + h D.
+template <int D, int NH, int NTHR>
+__device__ __forceinline__ void attend_list(const uint32_t* list, int n, const uint16_t* qx,
+                                            const bf16_t* __restrict__ Kx, const bf16_t* __restrict__ V,
+                                            float scale_log2, bf16_t* __restrict__ out, float* scratch) {
+  attend_list_core<D, NH, NTHR>(list, n, qx, Kx, V, scale_log2, scratch, [&](int h, int c, float, float L, float A) {
+    out[(size_t)h * D + c] = f32_to_bf16(L > 0.f ? A / L : 0.f);
+  });
 }
 
 }  // namespace loki

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.h"
@@ -33,7 +35,9 @@ template <typename T, int GT>
 __global__ __launch_bounds__(256) void qrot_kernel(const T* __restrict__ q, const T* __restrict__ P,
                                                    float* __restrict__ qrot,
                                                    bf16_t* __restrict__ qsplit, int Hq, int Hkv,
-                                                   int d) {
+                                                   int d, uint32_t* __restrict__ zero, int nzero) {
+  for (int i = (blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; i < nzero; i += gridDim.x * gridDim.y * 256)
+    zero[i] = 0u;
   // Block = (b, kv) group x 32 columns of P, staged in LDS with 16-byte
   // loads; thread = (column, j-slice).  Each column is kQrotSlices FMA chains
   // over consecutive j-ranges, added in range order.
@@ -863,6 +867,16 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
   }
   p.NAC = (S + p.AC - 1) / p.AC;
   const size_t rows = (size_t)B * Hq;
+  // blocks per head of the one-launch selection + attention: as many as
+  // one round of blocks on 256 CUs holds (each block repeats the head's
+  // selection, so a second round would repeat it again), at most one per
+  // 16-row tile of the kept list
+  p.NSPL = 1;
+  if (rows < 256) {
+    long long ns = 256 / (long long)rows;
+    ns = std::min(ns, std::min((long long)kSplitMax, std::max(1LL, (long long)(k + 15) / 16)));
+    p.NSPL = (int)std::max(1LL, ns);
+  }
   size_t off = 0;
   p.off_qrot = off;   off = align_up(off + rows * d * sizeof(float), 256);
   p.off_qsplit = off; off = align_up(off + rows * 4 * d * sizeof(uint16_t), 256);
@@ -876,6 +890,8 @@ bool make_decode_plan(DecodePlan& p, int B, int Hq, int Hkv, int S, int d, int r
   p.off_ckey = off;   off = align_up(off + rows * ldc * sizeof(uint32_t), 256);
   p.off_bitmap = off; off = align_up(off + rows * (size_t)p.W * sizeof(uint32_t), 256);
   p.off_part = off;   off = align_up(off + rows * (size_t)p.NAC * (d + 2) * sizeof(float), 256);
+  p.off_spart = off;  off = align_up(off + rows * (size_t)p.NSPL * (d + 2) * sizeof(float), 256);
+  p.off_scnt = off;   off = align_up(off + rows * sizeof(uint32_t), 256);
   p.bytes = off;
   return true;
 }
@@ -909,19 +925,20 @@ static hipError_t dispatch_group(int G, F&& f) {
 
 template <typename T>
 static hipError_t qrot_t(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                         bf16_t* qsplit, hipStream_t st) {
+                         bf16_t* qsplit, hipStream_t st, uint32_t* zero, int nzero) {
   return dispatch_group(p.G, [&](auto gt) {
     constexpr int GT = decltype(gt)::value;
     hipLaunchKernelGGL((qrot_kernel<T, GT>), dim3(p.B * p.Hkv, p.d / 32), dim3(256), 0, st,
-                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, p.Hq, p.Hkv, p.d);
+                       static_cast<const T*>(q), static_cast<const T*>(P), qrot, qsplit, p.Hq, p.Hkv, p.d,
+                       zero, zero ? nzero : 0);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                       uint16_t* qsplit, hipStream_t st) {
-  return p.dt == 0 ? qrot_t<float>(p, q, P, qrot, qsplit, st)
-                   : qrot_t<bf16_t>(p, q, P, qrot, qsplit, st);
+                       uint16_t* qsplit, hipStream_t st, uint32_t* zero, int nzero) {
+  return p.dt == 0 ? qrot_t<float>(p, q, P, qrot, qsplit, st, zero, nzero)
+                   : qrot_t<bf16_t>(p, q, P, qrot, qsplit, st, zero, nzero);
 }
 
 template <typename T, int GT>

@@ -15,6 +15,7 @@ constexpr int kFusedMaxS = 16384;       // fused path: a head's keys fit in LDS 
 constexpr int kPairThreads = 1024;      // threads of the fused kernel for pairs of grouped heads
 constexpr int kSelRegMaxT = 32;         // selection keeps up to 1024 x 32 keys of a head in registers
 constexpr int kSelChunk = 16384;        // long heads: tokens per first-stage selection block
+constexpr int kSplitMax = 16;           // most blocks sharing one head's selection + attention
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -30,10 +31,14 @@ struct DecodePlan {
   int W;         // bitmap words per query head: Sp / 32
   int SC, NSC;   // approximate-score kernel: tokens per block, blocks per (b,kv)
   int AC, NAC;   // attention kernel: tokens per block, blocks per (b,kv)
+  int NSPL;      // selection + attention in one launch: blocks per query head
   // workspace: q_rot, its bf16 split, keys [row][Sp], per-score-chunk key
   // extremes [row][NSC] (uint2 min, max), selection masks [row][Sp/16] (used
   // when a row's keys do not fit in LDS), bitmap [row][W], attention partials
   size_t off_qrot, off_qsplit, off_keys, off_mm, off_masks, off_cidx, off_ckey, off_bitmap, off_part, bytes;
+  // per query head: NSPL attention partials [row][NSPL][d + 2] and the count
+  // of its blocks done [row] (cleared by the query rotation)
+  size_t off_spart, off_scnt;
   // query-magnitude scoring: q_rot masked to each head's chosen dims, and its split
   size_t off_qrot_m, off_qsplit_m;
   // per-sequence lengths [B] on the device (each clamped into [1, S]), or
@@ -55,9 +60,10 @@ bool make_select_plan(SelectPlan& p, int rows, int S, int k);
 
 // ---- launchers: enqueue on `st`; return hipGetLastError() after the launches.
 // q_rot in fp32 and, when qsplit is non-null, its three-way bf16 split as
-// MFMA operands qsplit[row][part][d] (part 3 is zero).
+// MFMA operands qsplit[row][part][d] (part 3 is zero).  The same launch sets
+// zero[0..nzero) to 0 (the split attention's counters of this call).
 hipError_t launch_qrot(const DecodePlan& p, const void* q, const void* P, float* qrot,
-                       uint16_t* qsplit, hipStream_t st);
+                       uint16_t* qsplit, hipStream_t st, uint32_t* zero = nullptr, int nzero = 0);
 // Scores from `src` = K_rot (ld = d) or a lead-dims copy K_lead (ld = R >= r).
 // With as_keys, `out` receives order-preserving keys and, when mm is not
 // null, mm[row][chunk] the min / max key of each of the NSC score chunks.
@@ -115,14 +121,15 @@ hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld
 hipError_t launch_decode_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
                               const void* Kx, const void* V, void* out, int32_t* idx, bool plain, hipStream_t st);
 // Selection and exact attention of each query head in one launch (bf16, d 64
-// or 128): one block per query head over its keys keys[row][0..S) (row
+// or 128): p.NSPL blocks per query head over its keys keys[row][0..S) (row
 // stride ldk, S <= 32768), or, with cidx, over its chunk winners
 // keys / cidx[row][0..S2) (row stride ldk); writes idx and out.  qsplit is
-// the exact stage's split query.
+// the exact stage's split query.  With p.NSPL > 1, part and cnt are the
+// plan's off_spart / off_scnt regions, cnt zero on entry (launch_qrot).
 bool select_attend_fits(const DecodePlan& p);
 hipError_t launch_select_attend(const DecodePlan& p, const uint32_t* keys, const int32_t* cidx, int ldk, int S2,
                                 const uint16_t* qsplit, const void* Kx, const void* V, void* out, int32_t* idx,
-                                hipStream_t st);
+                                float* part, uint32_t* cnt, hipStream_t st);
 // Long heads (bf16): fused scores + the first selection stage, one block per
 // (query head, chunk of kSelChunk tokens), into the candidate lists cidx /
 // ckey (ldc words per row); then launch_select_merge finishes the selection.
