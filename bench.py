@@ -80,6 +80,34 @@ def summarize_trace(db: str) -> str:
     return "\n".join(out)
 
 
+def trace_json(db: str) -> dict:
+    """Average duration per kernel (us) from a rocprofv3 kernel-trace database,
+    keyed by the kernel's name without its argument list, with the decode
+    sources' hash (the bench line uses it only while the sources match)."""
+    con = sqlite3.connect(db)
+    agg: dict = {}
+    for name, st, en in con.execute("select name, start, end from kernels").fetchall():
+        agg.setdefault(name.split("(")[0], []).append((en - st) / 1000.0)
+    return {"source_hash": kernel_source_hash(),
+            "kernels": {k: {"calls": len(v), "avg_us": sum(v) / len(v)} for k, v in agg.items()}}
+
+
+def load_trace_us(workload: str, kernel_name: str):
+    """The committed kernel trace's average duration (us) of `kernel_name`, or
+    None when absent or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"trace_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    for key, v in t.get("kernels", {}).items():
+        if key.split("<")[0].endswith(kernel_name):
+            return v["avg_us"]
+    return None
+
+
 def _pmc(db: str, counter: str) -> dict:
     con = sqlite3.connect(db)
     rows = con.execute("select kernel_name, grid_size, value from counters_collection where counter_name=?",
@@ -445,11 +473,17 @@ def run(args) -> dict:
     dom_kernel = {"scores": score_stage_kernel(cfg), "attend": "attend_mfma_kernel"}[dom]
     achieved = per_kernel_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = load_traffic(args.workload, dom_kernel)
+    trace_us = None if args.ragged else load_trace_us(args.workload, dom_kernel)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic, 0),
                 "kernel": dom_kernel, "alg_bytes_per_launch": per_kernel_bytes[dom],
-                "avg_launch_us": round(stage_us[dom], 2)}
+                "avg_launch_us": round(stage_us[dom], 2),
+                # the same kernel's average duration in the committed rocprofv3
+                # trace (no events around it), and the fraction it gives
+                "trace_avg_us": None if trace_us is None else round(trace_us, 2),
+                "frac_trace": None if trace_us is None else
+                round(per_kernel_bytes[dom] / (trace_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     step_gbs = by_step / (ms_per_step * 1e-3) / 1e9
     mem = memory_reference()
 
@@ -1073,10 +1107,14 @@ def main() -> int:
                     help="project: time the key projection instead (use --workload C5); "
                          "append: time one decode step's cache append")
     ap.add_argument("--summarize-trace", metavar="DB")
+    ap.add_argument("--trace-json", metavar="DB", help="per-kernel average durations of a trace as JSON")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DB", "WRITE_DB"))
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.trace_json:
+        print(json.dumps(trace_json(args.trace_json), indent=1))
         return 0
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc), indent=1))

@@ -89,9 +89,18 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
       __syncthreads();  // sh.red is read by every thread before select_regs reuses sh
       kmm = smm;
     }
+    // the list first holds the kept positions in the key row; for chunk
+    // winners they become tokens below, every lookup in flight at once
+    // (positions ascend with tokens: each chunk lists its winners in order)
     select_regs<kSaThreads, T>(key, lds, take, Sx, k, 2 * ((Sx + 63) / 64), reinterpret_cast<int32_t*>(list),
-                               nullptr, sh, MERGE ? cidx + (size_t)row * ldk : nullptr, nullptr, 0, kmm);
+                               nullptr, sh, nullptr, nullptr, 0, kmm);
     __syncthreads();  // the list is complete
+    if constexpr (MERGE) {
+      const int32_t* crow = cidx + (size_t)row * ldk;
+#pragma unroll 4
+      for (int jj = tid; jj < k; jj += kSaThreads) list[jj] = (uint32_t)crow[list[jj]];
+      __syncthreads();
+    }
     for (int jj = klo + tid; jj < khi; jj += kSaThreads) orow[jj] = (int32_t)list[jj];
     n = k;
   }
