@@ -192,3 +192,34 @@ def test_calibrate_full_c5_cache(gpu_lib):
     # separated by more than the conservative bound: at least r of the two
     # heads' columns are still pinned
     assert n >= cfg.r
+    # every head's leading r columns as a subspace (what the scores use: q
+    # P_r P_r^T k), with no column matching: by Ky Fan, the energy of the
+    # exact Gram C captured by an orthonormal r-frame is at most the sum of
+    # its r largest eigenvalues, with equality on the top-r subspace only.
+    # The GPU's frame solves C + E (||E||_2 <= e): it loses at most 2 r e,
+    # and its bf16 rounding (2^-9 per entry) a second-order r 2^-18 lambda_0
+    # (doubled below)
+    gamma = 512 * 2.0 ** -24
+    B, Hkv, S, d = K.shape
+    for kv in range(cfg.Hkv):
+        A = _rows(K, kv)
+        C = A.T @ A
+        lam = np.linalg.eigvalsh(C)[::-1]
+        absA = np.abs(A)
+        e = gamma * np.linalg.norm(absA.T @ absA) + 1e-12 * lam[0]
+        Q, _ = np.linalg.qr(Pd[kv][:, :cfg.r])
+        loss = lam[:cfg.r].sum() - np.trace(Q.T @ C @ Q)
+        assert -1e-9 * lam[0] <= loss <= 2 * cfg.r * e + cfg.r * 2.0 ** -17 * lam[0], (kv, loss / lam[0])
+
+
+def test_calibrate_full_c5_cache_f32(gpu_lib):
+    # the same cache's values in fp32 (exact copies of the bf16 keys): the
+    # fp64 Gram's bound is tight enough to pin every column of every head
+    # against the oracle, which fixes the eigensolver over the whole basis
+    cfg = CONFIGS["C5"]
+    K = make_inputs(cfg, need_K=True)["K"].float()
+    P_g, lam_g = gpu_lib.loki_calibrate_pca(dev(K))
+    torch.cuda.synchronize()
+    assert P_g.dtype == torch.float32
+    n = check_against_oracle(K, P_g, lam_g, "f32")
+    assert n == cfg.Hkv * cfg.d
