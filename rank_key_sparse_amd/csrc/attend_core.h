@@ -97,25 +97,31 @@ __device__ __forceinline__ void attend_list_core(const uint32_t* list, int n, co
     const bool kept = q4 < NH && p < n && ((ent >> (30 + (q4 & 1))) & 1u);
     const float e = kept ? sum_split_rows(sacc) * scale_log2 : -INFINITY;
     const float tm = row16_max(e);
+    // the hardware exp2 (no denormal results: a weight below 2^-126 of the
+    // running maximum's is 0, which the sums cannot tell apart)
     float c[NH];
+    bool grew = false;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const float nm = fmaxf(mr[h], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tm), 16 * h)));
-      c[h] = (nm == -INFINITY) ? 1.f : exp2f(mr[h] - nm);
+      c[h] = (nm == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mr[h] - nm);
+      grew = grew || nm != mr[h];
       mr[h] = nm;
     }
     const float mh = (NH == 1 || q4 == 0) ? mr[0] : mr[NH - 1];
-    const float w = kept ? exp2f(e - mh) : 0.f;
+    const float w = kept ? __builtin_amdgcn_exp2f(e - mh) : 0.f;
     lp = fmaf(lp, (NH == 1 || q4 == 0) ? c[0] : c[NH - 1], w);
     float wv[NH][VP];
 #pragma unroll
     for (int u = 0; u < VP; ++u)
 #pragma unroll
       for (int h = 0; h < NH; ++h) wv[h][u] = __shfl(w, 16 * h + RPW * u + lg);
+    if (grew) {  // uniform: the maxima are the same in every lane
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int h = 0; h < NH; ++h) acc[h][i] *= c[h];
+        for (int h = 0; h < NH; ++h) acc[h][i] *= c[h];
+    }
 #pragma unroll
     for (int u = 0; u < VP; ++u) {
       float x[8];
