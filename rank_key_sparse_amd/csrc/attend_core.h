@@ -4,7 +4,9 @@
 // select and attend in one launch.
 //
 // list[i] = token | kept-by-head-0 << 30 | kept-by-head-1 << 31, i < n, in
-// ascending token order (n >= 1).  Wave w takes 16-row tiles w + NWV j of the
+// ascending token order (n >= 1), followed by kListPad entries that hold a
+// valid token and no head bit (token 0): the tiles past the end read them
+// instead of clamping every index.  Wave w takes 16-row tiles w + NWV j of the
 // list in one pass, double buffered: for a tile, the K rows (MFMA B operand,
 // 64 contiguous bytes of each of 16 rows per load instruction) and the V rows
 // (16-byte granules, RL lanes per row) are requested together, one tile
@@ -38,6 +40,7 @@ __device__ __forceinline__ float row16_max(float v) {
 }
 
 constexpr uint32_t kListTok = 0x3fffffffu;  // token bits of a list entry
+constexpr int kListPad = 16;                 // entries after a list's end that the attention may read
 
 // LDS words of the merge scratch: s_acc [NWV][NH][D] then s_ml [NWV][4].
 template <int D, int NH, int NTHR>
@@ -67,13 +70,13 @@ __device__ __forceinline__ void attend_list_core(const uint32_t* list, int n, co
   const int lg = lane / RL, li = lane % RL;
   const int ntile = (n + 15) >> 4;
   auto load_tile = [&](int t, uint4 (&kb)[KSD], uint4 (&vb)[VP]) {
-    const uint32_t tk = list[min(16 * t + m, n - 1)] & kListTok;
+    const uint32_t tk = list[16 * t + m] & kListTok;  // t <= ntile - 1: within the padding
     const bf16_t* kr = Kx + (size_t)tk * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < KSD; ++s) kb[s] = ldg16(kr + 32 * s);
 #pragma unroll
     for (int u = 0; u < VP; ++u) {
-      const uint32_t tv = list[min(16 * t + RPW * u + lg, n - 1)] & kListTok;
+      const uint32_t tv = list[16 * t + RPW * u + lg] & kListTok;
       vb[u] = ldg16(V + (size_t)tv * D + 8 * li);
     }
   };
@@ -93,8 +96,8 @@ __device__ __forceinline__ void attend_list_core(const uint32_t* list, int n, co
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_rows(qx, 0, D, NH, D, m, 32 * s + 8 * q4), as_bf16x8(kb[s]),
                                                      sacc, 0, 0, 0);
     const int p = 16 * t + m;
-    const uint32_t ent = list[min(p, n - 1)];
-    const bool kept = q4 < NH && p < n && ((ent >> (30 + (q4 & 1))) & 1u);
+    const uint32_t ent = list[p];  // a padding entry keeps no head
+    const bool kept = q4 < NH && ((ent >> (30 + (q4 & 1))) & 1u);
     const float e = kept ? sum_split_rows(sacc) * scale_log2 : -INFINITY;
     const float tm = row16_max(e);
     // the hardware exp2 (no denormal results: a weight below 2^-126 of the

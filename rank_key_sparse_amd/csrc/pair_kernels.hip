@@ -264,7 +264,10 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       // <= 16384), scanned together
       int incl = c, incl01 = c0 | (c1 << 16);
       block_incl_scan2<kPairThreads>(incl, incl01, sh[0], sh[1]);
-      if (tid == kPairThreads - 1) s_n = incl;
+      if (tid == kPairThreads - 1) {
+        s_n = incl;
+        for (int j = 0; j < kListPad; ++j) list[incl + j] = 0u;  // the attention's padding
+      }
       int pos = incl - c, p0 = (incl01 & 0xffff) - c0, p1 = (incl01 >> 16) - c1;
       int32_t* const o0 = idx + row0 * k;
       int32_t* const o1 = idx + (row0 + 1) * k;
@@ -280,10 +283,10 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     }
     __syncthreads();
     // the attention itself (both heads, one pass over the list); its merge
-    // scratch follows the list (<= Sp entries) in the LDS that held the keys
+    // scratch follows the list (<= Sp entries and the padding) in the LDS that held the keys
     const size_t cb = (size_t)gi * Scap * D;  // this group's rows of K and V
     attend_list<D, 2, kPairThreads>(list, s_n, MODE == 2 ? sqp : sqs, Kx + cb, V + cb, scale_log2, out + row0 * D,
-                                    reinterpret_cast<float*>(lk + Sp));
+                                    reinterpret_cast<float*>(lk + Sp + kListPad));
   }
 }
 
@@ -302,7 +305,7 @@ static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, cons
   // keys [2][Sp] (then the union list, <= Sp entries, and the attention's
   // merge scratch), at least the rotation scratch [2 + 16][d] words
   const int merge = p.d == 64 ? attend_merge_words<64, 2, kPairThreads>() : attend_merge_words<128, 2, kPairThreads>();
-  const size_t lds = (size_t)max(max(2 * p.Sp, 18 * p.d), p.Sp + merge) * sizeof(uint32_t);
+  const size_t lds = (size_t)max(max(2 * p.Sp, 18 * p.d), p.Sp + kListPad + merge) * sizeof(uint32_t);
   const int ngroups = p.B * p.Hkv;
   const dim3 grid((unsigned)((ngroups + 7) / 8 * 8 * (p.G / 2))), block(kPairThreads);
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d));

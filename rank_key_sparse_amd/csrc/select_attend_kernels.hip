@@ -56,6 +56,9 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
   const int S = seq_len(lens, b, Scap);  // this head's tokens
   const int tid = threadIdx.x;
   int32_t* orow = idx + (size_t)row * k;
+  // the attention's padding after the list (k or S entries; written by no
+  // other step)
+  if (tid < kListPad) list[(k >= S ? S : k) + tid] = 0u;
   // this block's share of the idx row
   const int klo = (int)((long long)k * j / nspl), khi = (int)((long long)k * (j + 1) / nspl);
   int n;
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
   __syncthreads();
   const size_t cb = ((size_t)b * Hkv + kv) * Scap * D;
   const uint16_t* qx = qsplit + (size_t)row * 4 * D;
-  float* scratch = reinterpret_cast<float*>(list + k);  // n <= k entries precede it
+  float* scratch = reinterpret_cast<float*>(list + k + kListPad);  // n <= k entries and the padding precede it
   if (nspl == 1) {
     attend_list<D, 1, kSaThreads>(list, n, qx, Kx + cb, V + cb, scale_log2, out + (size_t)row * D, scratch);
     return;
@@ -199,7 +202,7 @@ hipError_t launch_select_attend(const DecodePlan& p, const uint32_t* keys, const
   if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.d));
   const int mw = p.d == 64 ? attend_merge_words<64, 1, kSaThreads>() : attend_merge_words<128, 1, kSaThreads>();
-  const size_t lds = (size_t)(p.k + mw) * sizeof(uint32_t);
+  const size_t lds = (size_t)(p.k + kListPad + mw) * sizeof(uint32_t);
   auto go = [&](auto tt, auto dd, auto mg) {
     constexpr int TT = decltype(tt)::value, D = decltype(dd)::value;
     constexpr bool MG = decltype(mg)::value;
