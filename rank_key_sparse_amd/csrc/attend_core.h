@@ -49,8 +49,11 @@ constexpr int attend_merge_words() {
 }
 
 // All NTHR threads of the block call it, after a barrier that completes the
-// list.  qx: the heads' split query rows in LDS or global memory, [NH][4][D]
-// (part 3 zero); Kx, V: this key/value head's rows [S][D]; scratch: LDS of
+// list.  qx: the heads' split query rows in LDS, part 3 zero: with one head,
+// the MFMA A rows [16][D] (rows 0..3 the head's parts, rows 4..15 zero, so
+// that every lane reads its row with no condition, and the reads leave the
+// tile loop); with two, [2][4][D] (read per tile, lanes past row 7 get zero:
+// two heads' accumulators leave no registers for the operands); Kx, V: this key/value head's rows [S][D]; scratch: LDS of
 // attend_merge_words() floats that no thread reads or writes meanwhile.
 // emit(h, c, M, L, A) receives, for head h and dim c, the block's running
 // max M (log2 units), weight sum L and weighted sum A of V[.][c]; every
@@ -93,8 +96,10 @@ __device__ __forceinline__ void attend_list_core(const uint32_t* list, int n, co
     floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSD; ++s)  // the A operands are read per tile (LDS), not held in registers
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q_rows(qx, 0, D, NH, D, m, 32 * s + 8 * q4), as_bf16x8(kb[s]),
-                                                     sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          NH == 1 ? as_bf16x8(*reinterpret_cast<const uint4*>(qx + m * D + 32 * s + 8 * q4))
+                  : q_rows(qx, 0, D, NH, D, m, 32 * s + 8 * q4),
+          as_bf16x8(kb[s]), sacc, 0, 0, 0);
     const int p = 16 * t + m;
     const uint32_t ent = list[p];  // a padding entry keeps no head
     const bool kept = q4 < NH && ((ent >> (30 + (q4 & 1))) & 1u);

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
   __shared__ SelScratch<kSaThreads> sh;
   __shared__ uint32_t smm[2];
   __shared__ uint32_t s_last;
+  __shared__ __align__(16) uint16_t sq[16 * D];  // the MFMA A rows: the head's split parts, then zeros
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int row = (slot / nspl) * 8 + xcd, j = slot - (slot / nspl) * nspl;
   if (row >= rows) return;  // padding block (uniform)
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
   const int tid = threadIdx.x;
   int32_t* orow = idx + (size_t)row * k;
   // the attention's padding after the list (k or S entries; written by no
-  // other step)
+  // other step) and its A rows (ordered before it by the barriers below)
   if (tid < kListPad) list[(k >= S ? S : k) + tid] = 0u;
+  for (int i = tid; i < 16 * D; i += kSaThreads) sq[i] = i < 4 * D ? qsplit[(size_t)row * 4 * D + i] : (uint16_t)0;
   // this block's share of the idx row
   const int klo = (int)((long long)k * j / nspl), khi = (int)((long long)k * (j + 1) / nspl);
   int n;
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
   for (int jj = a0 + tid; jj < a1; jj += kSaThreads) list[jj] |= 1u << 30;
   __syncthreads();
   const size_t cb = ((size_t)b * Hkv + kv) * Scap * D;
-  const uint16_t* qx = qsplit + (size_t)row * 4 * D;
+  const uint16_t* qx = sq;
   float* scratch = reinterpret_cast<float*>(list + k + kListPad);  // n <= k entries and the padding precede it
   if (nspl == 1) {
     attend_list<D, 1, kSaThreads>(list, n, qx, Kx + cb, V + cb, scale_log2, out + (size_t)row * D, scratch);
