@@ -49,6 +49,8 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
   __shared__ __align__(16) uint32_t sel[2][kNB];
   __shared__ __align__(16) uint32_t take[2][kFusedMaxS / 32];
+  // fused forms: the tokens at or above each head's estimated bin (below)
+  __shared__ __align__(16) uint32_t cand[MODE == 0 ? 1 : 2][MODE == 0 ? 1 : kFusedMaxS / 32];
   __shared__ SelScratch<kPairThreads> sh[2];
   __shared__ uint32_t smm[2][2];  // per head {min, max} key
   __shared__ __align__(16) uint16_t sqs[2 * 4 * D];  // the pair's split rows [h][part][d]
@@ -73,10 +75,18 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   // MFMA, tiles past S are dropped at the store.
   const bf16_t* base = src + (size_t)gi * Scap * ld;  // rows of the cache (capacity Scap)
   const int nbat = ((S + 15) / 16 + NWV * U - 1) / (NWV * U);
+  // The lane's first token (16 wave + m) is recomputed from the thread id
+  // (opaque) wherever the score phase needs it: a copy kept live from the
+  // top gets spilled, and reloading it waits for every load in flight.
+  auto lane_tok = [&]() {
+    const int tt = opaque(tid);
+    return 16 * (tt >> 6) + (tt & 15);
+  };
   auto load_batch = [&](int bi, uint4 (&a)[U][KS]) {
+    const int tl = lane_tok();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = min(16 * (wave + NWV * (bi * U + u)) + m, S - 1);
+      const int t = min(tl + 16 * NWV * (bi * U + u), S - 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[u][s] = ldg16(base + (size_t)t * ld + min(32 * s + 8 * q4, ld - 8));
     }
@@ -85,39 +95,65 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   // qrot_kernel (d / 8-term FMA chains over eight j-slices, added in slice
   // order): the split rows go to LDS as this block's A operands (MODE 0: q_rot
   // and its split also to the workspace for the attention kernels).  The P
-  // column slice and q are requested first, together, then the first K batch.
-  const int J = d / 8, pc = tid % d, js = tid / d;
-  bf16_t pv[16];  // P[kv][js J + jj][pc], J <= 16
-  {
-    const bf16_t* Pc = P + (size_t)kv * d * d + pc;
+  // slices and q are requested first, then the first K batch.  Thread
+  // js NC4 + c4 of the first 8 NC4 (whole waves) holds rows js J .. js J + J
+  // of columns 4 c4 .. 4 c4 + 3 (8-byte loads): a quarter of the block
+  // requests P, in a quarter of the load instructions that one column per
+  // thread would take (the CU's memory pipe then takes the key batch
+  // sooner); every column's chain is unchanged.
+  constexpr int J = D / 8, NC4 = D / 4;
+  const int c4 = tid % NC4, js = tid / NC4;
+  const bool ploader = __builtin_amdgcn_readfirstlane(tid >> 6) < 8 * NC4 / 64;  // uniform per wave
+  uint2 pv[J];  // P[kv][js J + jj][4 c4 .. 4 c4 + 3]
+  if (ploader) {
+    const bf16_t* Pc = P + (size_t)kv * d * d + (size_t)js * J * d + 4 * c4;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) pv[jj] = Pc[(size_t)min(js * J + jj, d - 1) * d];  // clamped: always in bounds
+    for (int jj = 0; jj < J; ++jj) pv[jj] = *reinterpret_cast<const uint2*>(Pc + (size_t)jj * d);
   }
   float* sq = reinterpret_cast<float*>(lk);  // [2][d]
   float* sred = sq + 2 * d;                  // [8][2][d]
-  if (tid < 2 * d) sq[tid] = to_f32(q[row0 * d + tid]);  // the pair's heads are adjacent rows
+  // the pair's heads are adjacent rows of q; the value goes to LDS after the
+  // first key batch is requested, so that waiting for it (in order) leaves
+  // the batch in flight
+  // (q reached through an opaque copy of the pointer and a compiler barrier,
+  // which keep its load above the batch's: no instruction is emitted)
+  const bf16_t* qp = q + row0 * d;
+  asm volatile("" : "+s"(qp));
+  using gbf16_t = const __attribute__((address_space(1))) bf16_t;  // a global-memory load, not a flat one
+  const bf16_t qv = ((gbf16_t*)qp)[min(tid, 2 * d - 1)];
+  asm volatile("" ::: "memory");
   uint4 a0[U][KS], a1[U][KS];
   load_batch(0, a0);  // in flight during the rotation (unused when every token is kept)
+  if (tid < 2 * d) sq[tid] = to_f32(qv);
   {
     __syncthreads();
-    if (js < 8) {
-      float r0 = 0.f, r1 = 0.f;
+    if (ploader) {
+      float r[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        if (jj < J) {
-          const int j = js * J + jj;
-          const float pj = to_f32(pv[jj]);
-          r0 = fmaf(sq[j], pj, r0);
-          r1 = fmaf(sq[d + j], pj, r1);
+      for (int jj = 0; jj < J; ++jj) {
+        const int j = js * J + jj;
+        const float q0 = sq[j], q1 = sq[d + j];
+        const float pj[4] = {__uint_as_float(pv[jj].x << 16), __uint_as_float(pv[jj].x & 0xffff0000u),
+                             __uint_as_float(pv[jj].y << 16), __uint_as_float(pv[jj].y & 0xffff0000u)};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          r[0][c] = fmaf(q0, pj[c], r[0][c]);
+          r[1][c] = fmaf(q1, pj[c], r[1][c]);
         }
       }
-      const int c = pc;
-      sred[(2 * js) * d + c] = r0;
-      sred[(2 * js + 1) * d + c] = r1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sred[(2 * js) * d + 4 * c4 + c] = r[0][c];
+        sred[(2 * js + 1) * d + 4 * c4 + c] = r[1][c];
+      }
     }
     __syncthreads();
-    if (tid < 2 * d) {
-      const int h = tid / d, cc = tid - h * d;
+    // the thread's row and column are recomputed here (opaque): a copy kept
+    // from the top would be spilled, and its reload would wait for every
+    // load in flight (the first key batch), not only for the rotation's
+    const int tr = opaque(tid);
+    if (tr < 2 * d) {
+      const int h = tr / d, cc = tr - h * d;
       float v = sred[h * d + cc];
       for (int t = 1; t < 8; ++t) v += sred[(2 * t + h) * d + cc];
       const bf16_t hi = f32_to_bf16(v);
@@ -134,7 +170,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       }
       if constexpr (MODE == 2) {
         // the query itself: a bf16 value is its own first split part
-        sqp[(h * 4) * d + cc] = q[row0 * d + tid];
+        sqp[(h * 4) * d + cc] = q[row0 * d + tr];
 #pragma unroll
         for (int pt = 1; pt < 4; ++pt) sqp[(h * 4 + pt) * d + cc] = 0;
       }
@@ -147,6 +183,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     keep_all<kPairThreads>(S, k, W, idx + (row0 + 1) * k, brow2[1]);
     if constexpr (MODE == 0) return;
   } else {
+    SelScratch<kPairThreads>* const sh2e[2] = {&sh[0], &sh[1]};
     // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
     bf16x8_t qa[KS];
 #pragma unroll
@@ -159,7 +196,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // threshold bin): the selection then needs no histogram pass of its own.
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     Binner bq;  // this lane's head's bins (set after the first batch)
+    int te = kNB;  // fused forms: this lane's head's estimated bin (set after the first two batches)
     auto score_batch = [&](int bi, const uint4 (&a)[U][KS], auto binning) {
+      const int tl = lane_tok();
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -168,12 +207,14 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
           const uint4 x = 32 * s + 8 * q4 < r ? a[u][s] : make_uint4(0u, 0u, 0u, 0u);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(x), acc, 0, 0, 0);
         }
-        const int t = 16 * (wave + NWV * (bi * U + u)) + m;  // this lane's token; its head is q4
+        const int t = tl + 16 * NWV * (bi * U + u);  // this lane's token; its head is q4
         if (q4 < 2 && t < S) {
           const float sc = sum_split_rows(acc);
           lk[q4 * Sp + t] = __float_as_uint(sc);  // the selection bins the value itself
           if constexpr (decltype(binning)::value) {
-            atomicAdd(&sel[q4][bq.of_score(sc)], 1u);
+            const int bn = bq.of_score(sc);
+            atomicAdd(&sel[q4][bn], 1u);
+            if (MODE != 0 && bn >= te) atomicOr(&cand[MODE == 0 ? 0 : q4][t >> 5], 1u << (t & 31));
           } else {
             const uint32_t key = score_key(sc);
             kmn = min(kmn, key);
@@ -185,6 +226,8 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // the histograms are cleared now, under the loads in flight
     for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
     for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
+    if constexpr (MODE != 0)
+      for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&cand[0][0])[i] = 0u;
     if (tid < 2) {
       smm[tid][0] = 0xffffffffu;
       smm[tid][1] = 0u;
@@ -194,6 +237,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // the first batch: its keys' range per head fixes the bins
     load_batch(1, a1);
     score_batch(0, a0, std::false_type{});
+    load_batch(2, a0);
 #pragma unroll
     for (int x = 1; x < 16; x <<= 1) {  // over the 16 lanes of a head's row
       kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, x));
@@ -205,30 +249,60 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     }
     __syncthreads();
     bq.init(smm[q4 & 1][0], smm[q4 & 1][1]);
+    // this lane's first token, recomputed (opaque) for the read-back passes
+    // below: a reload of a spilled copy would wait for the batches in flight
+    const int tok_l = lane_tok();
 #pragma unroll
     for (int u = 0; u < U; ++u) {  // the first batch's keys, read back
-      const int t = 16 * (wave + NWV * u) + m;
+      const int t = tok_l + 16 * NWV * u;
       if (q4 < 2 && t < S) atomicAdd(&sel[q4][bq.of_score(__uint_as_float(lk[q4 * Sp + t]))], 1u);
     }
-    load_batch(2, a0);
-    // batch bi is in a1 and bi + 1 in a0 at the top of each step; the steady
+    // the second batch (a1): counted, not yet marked (te is past every bin);
+    // the fourth is requested before the estimate's barriers
+    score_batch(1, a1, std::true_type{});
+    load_batch(3, a1);
+    // Fused forms: a lower bound on each head's final threshold bin, so that
+    // the selection visits only the tokens at or above it.  The first two
+    // batches (the first n0 tokens) hold about k n0 / S of the head's k best;
+    // the bin of their want-th largest key, want a quarter above that plus
+    // 32, is then at or below the final threshold bin unless the best tokens
+    // crowd the start of the sequence (then the selection falls back to the
+    // full passes: the estimate only decides which tokens are marked, never
+    // the result).  Computed while the next two batches are in flight.
+    int te0 = 0, te1 = 0;
+    if constexpr (MODE != 0) {
+      __syncthreads();  // the first two batches' counts are complete
+      const int n0 = min(S, 2 * 16 * NWV * U);
+      const int want = (int)min((long long)n0, (5LL * k * n0 + 4LL * S - 1) / (4LL * S) + 32);
+      find_thresholds2<kPairThreads>(sel[0], sel[1], want, want, sh2e);
+      te0 = sh[0].t;
+      te1 = sh[1].t;
+      te = (q4 & 1) ? te1 : te0;
+#pragma unroll
+      for (int u = 0; u < 2 * U; ++u) {  // the first two batches' tokens at or above the estimate
+        const int t = tok_l + 16 * NWV * u;
+        if (q4 < 2 && t < S && bq.of_score(__uint_as_float(lk[q4 * Sp + t])) >= te)
+          atomicOr(&cand[MODE == 0 ? 0 : q4][t >> 5], 1u << (t & 31));
+      }
+    }
+    // batch bi is in a0 and bi + 1 in a1 at the top of each step; the steady
     // loop only requests batches that exist, and the last one to three are
     // scored after it, so that no load is left in flight past the scores
-    // (batches past the end, here and for nbat <= 2, score no token)
-    int bi = 1;
+    // (batches past the end, here and for nbat <= 4, score no token)
+    int bi = 2;
     for (; bi + 3 < nbat; bi += 2) {
-      score_batch(bi, a1, std::true_type{});
-      load_batch(bi + 2, a1);
-      score_batch(bi + 1, a0, std::true_type{});
-      load_batch(bi + 3, a0);
+      score_batch(bi, a0, std::true_type{});
+      load_batch(bi + 2, a0);
+      score_batch(bi + 1, a1, std::true_type{});
+      load_batch(bi + 3, a1);
     }
-    score_batch(bi, a1, std::true_type{});
+    score_batch(bi, a0, std::true_type{});
     if (bi + 2 < nbat) {  // uniform
-      load_batch(bi + 2, a1);
-      score_batch(bi + 1, a0, std::true_type{});
-      score_batch(bi + 2, a1, std::true_type{});
+      load_batch(bi + 2, a0);
+      score_batch(bi + 1, a1, std::true_type{});
+      score_batch(bi + 2, a0, std::true_type{});
     } else {
-      score_batch(bi + 1, a0, std::true_type{});
+      score_batch(bi + 1, a1, std::true_type{});
     }
     __syncthreads();  // every key and histogram count is in LDS
     const uint32_t* const key[2] = {lk, lk + Sp};  // the scores stay in LDS
@@ -237,8 +311,16 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
     SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
     const uint32_t* const kmm2[2] = {smm[0], smm[1]};
-    // the fused form writes idx itself while listing the kept tokens
-    select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2, true);
+    // the fused form writes idx itself while listing the kept tokens; it
+    // first tries the marked tokens only (the same result when the estimate
+    // holds)
+    bool done = false;
+    if constexpr (MODE != 0) {
+      const uint32_t* const cand2[2] = {cand[0], cand[MODE == 0 ? 0 : 1]};
+      done = select_cands2<kPairThreads>(key, lds2, take2, cand2, te0, te1, S, k, sh2, kmm2);
+    }
+    if (!done)  // uniform
+      select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2, true);
   }
   if constexpr (MODE != 0) {
     // ========================================================================

@@ -382,6 +382,41 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   }
 }
 
+// Both heads' threshold bins in one block scan of (count0 | count1 << 16)
+// from the top bin (each head holds fewer than 65536 keys): for head h the
+// bin holding its want_h-th largest key (1-based), with sh[h]->above the
+// count in higher bins and sh[h]->nt the count in that bin.  A head with
+// fewer than want_h keys in all gets bin 0.  Ends with a barrier, after
+// which the histograms may be overwritten.
+template <int NTHR>
+__device__ __forceinline__ void find_thresholds2(const uint32_t* hist0, const uint32_t* hist1, int want0, int want1,
+                                                 SelScratch<NTHR>* const (&sh)[2]) {
+  constexpr int BPT = kNB / NTHR;
+  const int top = kNB - 1 - BPT * (int)threadIdx.x;
+  int hv[2][BPT];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    hv[0][i] = (int)hist0[top - i];
+    hv[1][i] = (int)hist1[top - i];
+    mine += hv[0][i] | (hv[1][i] << 16);
+  }
+  const int above = block_incl_scan<NTHR>(mine, *sh[0]) - mine;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int want = h ? want1 : want0;
+    int a = (above >> (16 * h)) & 0xffff;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (a < want && a + hv[h][i] >= want) { sh[h]->t = top - i; sh[h]->above = a; sh[h]->nt = hv[h][i]; }
+      a += hv[h][i];
+    }
+    // the thread holding bin 0 (the last one) sees every count
+    if (threadIdx.x == NTHR - 1 && a < want) { sh[h]->t = 0; sh[h]->above = a - hv[h][BPT - 1]; sh[h]->nt = hv[h][BPT - 1]; }
+  }
+  __syncthreads();
+}
+
 // ============================================================================
 // Two heads at once (same S, k, W; the scores as raw fp32 bits in LDS,
 // sbits[h][token], read in the register layout of select_regs: bins come
@@ -434,29 +469,7 @@ __device__ __forceinline__ void select_regs2(const uint32_t* const (&sbits)[2], 
   if (!prebuilt) __syncthreads();  // uniform
 
   // threshold bins: one scan of (count0 | count1 << 16) from the top bin
-  {
-    constexpr int BPT = kNB / NTHR;
-    const int top = kNB - 1 - BPT * tid;
-    int hv[2][BPT];
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      hv[0][i] = (int)lds[0][top - i];
-      hv[1][i] = (int)lds[1][top - i];
-      mine += hv[0][i] | (hv[1][i] << 16);
-    }
-    const int above = block_incl_scan<NTHR>(mine, *sh[0]) - mine;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int a = (above >> (16 * h)) & 0xffff;
-#pragma unroll
-      for (int i = 0; i < BPT; ++i) {
-        if (a < k && a + hv[h][i] >= k) { sh[h]->t = top - i; sh[h]->above = a; sh[h]->nt = hv[h][i]; }
-        a += hv[h][i];
-      }
-    }
-    __syncthreads();  // ends every read of the histograms
-  }
+  find_thresholds2<NTHR>(lds[0], lds[1], k, k, sh);  // ends every read of the histograms
   int tb[2], need[2], nc[2];
   bool rank_path[2];
 #pragma unroll
@@ -580,6 +593,80 @@ __device__ __forceinline__ void select_regs2(const uint32_t* const (&sbits)[2], 
     const int st = wave * T + lane;
     if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow[h] + 2 * st) = make_uint2(klo[h], khi[h]);
   }
+}
+
+// ============================================================================
+// Two heads whose tokens at or above an estimated bin are already marked: a
+// caller that knows, for head h, a bin te[h] and has set bit t of cand[h] for
+// every token t whose bin is te[h] or higher (e.g. while the scores were
+// made, te[h] estimated from the first keys) lets the final passes visit only
+// those tokens instead of all S.  The result is select_regs2's: the same
+// histograms give the same threshold bin t_h, every token above it is kept,
+// and bin t_h's tokens (all marked, when te[h] <= t_h) are ranked exactly.
+// Scores in sbits[h][token] (fp32 bits), histograms in lds[h] over the bins
+// of kmm[h], take[h] zero and sh[h]->ccount 0 on entry.  Returns true with
+// take[h] = head h's kept-token bitmap (its ranking's bits ordered by the
+// caller's next barrier), or false, having changed nothing but sh[h]->t /
+// above / nt, when te[h] lies above t_h (the estimate missed) or bin t_h is
+// crowded (> kRankMax tokens): then the caller selects with select_regs2.
+// Uniform over the block.
+// ============================================================================
+template <int NTHR>
+__device__ __forceinline__ bool select_cands2(const uint32_t* const (&sbits)[2], uint32_t* const (&lds)[2],
+                                              uint32_t* const (&take)[2], const uint32_t* const (&cand)[2],
+                                              int te0, int te1, int S, int k, SelScratch<NTHR>* const (&sh)[2],
+                                              const uint32_t* const (&kmm)[2]) {
+  find_thresholds2<NTHR>(lds[0], lds[1], k, k, sh);  // ends every read of the histograms
+  int tb[2], need[2], nc[2];
+  bool ok = true;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    tb[h] = sh[h]->t;
+    need[h] = k - sh[h]->above;
+    nc[h] = sh[h]->nt;
+    ok = ok && tb[h] >= (h ? te1 : te0) && nc[h] <= kRankMax;
+  }
+  if (!ok) return false;
+  Binner bin[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) bin[h].init(kmm[h][0], kmm[h][1]);
+  // one bitmap word of one head per thread (2 ceil(S / 32) <= NTHR words for
+  // S <= 16 NTHR): the marked tokens above t_h set the kept word, those of
+  // bin t_h join the head's candidates in the space of its histogram
+  const int Wh = (S + 31) >> 5;
+  for (int i = threadIdx.x; i < 2 * Wh; i += NTHR) {
+    const int h = i >= Wh ? 1 : 0, w = i - h * Wh;
+    const Binner bh = h ? bin[1] : bin[0];
+    const int th = h ? tb[1] : tb[0];
+    const uint32_t* sb = h ? sbits[1] : sbits[0];
+    uint32_t* ck = h ? lds[1] : lds[0];
+    uint32_t c = h ? cand[1][w] : cand[0][w], word = 0u;
+    while (c) {
+      const int j = __ffs(c) - 1;
+      c &= c - 1u;
+      const int t = 32 * w + j;
+      const float sc = __uint_as_float(sb[t]);
+      const int b = bh.of_score(sc);
+      if (b > th) {
+        word |= 1u << j;
+      } else if (b == th) {
+        const int p = atomicAdd(&sh[h]->ccount, 1);
+        ck[p] = score_key(sc);
+        ck[kCap + p] = (uint32_t)t;
+      }
+    }
+    (h ? take[1] : take[0])[w] = word;
+  }
+  __syncthreads();
+  // the need best of each threshold bin (head h ranked by half h of the block)
+  static_assert(kRankMax <= NTHR / 2, "one thread per candidate");
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t* tk = take[h];
+    rank_candidates<NTHR / 2>(lds[h], lds[h] + kCap, nc[h], need[h],
+                              [&](uint32_t ii) { atomicOr(&tk[ii >> 5], 1u << (ii & 31)); }, h * (NTHR / 2));
+  }
+  return true;
 }
 
 // ============================================================================

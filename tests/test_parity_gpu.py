@@ -686,6 +686,31 @@ def test_pair_fused_rank_and_radix_heads(gpu_lib):
     assert np.array_equal(ig[:, 0::2], np.broadcast_to(np.arange(cfg.k), ig[:, 0::2].shape))
 
 
+@pytest.mark.parametrize("order", ["best_first", "best_last"])
+def test_pair_fused_score_order(gpu_lib, order):
+    # pair-fused path (512 grouped query heads).  The selection first estimates
+    # each head's threshold bin from the first 2048 tokens and visits only the
+    # tokens at or above it; here every group's rows are sorted by the scores
+    # of its first query head.  best_first: that head's best tokens fill the
+    # first batch, the estimate lies above the real threshold and the full
+    # selection runs; best_last: the first batch holds its worst tokens, so
+    # nearly every token is visited.  Either way the result is the oracle's
+    cfg = cfg_case("C3", S=4096, B=16)
+    x = dict(make_inputs(cfg))
+    _, s_o = oracle.select(x["q"], x["P"], x["K_rot"], cfg.r, cfg.k, return_scores=True)
+    G = cfg.Hq // cfg.Hkv
+    Kr, V = x["K_rot"].clone(), x["V"].clone()
+    for b in range(cfg.B):
+        for kv in range(cfg.Hkv):
+            s = s_o[b, kv * G]
+            perm = np.argsort(-s, kind="stable") if order == "best_first" else np.argsort(s, kind="stable")
+            perm = torch.from_numpy(perm.copy())
+            Kr[b, kv] = Kr[b, kv][perm]
+            V[b, kv] = V[b, kv][perm]
+    x["K_rot"], x["V"] = Kr, V
+    run_decode(gpu_lib, x, cfg.r, cfg.k, R=cfg.r)
+
+
 def test_decode_all_equal_keys_pair(gpu_lib):
     B, Hq, Hkv, S, d = 16, 32, 8, 2000, 128  # 512 grouped heads: pair-fused path
     Kr = torch.ones((B, Hkv, S, d), dtype=torch.bfloat16)
