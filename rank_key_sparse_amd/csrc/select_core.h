@@ -236,7 +236,10 @@ __device__ __forceinline__ void load_regs(const uint32_t* src, int S, uint32_t (
   for (int i = 0; i < T; ++i) key[i] = src[min(tok0 + 64 * i, S - 1)];
 }
 
-template <int NTHR, int T, bool KB = false>
+// LISTW: the kept positions are listed from the kept-position bitmap (one
+// block scan over its words, thread w listing word w) instead of lane by
+// lane from the step masks; okeys is then not written.
+template <int NTHR, int T, bool KB = false, bool LISTW = false>
 __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* lds, uint32_t* take,
                                             int S, int k, int W, int32_t* orow, uint32_t* brow,
                                             SelScratch<NTHR>& sh, const int32_t* map = nullptr,
@@ -357,6 +360,25 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
   }
 
   // 4. emit: lane i < T holds the kept mask of step wave * T + i
+  if constexpr (LISTW) {
+    static_assert(T <= 32, "one bitmap word per thread");
+    // each step's mask goes to take (its lane alone read those words above),
+    // then thread w lists word w (tokens 32 w ..) at its block-scan offset
+    {
+      const int st = wave * T + lane;
+      if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(take + 2 * st) = make_uint2(klo, khi);
+    }
+    __syncthreads();
+    const uint32_t wd = tid < W ? take[tid] : 0u;
+    const int c = __popc(wd);
+    int pos = block_incl_scan<NTHR>(c, sh) - c;
+    for (uint32_t u = wd; u; u &= u - 1u) {
+      const int t = 32 * tid + __ffs(u) - 1;
+      orow[pos++] = map ? map[t] : t + tok_base;
+    }
+    if (brow && tid < W) brow[tid] = wd;
+    return;
+  }
   const int cnt = (lane < T) ? __popc(klo) + __popc(khi) : 0;
   const int incl = wave_incl_scan(cnt);
   if (lane == 63) sh.wsel[wave] = incl;
