@@ -106,13 +106,8 @@ hipError_t launch_scores_mfma(const DecodePlan& p, const void* src, int ld, cons
 size_t score_select_lds_bytes(int Sp);
 hipError_t launch_score_select(const DecodePlan& p, const void* src, int ld, const uint16_t* qsplit,
                                int32_t* idx, uint32_t* bitmap, hipStream_t st);
-// Fused scores + top-k for pairs of heads of a group (bf16, G even, S <= kFusedMaxS).
+// Pairs of heads of a group in one kernel (bf16, G even, S <= kFusedMaxS).
 bool score_select_pair_fits(const DecodePlan& p);
-// The pair kernel also rotates its two query heads (q_rot and the split to
-// the workspace), so no rotation kernel runs before it.
-hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
-                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
-                                    hipStream_t st);
 // The whole decode of pairs of heads of a group in one launch (bf16, G even,
 // S <= kFusedMaxS, d 64 or 128): rotation, scores, selection into idx, and
 // the exact attention of both heads over their kept tokens into out.  With

@@ -28,29 +28,27 @@ namespace loki {
 // group get block ids with the same value mod 8 (one XCD) and consecutive
 // dispatch order, so their reads of the group's source share L2.
 //
-// MODE 0: the selection's kept-token bitmaps, q_rot and its split go to the
-//         workspace for the separate attention kernels.
-// MODE 1: the fused decode.  The bitmaps stay in LDS; the block lists the
-//         union of the pair's kept tokens in ascending order and runs the
-//         exact attention of both heads over it (section below), writing
-//         the pair's outputs.  Nothing else goes to global memory but idx.
-// MODE 2: MODE 1 with the exact stage taken by the query itself against
-//         unrotated keys (the asymmetric index: the scores used q A).
+// The kept-token bitmaps stay in LDS; the block lists the union of the
+// pair's kept tokens in ascending order and runs the exact attention of both
+// heads over it (section below), writing the pair's outputs.  Nothing else
+// goes to global memory but idx.
+// MODE 1: the exact stage takes q_rot against the rotated keys.
+// MODE 2: the exact stage takes the query itself against unrotated keys (the
+//         asymmetric index: the scores used q A).
 // ============================================================================
 template <int KS, int U, int D, int MODE>
 __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
-    const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P,
-    float* __restrict__ qrot, uint16_t* __restrict__ qsplit, int B, int Hq, int Hkv, int Scap, int Sp, int r,
-    int k, int W, int32_t* __restrict__ idx, uint32_t* __restrict__ bitmap, const bf16_t* __restrict__ Kx,
+    const bf16_t* __restrict__ src, int ld, const bf16_t* __restrict__ q, const bf16_t* __restrict__ P, int B,
+    int Hq, int Hkv, int Scap, int Sp, int r, int k, int W, int32_t* __restrict__ idx, const bf16_t* __restrict__ Kx,
     const bf16_t* __restrict__ V, bf16_t* __restrict__ out, float scale_log2, const int32_t* __restrict__ lens) {
+  static_assert(MODE == 1 || MODE == 2, "exact stage on q_rot or on the query itself");
   constexpr int NWV = kPairThreads / 64;
   constexpr int T = kFusedMaxS / kPairThreads;  // keys per lane in the selection
   constexpr int d = D;
   extern __shared__ __align__(16) uint32_t lk[];  // [2][Sp] fp32 score bits (first: rotation scratch)
   __shared__ __align__(16) uint32_t sel[2][kNB];
   __shared__ __align__(16) uint32_t take[2][kFusedMaxS / 32];
-  // fused forms: the tokens at or above each head's estimated bin (below)
-  __shared__ __align__(16) uint32_t cand[MODE == 0 ? 1 : 2][MODE == 0 ? 1 : kFusedMaxS / 32];
+  __shared__ __align__(16) uint32_t cand[2][kFusedMaxS / 32];  // tokens at or above each head's estimated bin
   __shared__ SelScratch<kPairThreads> sh[2];
   __shared__ uint32_t smm[2][2];  // per head {min, max} key
   __shared__ __align__(16) uint16_t sqs[2 * 4 * D];  // the pair's split rows [h][part][d]
@@ -63,10 +61,9 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   const int b = gi / Hkv, kv = gi - b * Hkv;
   const int S = seq_len(lens, b, Scap);  // this sequence's tokens
   const size_t row0 = (size_t)b * Hq + (size_t)kv * G + 2 * gp;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int m = lane & 15, q4 = lane >> 4;
-  uint32_t* const brow2[2] = {MODE == 0 ? bitmap + row0 * W : take[0],
-                              MODE == 0 ? bitmap + (row0 + 1) * W : take[1]};
+  uint32_t* const brow2[2] = {take[0], take[1]};
 
   // Wave w takes tiles w + NWV i (16 tokens each) in batches of U, double
   // buffered: the next batch is in flight while this one is multiplied.
@@ -93,8 +90,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   };
   // the pair's query rotation q_rot = q P[kv], with the arithmetic of
   // qrot_kernel (d / 8-term FMA chains over eight j-slices, added in slice
-  // order): the split rows go to LDS as this block's A operands (MODE 0: q_rot
-  // and its split also to the workspace for the attention kernels).  The P
+  // order): the split rows go to LDS as this block's A operands.  The P
   // slices and q are requested first, then the first K batch.  Thread
   // js NC4 + c4 of the first 8 NC4 (whole waves) holds rows js J .. js J + J
   // of columns 4 c4 .. 4 c4 + 3 (8-byte loads): a quarter of the block
@@ -163,11 +159,6 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       const bf16_t part[4] = {hi, mid, lo, 0};
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) sqs[(h * 4 + pt) * d + cc] = part[pt];
-      if constexpr (MODE == 0) {
-        qrot[(row0 + h) * d + cc] = v;
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) qsplit[((row0 + h) * 4 + pt) * d + cc] = part[pt];
-      }
       if constexpr (MODE == 2) {
         // the query itself: a bf16 value is its own first split part
         sqp[(h * 4) * d + cc] = q[row0 * d + tr];
@@ -181,7 +172,6 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
   if (k >= S) {
     keep_all<kPairThreads>(S, k, W, idx + row0 * k, brow2[0]);
     keep_all<kPairThreads>(S, k, W, idx + (row0 + 1) * k, brow2[1]);
-    if constexpr (MODE == 0) return;
   } else {
     SelScratch<kPairThreads>* const sh2e[2] = {&sh[0], &sh[1]};
     // A operands: the pair's two heads in rows 0..7 (row 4 h + split)
@@ -214,7 +204,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
           if constexpr (decltype(binning)::value) {
             const int bn = bq.of_score(sc);
             atomicAdd(&sel[q4][bn], 1u);
-            if (MODE != 0 && bn >= te) atomicOr(&cand[MODE == 0 ? 0 : q4][t >> 5], 1u << (t & 31));
+            if (bn >= te) atomicOr(&cand[q4][t >> 5], 1u << (t & 31));
           } else {
             const uint32_t key = score_key(sc);
             kmn = min(kmn, key);
@@ -226,8 +216,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // the histograms are cleared now, under the loads in flight
     for (int i = tid; i < 2 * kNB; i += kPairThreads) (&sel[0][0])[i] = 0u;
     for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&take[0][0])[i] = 0u;
-    if constexpr (MODE != 0)
-      for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&cand[0][0])[i] = 0u;
+    for (int i = tid; i < 2 * (kFusedMaxS / 32); i += kPairThreads) (&cand[0][0])[i] = 0u;
     if (tid < 2) {
       smm[tid][0] = 0xffffffffu;
       smm[tid][1] = 0u;
@@ -270,7 +259,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // full passes: the estimate only decides which tokens are marked, never
     // the result).  Computed while the next two batches are in flight.
     int te0 = 0, te1 = 0;
-    if constexpr (MODE != 0) {
+    {
       __syncthreads();  // the first two batches' counts are complete
       const int n0 = min(S, 2 * 16 * NWV * U);
       const int want = (int)min((long long)n0, (5LL * k * n0 + 4LL * S - 1) / (4LL * S) + 32);
@@ -282,7 +271,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
       for (int u = 0; u < 2 * U; ++u) {  // the first two batches' tokens at or above the estimate
         const int t = tok_l + 16 * NWV * u;
         if (q4 < 2 && t < S && bq.of_score(__uint_as_float(lk[q4 * Sp + t])) >= te)
-          atomicOr(&cand[MODE == 0 ? 0 : q4][t >> 5], 1u << (t & 31));
+          atomicOr(&cand[q4][t >> 5], 1u << (t & 31));
       }
     }
     // batch bi is in a0 and bi + 1 in a1 at the top of each step; the steady
@@ -308,21 +297,16 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     const uint32_t* const key[2] = {lk, lk + Sp};  // the scores stay in LDS
     uint32_t* const lds2[2] = {sel[0], sel[1]};
     uint32_t* const take2[2] = {take[0], take[1]};
-    int32_t* const orow2[2] = {idx + row0 * k, idx + (row0 + 1) * k};
     SelScratch<kPairThreads>* const sh2[2] = {&sh[0], &sh[1]};
     const uint32_t* const kmm2[2] = {smm[0], smm[1]};
-    // the fused form writes idx itself while listing the kept tokens; it
-    // first tries the marked tokens only (the same result when the estimate
-    // holds)
-    bool done = false;
-    if constexpr (MODE != 0) {
-      const uint32_t* const cand2[2] = {cand[0], cand[MODE == 0 ? 0 : 1]};
-      done = select_cands2<kPairThreads>(key, lds2, take2, cand2, te0, te1, S, k, sh2, kmm2);
-    }
-    if (!done)  // uniform
-      select_regs2<kPairThreads, T, MODE == 0>(key, lds2, take2, S, k, W, orow2, brow2, sh2, kmm2, true);
+    // the selection leaves the kept-token bitmaps in take (idx is written
+    // while the kept tokens are listed below); it first tries the marked
+    // tokens only (the same result when the estimate holds)
+    const uint32_t* const cand2[2] = {cand[0], cand[1]};
+    if (!select_cands2<kPairThreads>(key, lds2, take2, cand2, te0, te1, S, k, sh2, kmm2))  // uniform
+      select_regs2<kPairThreads, T>(key, lds2, take2, S, k, W, brow2, sh2, kmm2, true);
   }
-  if constexpr (MODE != 0) {
+  {
     // ========================================================================
     // Exact attention of the pair's two heads over their kept tokens.  The
     // union of the two kept sets is listed in ascending token order (entry =
@@ -381,8 +365,7 @@ bool score_select_pair_fits(const DecodePlan& p) {
 
 template <int MODE>
 static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
-                              float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap, const void* Kx,
-                              const void* V, void* out, hipStream_t st) {
+                              int32_t* idx, const void* Kx, const void* V, void* out, hipStream_t st) {
   if (!score_select_pair_fits(p)) return hipErrorInvalidValue;
   // keys [2][Sp] (then the union list, <= Sp entries, and the attention's
   // merge scratch), at least the rotation scratch [2 + 16][d] words
@@ -399,8 +382,8 @@ static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, cons
     hipError_t e = ensure_dynamic_lds(fn, (int)max(lds, (size_t)2 * kFusedMaxS * sizeof(uint32_t)));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((score_select_pair_kernel<K, 8 / K, D, MODE>), grid, block, lds, st, s, ld,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), qrot, qsplit, p.B, p.Hq,
-                       p.Hkv, p.S, p.Sp, p.r, p.k, p.W, idx, bitmap, static_cast<const bf16_t*>(Kx),
+                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(P), p.B, p.Hq, p.Hkv, p.S, p.Sp,
+                       p.r, p.k, p.W, idx, static_cast<const bf16_t*>(Kx),
                        static_cast<const bf16_t*>(V), static_cast<bf16_t*>(out), scale_log2, p.lens);
     return hipGetLastError();
   };
@@ -416,16 +399,10 @@ static hipError_t launch_pair(const DecodePlan& p, const void* src, int ld, cons
   }
 }
 
-hipError_t launch_score_select_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
-                                    float* qrot, uint16_t* qsplit, int32_t* idx, uint32_t* bitmap,
-                                    hipStream_t st) {
-  return launch_pair<0>(p, src, ld, q, P, qrot, qsplit, idx, bitmap, nullptr, nullptr, nullptr, st);
-}
-
 hipError_t launch_decode_pair(const DecodePlan& p, const void* src, int ld, const void* q, const void* P,
                               const void* Kx, const void* V, void* out, int32_t* idx, bool plain, hipStream_t st) {
-  return plain ? launch_pair<2>(p, src, ld, q, P, nullptr, nullptr, idx, nullptr, Kx, V, out, st)
-               : launch_pair<1>(p, src, ld, q, P, nullptr, nullptr, idx, nullptr, Kx, V, out, st);
+  return plain ? launch_pair<2>(p, src, ld, q, P, idx, Kx, V, out, st)
+               : launch_pair<1>(p, src, ld, q, P, idx, Kx, V, out, st);
 }
 
 }  // namespace loki

@@ -455,14 +455,13 @@ __device__ __forceinline__ void find_thresholds2(const uint32_t* hist0, const ui
 // range, e.g. of the first keys made; keys outside it fall into the end
 // bins, which keeps the map monotone, so the selection stays exact: only the
 // threshold bin's size depends on the range).  lds[h] / take[h] / sh[h] are
-// separate per head.  Output per head as for select_regs (no map / okeys);
-// without EMIT only the kept-token bitmaps brow[h] are written (a caller
-// that lists the kept tokens itself) and orow is not used.
+// separate per head.  Output: head h's kept-token bitmap in brow[h] (W words;
+// the caller lists the kept tokens itself).
 // ============================================================================
-template <int NTHR, int T, bool EMIT = true>
+template <int NTHR, int T>
 __device__ __forceinline__ void select_regs2(const uint32_t* const (&sbits)[2], uint32_t* const (&lds)[2],
                                              uint32_t* const (&take)[2], int S, int k, int W,
-                                             int32_t* const (&orow)[2], uint32_t* const (&brow)[2],
+                                             uint32_t* const (&brow)[2],
                                              SelScratch<NTHR>* const (&sh)[2],
                                              const uint32_t* const (&kmm)[2], bool prebuilt = false) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -588,33 +587,11 @@ __device__ __forceinline__ void select_regs2(const uint32_t* const (&sbits)[2], 
     }
   }
 
-  // 4. emit both heads: one scan of (count0 | count1 << 16)
-  if constexpr (!EMIT) {
-    const int st = wave * T + lane;
+  // 4. each step's kept mask to head h's bitmap
+  const int st = wave * T + lane;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow[h] + 2 * st) = make_uint2(klo[h], khi[h]);
-    return;
-  }
-  const int cnt = (lane < T) ? ((__popc(klo[0]) + __popc(khi[0])) | ((__popc(klo[1]) + __popc(khi[1])) << 16)) : 0;
-  const int incl = wave_incl_scan(cnt);
-  if (lane == 63) sh[0]->wsel[wave] = incl;
-  __syncthreads();  // also: every read of lds / take above is done
-  const int offp = waves_below<NTHR>(sh[0]->wsel) + incl - cnt;
-  const int t0 = opaque(regs_tok0<T>());
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int off = (offp >> (16 * h)) & 0xffff;
-#pragma unroll
-    for (int i = 0; i < T; ++i) {
-      const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi[h], i) << 32) |
-                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)klo[h], i);
-      const int o = __builtin_amdgcn_readlane(off, i);
-      if ((f >> lane) & 1ull) orow[h][o + bits_below(f)] = t0 + 64 * i;
-    }
-    const int st = wave * T + lane;
+  for (int h = 0; h < 2; ++h)
     if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow[h] + 2 * st) = make_uint2(klo[h], khi[h]);
-  }
 }
 
 // ============================================================================
