@@ -2,7 +2,7 @@
 // head's keys fit in LDS): one block of 1024 threads per pair of query heads
 // of a (b, kv) group rotates the pair's queries, scores every cached token
 // for both heads from one read of the group's score source, selects each
-// head's k best tokens and, in the fused form, runs the exact attention of
+// head's k best tokens and runs the exact attention of
 // both heads over their kept tokens and writes the outputs: the whole decode
 // step of the pair in one launch.
 #include <hip/hip_runtime.h>
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // threshold bin): the selection then needs no histogram pass of its own.
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     Binner bq;  // this lane's head's bins (set after the first batch)
-    int te = kNB;  // fused forms: this lane's head's estimated bin (set after the first two batches)
+    int te = kNB;  // this lane's head's estimated bin (set after the first two batches)
     auto score_batch = [&](int bi, const uint4 (&a)[U][KS], auto binning) {
       const int tl = lane_tok();
 #pragma unroll
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kPairThreads, 4) void score_select_pair_kernel(
     // the fourth is requested before the estimate's barriers
     score_batch(1, a1, std::true_type{});
     load_batch(3, a1);
-    // Fused forms: a lower bound on each head's final threshold bin, so that
+    // A lower bound on each head's final threshold bin, so that
     // the selection visits only the tokens at or above it.  The first two
     // batches (the first n0 tokens) hold about k n0 / S of the head's k best;
     // the bin of their want-th largest key, want a quarter above that plus
