@@ -413,7 +413,9 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_kernel(const uint32_
   }
   uint32_t key[T];
   load_regs<T>(rk, L, key);
-  select_regs<kSelThreads, T>(key, lds, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base);
+  // the winners' keys are read back from the chunk's row while they are listed
+  select_regs<kSelThreads, T>(key, lds, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base, nullptr,
+                              rk);
 }
 
 template <int T>

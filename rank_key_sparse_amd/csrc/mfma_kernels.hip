@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kChunkThreads) void score_select_chunk_kernel(
   }
   uint32_t key[T];  // the selection's register layout
   load_regs<T>(lk, L, key);
-  select_regs<kChunkThreads, T>(key, sel, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base);
+  // the winners' keys are read back from lk while they are listed
+  select_regs<kChunkThreads, T>(key, sel, take, L, k, 2 * ((L + 63) / 64), oi, nullptr, sh, nullptr, ok, base,
+                                nullptr, lk);
 }
 
 // ============================================================================

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kSaThreads, 4) void select_attend_kernel(
     // the list first holds the kept positions in the key row; for chunk
     // winners they become tokens below, every lookup in flight at once
     // (positions ascend with tokens: each chunk lists its winners in order)
-    select_regs<kSaThreads, T, false, true>(key, lds, take, Sx, k, 2 * ((Sx + 63) / 64),
+    select_regs<kSaThreads, T>(key, lds, take, Sx, k, 2 * ((Sx + 63) / 64),
                                             reinterpret_cast<int32_t*>(list), nullptr, sh, nullptr, nullptr, 0, kmm);
     __syncthreads();  // the list is complete
     if constexpr (MERGE) {

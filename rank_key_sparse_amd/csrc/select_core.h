@@ -13,8 +13,8 @@
 //    select inside bin t finds the k-th key K* and its tie quota, and a pass
 //    in index order takes key > K* and the first `quota` keys equal to K*
 //    (lower index wins);
-// 4. emit kept = above | taken: per-step counts, a block prefix, indices
-//    compacted in ascending order, and the kept-token bitmap words.
+// 4. emit kept = above | taken: the kept-token bitmap words, then per-word
+//    counts, a block prefix and the indices listed in ascending order.
 //
 // Two forms.  select_regs: the head's keys sit in registers (lane l of wave
 // w holds tokens w*64T + 64i + l, i < T), so every pass is a register pass
@@ -208,7 +208,8 @@ __device__ __forceinline__ void rank_candidates(const uint32_t* ck, const uint32
 // threads of the block call it.
 // Output: orow[0..k) = the kept positions p, ascending, written as map[p]
 // when map is given, else as p + tok_base; with okeys, okeys[i] receives the
-// key of orow[i]; with brow, the kept-position bitmap (W words).
+// key of orow[i], read from lkeys[p]; with brow, the kept-position bitmap (W
+// words).  The block's take holds at least W words.
 // kmm: when given, {min, max} of the keys (e.g. gathered while the keys were
 // made), readable by every thread after one barrier; the min / max pass is
 // then skipped.  KB: keep each key's bin in registers from the histogram to
@@ -236,15 +237,17 @@ __device__ __forceinline__ void load_regs(const uint32_t* src, int S, uint32_t (
   for (int i = 0; i < T; ++i) key[i] = src[min(tok0 + 64 * i, S - 1)];
 }
 
-// LISTW: the kept positions are listed from the kept-position bitmap (one
-// block scan over its words, thread w listing word w) instead of lane by
-// lane from the step masks; okeys is then not written.
-template <int NTHR, int T, bool KB = false, bool LISTW = false>
+// The kept positions are listed from the kept-position bitmap: each step's
+// mask is stored by its lane, then one block scan over the bitmap words
+// (each thread a contiguous run of them) gives every thread its offset.
+// okeys[i], when wanted, is read from lkeys (the keys by position, in LDS or
+// global memory).
+template <int NTHR, int T, bool KB = false>
 __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* lds, uint32_t* take,
                                             int S, int k, int W, int32_t* orow, uint32_t* brow,
                                             SelScratch<NTHR>& sh, const int32_t* map = nullptr,
                                             uint32_t* okeys = nullptr, int tok_base = 0,
-                                            const uint32_t* kmm = nullptr) {
+                                            const uint32_t* kmm = nullptr, const uint32_t* lkeys = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t* hist = lds;
 
@@ -359,48 +362,26 @@ __device__ __forceinline__ void select_regs(const uint32_t (&key)[T], uint32_t* 
     }
   }
 
-  // 4. emit: lane i < T holds the kept mask of step wave * T + i
-  if constexpr (LISTW) {
-    static_assert(T <= 32, "one bitmap word per thread");
-    // each step's mask goes to take (its lane alone read those words above),
-    // then thread w lists word w (tokens 32 w ..) at its block-scan offset
-    {
-      const int st = wave * T + lane;
-      if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(take + 2 * st) = make_uint2(klo, khi);
-    }
-    __syncthreads();
-    const uint32_t wd = tid < W ? take[tid] : 0u;
-    const int c = __popc(wd);
-    int pos = block_incl_scan<NTHR>(c, sh) - c;
-    for (uint32_t u = wd; u; u &= u - 1u) {
-      const int t = 32 * tid + __ffs(u) - 1;
-      orow[pos++] = map ? map[t] : t + tok_base;
-    }
-    if (brow && tid < W) brow[tid] = wd;
-    return;
-  }
-  const int cnt = (lane < T) ? __popc(klo) + __popc(khi) : 0;
-  const int incl = wave_incl_scan(cnt);
-  if (lane == 63) sh.wsel[wave] = incl;
-  __syncthreads();  // also: every read of lds / take above is done
-  const int off = waves_below<NTHR>(sh.wsel) + incl - cnt;
+  // 4. emit: lane i < T holds the kept mask of step wave * T + i; it goes
+  // to take (its lane alone read those words above), then thread t lists
+  // words t R .. t R + R - 1 (tokens 32 w ..) at its block-scan offset
   {
-    const int t0 = opaque(regs_tok0<T>());
-#pragma unroll
-    for (int i = 0; i < T; ++i) {
-      const uint64_t f = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, i) << 32) |
-                         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)klo, i);
-      const int o = __builtin_amdgcn_readlane(off, i);
-      if ((f >> lane) & 1ull) {
-        const int pos = o + bits_below(f), t = t0 + 64 * i;
-        orow[pos] = map ? map[t] : t + tok_base;
-        if (okeys) okeys[pos] = key[i];
-      }
-    }
-  }
-  if (brow) {
     const int st = wave * T + lane;
-    if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(brow + 2 * st) = make_uint2(klo, khi);
+    if (lane < T && 2 * st < W) *reinterpret_cast<uint2*>(take + 2 * st) = make_uint2(klo, khi);
+  }
+  __syncthreads();
+  const int R = (W + NTHR - 1) / NTHR, w0 = tid * R, w1 = min(w0 + R, W);
+  int c = 0;
+  for (int w = w0; w < w1; ++w) c += __popc(take[w]);
+  int pos = block_incl_scan<NTHR>(c, sh) - c;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t wd = take[w];
+    for (uint32_t u = wd; u; u &= u - 1u, ++pos) {
+      const int t = 32 * w + __ffs(u) - 1;
+      orow[pos] = map ? map[t] : t + tok_base;
+      if (okeys) okeys[pos] = lkeys[t];
+    }
+    if (brow) brow[w] = wd;
   }
 }
 
