@@ -853,7 +853,10 @@ def run_asym(args) -> dict:
     by_gather = U * cfg.d * 2 * e
     by_step = by_scores + by_gather + cfg.Hkv * cfg.d * cfg.d * e + 2 * cfg.B * cfg.Hq * cfg.d * e \
         + cfg.B * cfg.Hq * cfg.k * 4
-    per = {"scores": by_scores, "attend": by_gather}
+    # the pair kernel runs the whole step (its later stage events are empty):
+    # its bytes per launch are the step's
+    whole = score_stage_kernel(cfg) == "score_select_pair_kernel"
+    per = {"scores": by_step if whole else by_scores, "attend": by_gather}
     dom = max(("scores", "attend"), key=lambda s_: stage_us[s_])
     kern = {"scores": score_stage_kernel(cfg), "attend": "attend_mfma_kernel"}[dom]
     ach = per[dom] / (stage_us[dom] * 1e-6) / 1e9
