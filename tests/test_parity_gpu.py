@@ -689,13 +689,18 @@ def test_pair_fused_rank_and_radix_heads(gpu_lib):
 @pytest.mark.parametrize("order", ["best_first", "best_last"])
 def test_pair_fused_score_order(gpu_lib, order):
     # pair-fused path (512 grouped query heads).  The selection first estimates
-    # each head's threshold bin from the first 2048 tokens and visits only the
-    # tokens at or above it; here every group's rows are sorted by the scores
-    # of its first query head.  best_first: that head's best tokens fill the
-    # first batch, the estimate lies above the real threshold and the full
-    # selection runs; best_last: the first batch holds its worst tokens, so
-    # nearly every token is visited.  Either way the result is the oracle's
-    cfg = cfg_case("C3", S=4096, B=16)
+    # each head's threshold bin from the first 4096 tokens (two score batches)
+    # and visits only the tokens at or above it; here every group's rows are
+    # sorted by the scores of its first query head.  best_first: that head's
+    # best tokens fill the sample, the estimate lies above the real threshold
+    # and the full selection runs; best_last: the sample holds its worst
+    # tokens, whose range fixes the bins, so the best tokens crowd the top end
+    # bin and the full selection (its exact radix path) runs as well.  With
+    # the natural order every block takes the marked tokens only.  Either way
+    # the result is the oracle's.  S = 8192 keeps the sample a strict part of
+    # the sequence, so that best_first really misses: the sample's want-th
+    # largest (want about 0.69 k) lies above the k-th
+    cfg = cfg_case("C3", S=8192, B=16)
     x = dict(make_inputs(cfg))
     _, s_o = oracle.select(x["q"], x["P"], x["K_rot"], cfg.r, cfg.k, return_scores=True)
     G = cfg.Hq // cfg.Hkv
